@@ -1,0 +1,45 @@
+"""Work and traffic counts used to report throughput, and the MI355X peaks.
+
+The FLOP count follows the training-cost guide (tool.smithlab.co.kr,
+"attention compute and training cost" section): a causal attention forward
+costs 2 * N * h * d FLOPs per token per layer, i.e. two N x N x d products
+of 2 FLOPs per multiply-add, halved by the causal mask.  For a batch this is
+4 * B * Hq * Nq * Nk * d, halved when causal.
+"""
+from __future__ import annotations
+
+# MI355X published peaks (dense, no structured sparsity).
+PEAK_BF16_MFMA_TFLOPS = 2500.0     # bf16 / fp16 dense matrix-core peak
+PEAK_HBM_GBS = 8000.0              # HBM3E bandwidth
+PEAK_FP32_VECTOR_TFLOPS = 157.3
+
+
+def attention_fwd_flops(B, Hq, Nq, Nk, d, causal) -> float:
+    """Forward FLOPs: QK^T and PV, 2 FLOPs per multiply-add; /2 if causal."""
+    f = 4.0 * B * Hq * Nq * Nk * d
+    return f / 2.0 if causal else f
+
+
+def attention_fwd_bytes(B, Hq, Hkv, Nq, Nk, d, out_bytes=2, in_bytes=2) -> float:
+    """Algorithmic HBM bytes: Q, K, V read once, O and the fp32 lse written
+    once.  Re-reads of K/V by several Q blocks and split-KV partials are an
+    implementation's overhead and are not counted."""
+    q = B * Hq * Nq * d * in_bytes
+    kv = 2 * B * Hkv * Nk * d * in_bytes
+    o = B * Hq * Nq * d * out_bytes
+    lse = B * Hq * Nq * 4
+    return float(q + kv + o + lse)
+
+
+def lse_bytes(B, Hq, Nq) -> int:
+    """Bytes of the saved per-row statistic: one fp32 per query row."""
+    return 4 * B * Hq * Nq
+
+
+def training_attention_flops_per_token(seq_len, heads, head_dim, layers,
+                                       backward_factor=2.5) -> float:
+    """Causal training FLOPs per token: forward plus a backward priced at
+    ``backward_factor`` times the forward (recomputation included)."""
+    fwd_per_token = attention_fwd_flops(1, heads, seq_len, seq_len, head_dim,
+                                        True) / seq_len
+    return (1.0 + backward_factor) * fwd_per_token * layers

@@ -1,0 +1,143 @@
+"""Seeded synthetic inputs for the fused attention forward, shared by the
+oracle side and the GPU side.
+
+This module holds no attention arithmetic.  It only
+
+* names the five workloads (shapes, mask flag, scale, value distribution),
+* draws the seeded fp32 values and rounds them to bf16 (round to nearest,
+  ties to even), returning the raw bf16 bit patterns as ``uint16`` arrays,
+* decodes bf16 bit patterns back to exact float values.
+
+Layouts: Q is ``[B, Hq, Nq, d]``, K and V are ``[B, Hkv, Nk, d]``, all
+contiguous with ``d`` fastest.
+
+Generator recipe (one fresh ``numpy.random.default_rng(seed)`` per call):
+draw Q, K, V in that order with ``standard_normal(dtype=float32)``; for the
+outlier workload then draw the Q mask and the K mask as
+``random() < 0.01`` (independent Bernoulli(0.01) per element) and multiply
+the selected entries by 8 (a power of two, so exact before or after the
+bf16 rounding); finally round every fp32 value to bf16.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv",
+    "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
+]
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    """One attention-forward problem: shapes, mask, scale, distribution."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    causal: bool
+    scale: float
+    outliers: bool = False   # 1% of Q and K entries scaled by 8
+
+    @property
+    def group(self) -> int:
+        return self.Hq // self.Hkv
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads, in order: tiny, MHA d=64, causal d=128 with outlier
+# scores, GQA prefill shaped like Qwen3-4B attention (32 query heads, 8 KV
+# heads, head dim 128), and single-query split-KV decode over a 32K cache.
+WORKLOADS = (
+    Workload("tiny_b1_h1_n256_d64", 1, 1, 1, 256, 256, 64, False, 1.0 / 8.0),
+    Workload("mha_b4_h16_n2048_d64", 4, 16, 16, 2048, 2048, 64, False,
+             1.0 / math.sqrt(64)),
+    Workload("causal_outlier_b2_h16_n4096_d128", 2, 16, 16, 4096, 4096, 128,
+             True, 1.0 / math.sqrt(128), outliers=True),
+    Workload("gqa_prefill_b1_hq32_hkv8_n8192_d128_causal", 1, 32, 8, 8192,
+             8192, 128, True, 1.0 / math.sqrt(128)),
+    Workload("decode_b16_hq32_hkv8_nq1_nk32768_d128", 16, 32, 8, 1, 32768,
+             128, False, 1.0 / math.sqrt(128)),
+)
+
+
+def workload(i_or_name) -> Workload:
+    if isinstance(i_or_name, int):
+        return WORKLOADS[i_or_name]
+    for w in WORKLOADS:
+        if w.name == i_or_name:
+            return w
+    raise KeyError(i_or_name)
+
+
+# ---------------------------------------------------------------- bf16 codec
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest, ties to even.
+
+    NaN maps to a quiet NaN (0x7FC0 with the sign kept); infinities and
+    values that round past the largest finite bf16 become infinities.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    rounded = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        sign = (u >> np.uint32(16)).astype(np.uint16) & np.uint16(0x8000)
+        rounded = np.where(nan, sign | np.uint16(0x7FC0), rounded)
+    return rounded
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> the exact fp32 values they encode."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> exact float64 values (no rounding happens)."""
+    return bf16_bits_to_f32(b).astype(np.float64)
+
+
+# ------------------------------------------------------------ the generator
+def make_qkv(B, Hq, Hkv, Nq, Nk, d, *, seed=0, outliers=False,
+             dist="normal", grid=None):
+    """Draw Q, K, V as bf16 bit patterns (uint16 arrays).
+
+    ``dist`` is ``"normal"`` (the recipe in the module docstring) or
+    ``"grid"``: values drawn uniformly from the integers in
+    ``[-grid, grid]`` times 1/8, which bf16 holds exactly; tests that need
+    exactly representable shifted keys use it.
+    """
+    rng = np.random.default_rng(seed)
+    shapes = ((B, Hq, Nq, d), (B, Hkv, Nk, d), (B, Hkv, Nk, d))
+    if dist == "normal":
+        q, k, v = (rng.standard_normal(s, dtype=np.float32) for s in shapes)
+    elif dist == "grid":
+        g = 4 if grid is None else int(grid)
+        q, k, v = (rng.integers(-g, g + 1, size=s).astype(np.float32) / 8.0
+                   for s in shapes)
+    else:
+        raise ValueError(dist)
+    if outliers:
+        mq = rng.random(q.shape) < 0.01
+        mk = rng.random(k.shape) < 0.01
+        q = np.where(mq, q * np.float32(8.0), q).astype(np.float32)
+        k = np.where(mk, k * np.float32(8.0), k).astype(np.float32)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def make_inputs(w, seed=0):
+    """Q, K, V bit patterns for a workload (index, name or ``Workload``)."""
+    if not isinstance(w, Workload):
+        w = workload(w)
+    return make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, seed=seed,
+                    outliers=w.outliers)

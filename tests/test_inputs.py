@@ -1,0 +1,91 @@
+"""The seeded input generator: bf16 rounding, reproducibility, recipe."""
+import numpy as np
+import pytest
+
+from fa_inputs import (WORKLOADS, bf16_bits_to_f32, f32_to_bf16_bits,
+                       make_inputs, make_qkv, workload)
+
+
+def _torch_bf16_bits(x):
+    torch = pytest.importorskip("torch")
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_bf16_rounding_matches_torch_on_random_values():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32),
+                        (rng.standard_normal(10000) * 1e30).astype(np.float32),
+                        (rng.standard_normal(10000) * 1e-38).astype(np.float32)])
+    np.testing.assert_array_equal(f32_to_bf16_bits(x), _torch_bf16_bits(x))
+
+
+def test_bf16_rounding_ties_and_edges():
+    # exact ties: lower 16 bits 0x8000, with even and odd upper halves
+    u = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80FFFF, 0x3F807FFF,
+                  0x00000000, 0x80000000, 0x00008000, 0x00018000,  # +-0, subnormal ties
+                  0x7F7FFFFF,                                       # max float -> inf
+                  0x7F800000, 0xFF800000, 0x7FC00000, 0x7F800001],  # inf, nan
+                 dtype=np.uint32)
+    x = u.view(np.float32)
+    ours = f32_to_bf16_bits(x)
+    ref = _torch_bf16_bits(x)
+    finite = np.isfinite(x) | np.isinf(x)
+    np.testing.assert_array_equal(ours[finite], ref[finite])
+    assert ours[0] == 0x3F80 and ours[1] == 0x3F82       # ties to even
+    assert ours[9] == 0x7F80                             # overflow to inf
+    nan = np.isnan(bf16_bits_to_f32(ours))
+    np.testing.assert_array_equal(nan, np.isnan(x))
+
+
+def test_bf16_decode_is_exact():
+    b = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    f = bf16_bits_to_f32(b)
+    ok = ~np.isnan(f)
+    np.testing.assert_array_equal(f32_to_bf16_bits(f[ok]), b[ok])
+
+
+def test_generator_is_seeded_and_shaped():
+    q1, k1, v1 = make_qkv(2, 4, 2, 7, 9, 8, seed=3)
+    q2, k2, v2 = make_qkv(2, 4, 2, 7, 9, 8, seed=3)
+    q3, _, _ = make_qkv(2, 4, 2, 7, 9, 8, seed=4)
+    assert q1.shape == (2, 4, 7, 8) and k1.shape == (2, 2, 9, 8)
+    assert q1.dtype == np.uint16
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(v1, v2)
+    assert np.any(q1 != q3)
+
+
+def test_generator_recipe_order():
+    """Q, K, V come from one PCG64 stream in that order, fp32 normals."""
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, 1, 256, 64), dtype=np.float32)
+    k = rng.standard_normal((1, 1, 256, 64), dtype=np.float32)
+    v = rng.standard_normal((1, 1, 256, 64), dtype=np.float32)
+    Q, K, V = make_inputs(0)
+    np.testing.assert_array_equal(Q, f32_to_bf16_bits(q))
+    np.testing.assert_array_equal(K, f32_to_bf16_bits(k))
+    np.testing.assert_array_equal(V, f32_to_bf16_bits(v))
+
+
+def test_outlier_fraction():
+    q, k, v = make_qkv(1, 4, 4, 512, 512, 128, seed=0, outliers=True)
+    qf, vf = bf16_bits_to_f32(q), bf16_bits_to_f32(v)
+    frac_q = np.mean(np.abs(qf) > 6.0)
+    frac_v = np.mean(np.abs(vf) > 6.0)
+    # N(0,1) beyond 6 is ~2e-9; 1% of entries scaled by 8 are beyond 6 about
+    # 55% of the time (|x| > 0.75)
+    assert 0.004 < frac_q < 0.007
+    assert frac_v < 1e-5
+
+
+def test_workload_table():
+    assert len(WORKLOADS) == 5
+    w = workload(3)
+    assert (w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, w.causal) == (1, 32, 8, 8192,
+                                                              8192, 128, True)
+    assert w.group == 4
+    assert workload(w.name) is w
+    d = workload(4)
+    assert (d.Nq, d.Nk, d.B) == (1, 32768, 16)
+    assert workload(2).outliers and not workload(1).outliers

@@ -1,0 +1,183 @@
+"""Throughput of the fused attention forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline]
+
+A step is one ``fa_fwd`` call over the whole workload with inputs resident
+in HBM.  W untimed steps, then exactly K timed steps bracketed by device
+synchronisation; each launch is also bracketed by HIP events on the stream
+it runs on, which gives the average kernel duration used for the roofline.
+Prints ONE JSON line.
+
+Default workload: causal GQA prefill shaped like Qwen3-4B attention
+(B=1, Hq=32, Hkv=8, N=8192, d=128), the configuration the headline metric
+is quoted on.  ``--workload decode`` runs the single-query KV-split decode
+(B=16, Hq=32, Hkv=8, Nk=32768, d=128) and reports HBM GB/s instead.
+
+The CPU baseline is the float64 oracle (test infrastructure) timed on the
+host on a bounded sample of the same workload: whole heads of the prefill,
+added one at a time until about 10 s of CPU work has been done.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from fa_inputs import make_inputs, workload  # noqa: E402
+from exact_io_aware_05_amd.metrics import (  # noqa: E402
+    PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_fwd_bytes,
+    attention_fwd_flops)
+
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
+WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
+             "tiny": 0}
+# HBM bytes per dispatch of the prefill kernel from rocprofv3 PMC counters
+# (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration factor);
+# None until counters have been taken for the current kernel.
+MEASURED_TRAFFIC = {}
+
+
+def _dev_tensor(bits):
+    import torch
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def cpu_baseline(w, q, k, v, budget_s=10.0):
+    """Oracle TFLOP/s on whole heads of batch 0, one head at a time."""
+    from fa_inputs import bf16_bits_to_f64
+    from oracle import reference_attention
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()
+                       if i.get("internal_api") in ("openblas", "mkl", "blis")),
+                      default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    G = w.Hq // w.Hkv
+    scale = float(np.float32(w.scale))
+    done, t_total = 0, 0.0
+    while done < w.Hq and t_total < budget_s:
+        h = done
+        qh = bf16_bits_to_f64(q[:1, h:h + 1])
+        kh = bf16_bits_to_f64(k[:1, h // G:h // G + 1])
+        vh = bf16_bits_to_f64(v[:1, h // G:h // G + 1])
+        t0 = time.perf_counter()
+        reference_attention(qh, kh, vh, causal=w.causal, scale=scale)
+        t_total += time.perf_counter() - t0
+        done += 1
+    flops = attention_fwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{done} of {w.B * w.Hq} heads (batch 0, heads 0..{done - 1}), "
+                  f"all {w.Nq} query rows each, float64 numpy; {t_total:.1f} s",
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gqa_prefill", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the attention forward runs on "
+              "one MI355X and no multi-GPU path is built (see DESIGN.md for "
+              "how it would shard). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    from exact_io_aware_05_amd import ops
+
+    w = workload(WORKLOADS[args.workload])
+    q, k, v = make_inputs(w, seed=0)
+    Q, K, V = _dev_tensor(q), _dev_tensor(k), _dev_tensor(v)
+    o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    ms_per_step = wall * 1e3 / args.steps
+
+    flops = attention_fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    nbytes = attention_fwd_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    traffic = MEASURED_TRAFFIC.get(w.name)
+    if w.Nq == 1:
+        value = nbytes / (ms_per_step * 1e-3) / 1e9
+        unit, metric = "GB/s", f"attn decode HBM GB/s ({w.name})"
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    else:
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        unit, metric = "TFLOP/s", METRIC if w.name == workload(3).name else \
+            f"attn fwd TFLOP/s ({w.name})"
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+                "traffic": traffic}
+
+    out = {
+        "metric": metric,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) fp32 rounded to bf16)",
+        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "out_dtype": "bf16",
+                   "kernel_ms": round(kern_ms, 4),
+                   "pct_bf16_mfma_peak": round(100 * flops / (kern_ms * 1e-3)
+                                               / 1e12 / PEAK_BF16_MFMA_TFLOPS, 2)},
+        "roofline": roof,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        if w.Nq == 1:
+            cb = out["cpu_baseline"]
+            cb["note"] = "oracle TFLOP/s (decode bytes are not a CPU metric)"
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,69 @@
+"""ctypes loader for ``libfa.so`` (the C interface declared in include/fa.h).
+
+The library is the only compute path: if it is missing it is built from
+source with hipcc, and if it cannot be loaded an error is raised.  There is
+no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_OUT_BF16, FA_OUT_F32 = 0, 1
+
+_c_int, _c_float, _c_size, _vp = (ctypes.c_int, ctypes.c_float,
+                                  ctypes.c_size_t, ctypes.c_void_p)
+
+# name -> (restype, argtypes), mirroring include/fa.h
+SIGNATURES = {
+    "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
+                        _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "fa_splitkv_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int,
+                                             _c_int]),
+    "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_float, _c_int, _c_int, _vp, _c_size, _vp]),
+    "fa_default_num_splits": (_c_int, [_c_int] * 6),
+    "fa_status_string": (ctypes.c_char_p, [_c_int]),
+    "fa_last_hip_error": (_c_int, []),
+}
+
+_lock = threading.Lock()
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        msg = lib.fa_status_string(status).decode()
+        if status == FA_ERR_HIP:
+            msg += f" (hipError_t {lib.fa_last_hip_error()})"
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def load():
+    """Load libfa.so, building it first if it is not there."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                from .build import build
+                build()
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FAError(status, where)

@@ -1,0 +1,159 @@
+// C interface of the attention library (declared in include/fa.h):
+// argument validation, choice between the prefill and KV-split forms,
+// workspace handling and error reporting.  No HIP call happens before every
+// argument check has passed.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return FA_OK;
+  g_last_hip_error = (int)e;
+  return FA_ERR_HIP;
+}
+
+bool aligned16(const void* p) {
+  return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+// Checks shared by both forward entry points; pure host arithmetic.
+int check_common(const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
+                 int d, float scale, int out_dtype) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || d < 1)
+    return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
+  if (out_dtype != FA_OUT_BF16 && out_dtype != FA_OUT_F32)
+    return FA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // element counts must stay well inside 64-bit offsets and 32-bit rows
+  const long long rows_q = (long long)B * Hq * Nq;
+  const long long rows_k = (long long)B * Hkv * Nk;
+  if (rows_q > (1LL << 40) || rows_k > (1LL << 40)) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// Is the current device gfx950?  Cached per device id.
+int check_device() {
+  static int cache[64];  // 0 unknown, 1 supported, 2 unsupported
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev >= 0 && dev < 64 && cache[dev]) return cache[dev] == 1 ? FA_OK : FA_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_status(e);
+  const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev >= 0 && dev < 64) cache[dev] = ok ? 1 : 2;
+  return ok ? FA_OK : FA_ERR_UNSUPPORTED;
+}
+
+// Heuristic for the KV-split form: used when the packed query rows of one
+// KV head (Nq * Hq / Hkv) are few (decode, short chunks); then enough chunks
+// to give about 2048 waves (8 per compute unit), each with >= 4 key blocks.
+int default_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
+  const long long R = (long long)Nq * (Hq / Hkv);
+  if (R > 64) return 0;
+  const long long units = (long long)B * Hkv * ((R + fa::kSplitRows - 1) / fa::kSplitRows);
+  const long long nblk = (Nk + fa::kSplitKeys - 1) / fa::kSplitKeys;
+  long long s = (2048 + units - 1) / units;
+  long long cap = nblk / 4;
+  if (cap < 1) cap = 1;
+  if (s > cap) s = cap;
+  if (s > fa::kMaxSplits) s = fa::kMaxSplits;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported shape or device";
+    case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error (see fa_last_hip_error)";
+    default: return "unknown fa status";
+  }
+}
+
+int fa_last_hip_error(void) { return g_last_hip_error; }
+
+size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {
+  if (B < 1 || Hq < 1 || Nq < 1 || d < 1 || num_splits < 1) return 0;
+  return fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, num_splits);
+}
+
+int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv) return 0;
+  if (d != 64 && d != 128) return 0;
+  return default_splits(B, Hq, Hkv, Nq, Nk);
+}
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int out_dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes < fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d,
+                                                    num_splits))
+    return FA_ERR_INVALID_ARG;
+  const long long rowtiles = ((long long)Nq * (Hq / Hkv) + fa::kSplitRows - 1) /
+                             fa::kSplitRows;
+  if ((long long)B * Hkv * rowtiles * num_splits > (1LL << 31) - 64)
+    return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  return hip_status(fa::launch_splitkv(q, k, v, o, lse, s,
+                                       out_dtype == FA_OUT_F32, num_splits,
+                                       workspace, stream));
+}
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+           float scale, int out_dtype, hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  const int splits = default_splits(B, Hq, Hkv, Nq, Nk);
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  const bool f32 = out_dtype == FA_OUT_F32;
+  if (splits == 0)
+    return hip_status(fa::launch_prefill(q, k, v, o, lse, s, f32, stream));
+  const size_t bytes =
+      fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, splits);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
+  hipError_t e2 = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(e2);
+}
+
+}  // extern "C"

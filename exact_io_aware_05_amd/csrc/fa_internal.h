@@ -1,0 +1,35 @@
+// Host-side launchers behind the C interface in fa.h.  Arguments are
+// already validated; each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+struct Shape {
+  int B, Hq, Hkv, Nq, Nk, d;
+  int causal;
+  float scale;
+};
+
+// Rows of queries per prefill workgroup and keys per streamed K/V block.
+constexpr int kPrefillRows = 128;
+constexpr int kPrefillKeys = 64;
+// Keys per block and query rows per wave in the KV-split kernel.
+constexpr int kSplitKeys = 32;
+constexpr int kSplitRows = 32;
+constexpr int kMaxSplits = 4096;
+
+hipError_t launch_prefill(const void* q, const void* k, const void* v,
+                          void* o, float* lse, const Shape& s, bool out_f32,
+                          hipStream_t stream);
+
+hipError_t launch_splitkv(const void* q, const void* k, const void* v,
+                          void* o, float* lse, const Shape& s, bool out_f32,
+                          int num_splits, void* workspace,
+                          hipStream_t stream);
+
+size_t splitkv_workspace_bytes(long long rows, int d, int num_splits);
+
+}  // namespace fa

@@ -1,0 +1,320 @@
+// KV-split attention forward (the Flash-Decoding form: "FlashAttention
+// Analysis", ryotta.opik.net, "Flash-Decoding" paragraph).  With one query
+// and thousands of cached keys there are too few query rows to fill the GPU,
+// so the key axis is cut into chunks that are processed in parallel, each
+// producing an unnormalised partial result (m, l, O~); a second kernel
+// combines the chunks with the log-sum-exp rule.
+//
+// Partial kernel: one wave per (batch, KV head, block of 32 packed query
+// rows, chunk).  The packed rows are the (query, head-in-group) pairs of
+// one KV head, so the Hq/Hkv query heads that share a KV head read each
+// K/V byte once.  The step is HBM-bound, so K and V are read straight into
+// matrix-core operand registers with no LDS round trip and no barrier, the
+// next 32-key block is fetched while the current one is computed, and the
+// transposition V needs for the P V product is done in registers:
+// * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  The contraction index (head
+//   dimension) is permuted so that each lane reads one contiguous half row
+//   of K (16 bytes per step); Q uses the same permutation.  Score register
+//   r of a lane holds key 16(r/8) + 8h + r%8 (the A-operand row order is
+//   chosen for that), which is the B-operand layout of P for the P V step.
+// * O^T = V^T P^T: a lane loads 8 consecutive V rows at head-dimension
+//   columns 4 col .. 4 col + 3 (whole rows are read per instruction) and
+//   v_perm_b32 repacks them into the A operands of 4 output tiles, where
+//   tile t, operand row a is head-dimension column 4a + t.
+// Merge kernel: one wave per output row, chunks visited in order.
+#include "fa_device.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int KB = kSplitKeys;  // 32 keys per block
+constexpr int NT = 256;         // 4 independent waves per workgroup
+
+// Per-wave register state of one 32-key block.
+template <int D>
+struct KvRegs {
+  static constexpr int NSTEP = D / 16;  // score k-steps
+  static constexpr int CPL = D / 32;    // V columns per lane (= O^T tiles)
+  u32x4 kf[NSTEP];                      // K operand, one per k-step
+  // V: [k-step s][row e] -> CPL bf16 values (CPL/2 dwords)
+  uint32_t vr[2][8][CPL / 2];
+
+  __device__ __forceinline__ void load(const uint16_t* kh, const uint16_t* vh,
+                                       int kb, int Nk, int h, int col) {
+    // K row for operand row `col`: key 16(a/8)... realised by the bit swap
+    const int kr = kb + ((col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1));
+    const bool kok = kr < Nk;
+    const uint16_t* kp = kh + (int64_t)(kok ? kr : 0) * D + (D / 2) * h;
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      kf[t] = kok ? ldg16(kp + 8 * t) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int vrow = kb + 16 * s + 8 * h + e;
+        const bool vok = vrow < Nk;
+        const uint16_t* vp = vh + (int64_t)(vok ? vrow : 0) * D + CPL * col;
+        if (CPL == 4) {
+          u32x2 x = vok ? *reinterpret_cast<const u32x2*>(vp) : u32x2{0u, 0u};
+          vr[s][e][0] = x[0];
+          vr[s][e][CPL / 2 - 1] = x[1];
+        } else {
+          vr[s][e][0] = vok ? *reinterpret_cast<const uint32_t*>(vp) : 0u;
+        }
+      }
+    }
+  }
+
+  // A operand (V^T) of output tile tt for k-step s: 8 keys of column
+  // CPL * col + tt, keys in the order e = 0..7.
+  __device__ __forceinline__ bf16x8 vop(int s, int tt) const {
+    const int dw = tt >> 1;
+    const uint32_t sel = (tt & 1) ? 0x07060302u : 0x05040100u;
+    u32x4 a;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      a[j] = __builtin_amdgcn_perm(vr[s][2 * j + 1][dw], vr[s][2 * j][dw], sel);
+    return __builtin_bit_cast(bf16x8, a);
+  }
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, float* __restrict__ ws_o,
+    float2* __restrict__ ws_ml, int Hq, int Hkv, int Nq, int Nk, float c2,
+    int n_rowtiles, int num_splits, int blocks_per_split, int n_items) {
+  constexpr int NSTEP = D / 16;
+  constexpr int CPL = D / 32;
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  if (item >= n_items) return;  // whole wave leaves; no barrier below
+  const int h = lane >> 5, col = lane & 31;
+
+  const int sp = item % num_splits;
+  const int t1 = item / num_splits;
+  const int rt = t1 % n_rowtiles;
+  const int bh = t1 / n_rowtiles;  // b * Hkv + hkv
+  const int b = bh / Hkv, hkv = bh % Hkv;
+  const int G = Hq / Hkv;
+  const int R = Nq * G;
+  const int prow = rt * 32 + col;  // packed (query, head-in-group) row
+  const bool row_ok = prow < R;
+  const int iq = row_ok ? prow / G : 0;
+  const int hq = hkv * G + (row_ok ? prow % G : 0);
+  const int off = Nk - Nq;
+  const int64_t qrow_id = (int64_t)(b * Hq + hq) * Nq + iq;
+
+  // Q^T operand with the permuted head dimension: step t, lane half h
+  // covers columns (D/2) h + 8t .. +7.
+  bf16x8 qf[NSTEP];
+  {
+    const uint16_t* qp = q + qrow_id * D + (D / 2) * h;
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      qf[t] = __builtin_bit_cast(
+          bf16x8, row_ok ? ldg16(qp + 8 * t) : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  const uint16_t* kh = k + (int64_t)bh * Nk * D;
+  const uint16_t* vh = v + (int64_t)bh * Nk * D;
+  const int nblk_all = (Nk + KB - 1) / KB;
+  const int blk0 = sp * blocks_per_split;
+  int blk1 = min(blk0 + blocks_per_split, nblk_all);
+  if (CAUSAL) {
+    // last key visible to the last packed row of this tile
+    const int last_q = min(R - 1, rt * 32 + 31) / G;
+    const int kv_end = min(Nk, last_q + off + 1);
+    blk1 = min(blk1, kv_end > 0 ? (kv_end + KB - 1) / KB : 0);
+  }
+  const int lim = CAUSAL ? min(Nk - 1, iq + off) : Nk - 1;
+  // smallest per-row limit in this row tile (its first packed row)
+  const int lim_first = CAUSAL ? min(Nk - 1, (rt * 32) / G + off) : Nk - 1;
+
+  f32x16 acc[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) acc[i] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+
+  KvRegs<D> cur, nxt;
+  if (blk0 < blk1) cur.load(kh, vh, blk0 * KB, Nk, h, col);
+  for (int blk = blk0; blk < blk1; ++blk) {
+    const int kb = blk * KB;
+    const bool has_next = blk + 1 < blk1;
+    if (has_next) nxt.load(kh, vh, kb + KB, Nk, h, col);
+
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      s = mfma32x32x16(__builtin_bit_cast(bf16x8, cur.kf[t]), qf[t], s);
+
+    const bool need_mask = kb + KB - 1 > lim_first;
+    uint32_t vis = 0xffffu;
+    if (need_mask) {
+      vis = 0;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = kb + 16 * (r >> 3) + 8 * h + (r & 7);
+        if (key <= lim) vis |= 1u << r;
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!(vis & (1u << r))) s[r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    mx = pair_max(mx);
+    const float m_new = fmaxf(m, mx * c2);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = exp2_fast(m - m_use);
+    m = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float p = exp2_fast(fmaf(s[r], c2, -m_use));
+      if (need_mask && !(vis & (1u << r))) p = 0.f;
+      s[r] = p;
+      rs += p;
+    }
+    l = alpha * l + rs;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) acc[i] *= alpha;
+    const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 8);
+#pragma unroll
+    for (int tt = 0; tt < CPL; ++tt) {
+      acc[tt] = mfma32x32x16(cur.vop(0, tt), p0, acc[tt]);
+      acc[tt] = mfma32x32x16(cur.vop(1, tt), p1, acc[tt]);
+    }
+    if (has_next) cur = nxt;
+  }
+
+  // ---- partial result of this chunk (unnormalised O, max m, sum l)
+  const float lt = pair_sum(l);
+  if (row_ok) {
+    float* op = ws_o + (qrow_id * num_splits + sp) * D;
+#pragma unroll
+    for (int gg = 0; gg < 4; ++gg) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int a = 8 * gg + 4 * h + e;  // operand row -> columns CPL*a + tt
+        if (CPL == 4) {
+          *reinterpret_cast<f32x4*>(op + 4 * a) =
+              f32x4{acc[0][4 * gg + e], acc[1][4 * gg + e],
+                    acc[2][4 * gg + e], acc[3][4 * gg + e]};
+        } else {
+          *reinterpret_cast<float2*>(op + CPL * a) =
+              float2{acc[0][4 * gg + e], acc[CPL - 1][4 * gg + e]};
+        }
+      }
+    }
+    if (h == 0) ws_ml[qrow_id * num_splits + sp] = float2{m, lt};
+  }
+}
+
+// One wave per output row; each lane owns D/64 columns.
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(NT) void splitkv_merge_kernel(
+    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
+    void* __restrict__ o, float* __restrict__ lse, long long n_rows,
+    int num_splits) {
+  constexpr int CPL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  if (row >= n_rows) return;
+  const float2* ml = ws_ml + row * num_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[s].x);
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  float L = 0.f;
+  float a[CPL];
+#pragma unroll
+  for (int i = 0; i < CPL; ++i) a[i] = 0.f;
+  const float* op = ws_o + row * num_splits * D + CPL * lane;
+  for (int s = 0; s < num_splits; ++s) {
+    const float2 x = ml[s];
+    const float w = exp2_fast(x.x - Mu);  // empty chunk: m = -inf -> 0
+    L += w * x.y;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) a[i] += w * op[(int64_t)s * D + i];
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  if (OUT_F32) {
+    float* dst = static_cast<float*>(o) + row * D + CPL * lane;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) dst[i] = a[i] * inv;
+  } else {
+    uint16_t* dst = static_cast<uint16_t*>(o) + row * D + CPL * lane;
+    if (CPL == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a[0] * inv, a[CPL - 1] * inv);
+    } else {
+      const uint32_t pk = pack_bf16x2(a[0] * inv, 0.f);
+      dst[0] = (uint16_t)(pk & 0xffffu);
+    }
+  }
+  if (lane == 0)
+    lse[row] = L > 0.f ? (Mu + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
+}
+
+template <int D, bool CAUSAL, bool OUT_F32>
+hipError_t launch(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const Shape& s, int num_splits, void* ws,
+                  hipStream_t stream) {
+  const int G = s.Hq / s.Hkv;
+  const long long R = (long long)s.Nq * G;
+  const int n_rowtiles = (int)((R + kSplitRows - 1) / kSplitRows);
+  const int nblk_all = (s.Nk + KB - 1) / KB;
+  const int bps = (nblk_all + num_splits - 1) / num_splits;
+  const long long n_items = (long long)s.B * s.Hkv * n_rowtiles * num_splits;
+  const long long n_rows = (long long)s.B * s.Hq * s.Nq;
+  float* ws_o = static_cast<float*>(ws);
+  float2* ws_ml = reinterpret_cast<float2*>(ws_o + n_rows * num_splits * D);
+  const float c2 = s.scale * kLog2e;
+  const unsigned wpb = NT / 64;
+  hipLaunchKernelGGL((splitkv_partial_kernel<D, CAUSAL>),
+                     dim3((unsigned)((n_items + wpb - 1) / wpb)), dim3(NT), 0,
+                     stream, static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), ws_o, ws_ml, s.Hq, s.Hkv,
+                     s.Nq, s.Nk, c2, n_rowtiles, num_splits, bps,
+                     (int)n_items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((splitkv_merge_kernel<D, OUT_F32>),
+                     dim3((unsigned)((n_rows + wpb - 1) / wpb)), dim3(NT), 0,
+                     stream, ws_o, ws_ml, o, lse, n_rows, num_splits);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t splitkv_workspace_bytes(long long rows, int d, int num_splits) {
+  return (size_t)rows * (size_t)num_splits * ((size_t)d * 4 + 8);
+}
+
+hipError_t launch_splitkv(const void* q, const void* k, const void* v,
+                          void* o, float* lse, const Shape& s, bool out_f32,
+                          int num_splits, void* workspace,
+                          hipStream_t stream) {
+  const bool c = s.causal != 0;
+#define FA_DISPATCH(D_)                                                     \
+  if (s.d == D_) {                                                          \
+    if (c)                                                                  \
+      return out_f32 ? launch<D_, true, true>(q, k, v, o, lse, s,           \
+                                              num_splits, workspace, stream) \
+                     : launch<D_, true, false>(q, k, v, o, lse, s,          \
+                                               num_splits, workspace, stream); \
+    return out_f32 ? launch<D_, false, true>(q, k, v, o, lse, s, num_splits, \
+                                             workspace, stream)             \
+                   : launch<D_, false, false>(q, k, v, o, lse, s, num_splits, \
+                                              workspace, stream);           \
+  }
+  FA_DISPATCH(128)
+  FA_DISPATCH(64)
+#undef FA_DISPATCH
+  return hipErrorInvalidValue;
+}
+
+}  // namespace fa

@@ -1,0 +1,98 @@
+"""PyTorch-facing binding of the attention library.
+
+Argument marshalling only: tensors supply device pointers, shapes and the
+current HIP stream; every step of the computation runs in the HIP kernels of
+``libfa.so``.  Layouts (contiguous, head dimension fastest):
+
+    q [B, Hq, Nq, d] bf16,  k, v [B, Hkv, Nk, d] bf16
+    o [B, Hq, Nq, d] bf16 or fp32,  lse [B, Hq, Nq] fp32 (natural log)
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
+
+__all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
+           "default_num_splits"]
+
+
+def _dims(q, k, v):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{name} must be a 4-D tensor [B, H, N, d]")
+        if t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bfloat16")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("shape mismatch between q, k and v")
+    return B, Hq, Hkv, Nq, Nk, d
+
+
+def _out(q, B, Hq, Nq, d, out_dtype, o, lse):
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=out_dtype, device=q.device)
+    elif (o.dtype != out_dtype or tuple(o.shape) != (B, Hq, Nq, d)
+          or not o.is_contiguous()):
+        raise ValueError("o has the wrong dtype, shape or layout")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)
+          or not lse.is_contiguous()):
+        raise ValueError("lse has the wrong dtype, shape or layout")
+    return o, lse
+
+
+def _stream(q):
+    return torch.cuda.current_stream(q.device).cuda_stream
+
+
+def fa_fwd(q, k, v, causal=False, scale=None, out_dtype=torch.bfloat16,
+           o=None, lse=None):
+    """Attention forward through ``fa_fwd``; returns ``(o, lse)``."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    st = load().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                       lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                       scale,
+                       FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16,
+                       _stream(q))
+    check(st, "fa_fwd")
+    return o, lse
+
+
+def splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) -> int:
+    return int(load().fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits))
+
+
+def default_num_splits(B, Hq, Hkv, Nq, Nk, d) -> int:
+    return int(load().fa_default_num_splits(B, Hq, Hkv, Nq, Nk, d))
+
+
+def fa_fwd_splitkv(q, k, v, num_splits, causal=False, scale=None,
+                   out_dtype=torch.bfloat16, o=None, lse=None, workspace=None):
+    """KV-split forward through ``fa_fwd_splitkv`` with a torch-allocated
+    workspace (uint8 device tensor); returns ``(o, lse)``."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    need = splitkv_workspace_bytes(B, Hq, Nq, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load().fa_fwd_splitkv(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16,
+        int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q))
+    check(st, "fa_fwd_splitkv")
+    return o, lse

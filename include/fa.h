@@ -1,0 +1,133 @@
+/*
+ * fa.h - fused exact attention forward for AMD MI355X (gfx950).
+ *
+ * The library computes, for every batch b and query head hq,
+ *
+ *     O   = softmax(scale * Q K^T + mask) V
+ *     lse = log(sum_j exp(scale * q_i . k_j))   over the visible keys j
+ *
+ * without ever writing the Nq x Nk score or probability matrices to memory.
+ * The algorithm is the tiled online softmax ("FlashAttention Analysis",
+ * ryotta.opik.net, section 3 "Tiling + Online Softmax"): a block of query
+ * rows stays on chip while K/V blocks stream through it, a running row max
+ * m and running sum l are kept, the partial output is rescaled by
+ * exp(m_old - m_new) when the max grows, and O is divided by l once at the
+ * end.  One fp32 logsumexp per query row is written for a
+ * recomputation-based backward pass (FlashAttention version/GPU/training-
+ * cost guide, tool.smithlab.co.kr, section on attention memory during
+ * training).  The KV-split entry point is the Flash-Decoding form (same
+ * "FlashAttention Analysis" page, "Flash-Decoding" paragraph): chunks of
+ * the key axis are processed in parallel and merged by a log-sum-exp
+ * reduction.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers owned by the caller, 16-byte
+ *   aligned, contiguous, head dimension fastest:
+ *       q   [B, Hq,  Nq, d]  bf16
+ *       k,v [B, Hkv, Nk, d]  bf16
+ *       o   [B, Hq,  Nq, d]  bf16 (FA_OUT_BF16) or fp32 (FA_OUT_F32)
+ *       lse [B, Hq,  Nq]     fp32, natural log
+ * - Grouped-query attention: query head hq reads KV head hq / (Hq / Hkv);
+ *   Hq must be a multiple of Hkv (Hkv == Hq is plain multi-head attention).
+ *   The KV head count is passed instead of replicating K/V (cost guide,
+ *   adoption checklist).
+ * - causal != 0 hides key j from query i when j > i + (Nk - Nq): the mask is
+ *   aligned at the last key, which is the usual lower triangle when
+ *   Nq == Nk and lets a single query see every key.  A query row that sees
+ *   no key at all (only possible when causal and Nq > Nk) gets O = 0 and
+ *   lse = -inf.
+ * - scale must be finite and >= 0 (1/sqrt(d) is the usual value).
+ * - d must be 64 or 128.
+ * - Every call is asynchronous: it validates its arguments on the host,
+ *   enqueues kernels on `stream` and returns.  Results are valid once the
+ *   stream has been synchronised; buffers must stay alive until then.
+ * - Results are deterministic: repeated calls with the same arguments give
+ *   bitwise identical outputs (fixed reduction orders, no float atomics).
+ *
+ * Errors
+ * ------
+ * Every entry point returns a status code.  All argument checks happen
+ * before any HIP call, and nothing is written when a check fails.
+ *   FA_ERR_INVALID_ARG  null or misaligned pointer, a size < 1, Hq not a
+ *                       multiple of Hkv, scale not finite or negative, bad
+ *                       out_dtype, workspace too small, num_splits < 1.
+ *   FA_ERR_UNSUPPORTED  d not 64 or 128, sizes beyond the 64-bit/grid
+ *                       limits, or the current device is not gfx950.
+ *   FA_ERR_HIP          a HIP runtime or launch error; the hipError_t is
+ *                       available from fa_last_hip_error() on the same
+ *                       thread.  Outputs are then undefined.
+ * No C++ exception crosses this interface.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hipStream_t;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,
+  FA_ERR_UNSUPPORTED = 2,
+  FA_ERR_HIP = 3
+};
+
+enum { FA_OUT_BF16 = 0, FA_OUT_F32 = 1 };
+
+/*
+ * Attention forward.  Picks the execution form by shape: the tiled prefill
+ * kernel (a workgroup per block of 128 query rows of one head) when there
+ * are enough query rows to fill the GPU, otherwise the KV-split form with
+ * fa_default_num_splits() chunks.  The KV-split form needs a temporary fp32
+ * workspace (fa_splitkv_workspace_bytes), which this call takes with
+ * hipMallocAsync on `stream` and returns with hipFreeAsync on the same
+ * stream.  `stream` may be NULL (the null stream).
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+           float scale, int out_dtype, hipStream_t stream);
+
+/*
+ * KV-split (Flash-Decoding) forward with a caller-owned workspace.
+ * The key axis is cut into `num_splits` chunks of whole 32-key blocks; each
+ * (batch, KV head, chunk) computes unnormalised partial results for all
+ * Hq/Hkv query heads of the group and all Nq queries, and a second kernel
+ * merges the chunks in chunk order by the log-sum-exp rule.  Chunks that
+ * hold no key (num_splits larger than the number of 32-key blocks) weigh
+ * nothing.  `workspace` is a device buffer of at least
+ * fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) bytes, 16-byte
+ * aligned; its contents on entry do not matter and on return are scratch.
+ * num_splits must be in [1, 4096].
+ */
+size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d,
+                                  int num_splits);
+
+int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int out_dtype, int num_splits,
+                   void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * The number of chunks fa_fwd uses for the KV-split form at this shape, or
+ * 0 when fa_fwd uses the prefill kernel instead.  Pure host arithmetic; no
+ * HIP call.  Returns 0 for invalid sizes as well.
+ */
+int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/* Static, human-readable text for a status code. */
+const char* fa_status_string(int status);
+
+/* The hipError_t (as int) behind the last FA_ERR_HIP on this thread. */
+int fa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -1,0 +1,124 @@
+"""The C interface on the host: the library loads without a GPU, exports
+every function the header declares, and rejects bad arguments with the
+documented status codes before touching the GPU (no compute call here)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+from exact_io_aware_05_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_header_declares_the_interface():
+    assert _declared_functions() == sorted(_lib.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(fa_[a-z0-9_]+)", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code, word in ((0, b"FA_OK"), (1, b"INVALID"), (2, b"UNSUPPORTED"),
+                       (3, b"HIP")):
+        assert word in lib.fa_status_string(code)
+    assert lib.fa_status_string(99) == b"unknown fa status"
+
+
+# fake but aligned, non-null "device" pointers: validation must fail first
+P = 0x10000
+
+
+def _fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=64,
+             causal=0, scale=0.125, out=0)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"],
+                      a["Hkv"], a["Nq"], a["Nk"], a["d"], a["causal"],
+                      a["scale"], a["out"], None)
+
+
+def _split(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=1, Nk=64, d=64,
+             causal=0, scale=0.125, out=0, S=2, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_fwd_splitkv(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                              a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                              a["causal"], a["scale"], a["out"], a["S"],
+                              a["ws"], a["wsb"], None)
+
+
+INVALID = [
+    dict(q=None), dict(k=None), dict(v=None), dict(o=None), dict(lse=None),
+    dict(q=P + 8), dict(k=P + 2), dict(v=P + 4), dict(o=P + 1), dict(lse=P + 2),
+    dict(B=0), dict(Hq=0), dict(Hkv=0), dict(Nq=0), dict(Nk=0), dict(d=0),
+    dict(B=-1), dict(Hq=6, Hkv=4), dict(scale=math.nan), dict(scale=math.inf),
+    dict(scale=-0.5), dict(out=2), dict(out=-1),
+]
+
+
+@pytest.mark.parametrize("kw", INVALID, ids=lambda k: str(k))
+def test_fwd_invalid_arguments(lib, kw):
+    assert _fwd(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [32, 96, 256, 100])
+def test_fwd_unsupported_head_dim(lib, d):
+    assert _fwd(lib, d=d) == _lib.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw", INVALID + [dict(S=0), dict(S=5000), dict(ws=None),
+                                          dict(ws=P + 4), dict(wsb=16)],
+                         ids=lambda k: str(k))
+def test_splitkv_invalid_arguments(lib, kw):
+    assert _split(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_splitkv_workspace_size(lib):
+    # rows * splits * (d fp32 partial output + (m, l))
+    assert lib.fa_splitkv_workspace_bytes(16, 32, 1, 128, 16) == \
+        16 * 32 * 16 * (128 * 4 + 8)
+    assert lib.fa_splitkv_workspace_bytes(1, 1, 1, 64, 1) == 64 * 4 + 8
+    assert lib.fa_splitkv_workspace_bytes(0, 1, 1, 64, 1) == 0
+    assert lib.fa_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0
+
+
+def test_default_split_choice(lib):
+    # single-query decode over a 32K cache, 128 (batch, KV head) pairs
+    assert lib.fa_default_num_splits(16, 32, 8, 1, 32768, 128) == 16
+    # prefill shapes use the tiled kernel
+    assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 128) == 0
+    assert lib.fa_default_num_splits(4, 16, 16, 2048, 2048, 64) == 0
+    # small caches get at most one chunk per 4 blocks of 32 keys
+    assert lib.fa_default_num_splits(1, 1, 1, 1, 64, 64) == 1
+    assert lib.fa_default_num_splits(1, 1, 1, 1, 4096, 64) == 32
+    # invalid sizes give 0
+    assert lib.fa_default_num_splits(1, 3, 2, 1, 64, 64) == 0
+    assert lib.fa_default_num_splits(1, 1, 1, 1, 64, 80) == 0
+
+
+def test_no_hip_error_recorded_by_validation(lib):
+    _fwd(lib, q=None)
+    _split(lib, S=0)
+    assert lib.fa_last_hip_error() == 0

@@ -1,0 +1,140 @@
+"""Properties of the HIP path that hold at any size: closed forms, exact
+equalities between equivalent calls, determinism, full coverage of the
+outputs."""
+import math
+
+import numpy as np
+import pytest
+
+from fa_inputs import bf16_bits_to_f64, make_qkv, workload
+from tests.gpu_util import LSE_TOL, O_TOL, dev, f64, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _ops():
+    from exact_io_aware_05_amd import ops
+    return ops
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_scale_zero_gives_mean_of_visible_values(causal, d):
+    B, Hq, Hkv, N = 1, 4, 2, 333
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, d, seed=3)
+    o, lse = _ops().fa_fwd(dev(q), dev(k), dev(v), causal=causal, scale=0.0,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O, L = host(o), host(lse)
+    vf = f64(v)
+    for h in range(Hq):
+        vh = vf[0, h // 2]
+        cnt = np.arange(1, N + 1) if causal else np.full(N, N)
+        mean = np.cumsum(vh, axis=0)[cnt - 1] / cnt[:, None]
+        assert np.max(np.abs(O[0, h] - mean)) <= O_TOL
+        assert np.max(np.abs(L[0, h] - np.log(cnt))) <= LSE_TOL
+
+
+def test_gqa_equals_replicated_heads_bitwise():
+    B, Hq, Hkv, N, d = 2, 8, 2, 300, 128
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, d, seed=4)
+    rep = Hq // Hkv
+    kr, vr = np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1)
+    for causal in (False, True):
+        o1, l1 = _ops().fa_fwd(dev(q), dev(k), dev(v), causal=causal)
+        o2, l2 = _ops().fa_fwd(dev(q), dev(kr), dev(vr), causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("idx", [1, 3, 4])
+def test_deterministic_reruns(idx):
+    w = workload(idx).with_(B=min(workload(idx).B, 2))
+    q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, seed=5)
+    Q, K, V = dev(q), dev(k), dev(v)
+    o1, l1 = _ops().fa_fwd(Q, K, V, causal=w.causal, scale=w.scale)
+    o2, l2 = _ops().fa_fwd(Q, K, V, causal=w.causal, scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("idx", [1, 3])
+def test_every_output_written(idx):
+    """Outputs pre-filled with NaN come back fully finite."""
+    w = workload(idx).with_(B=1, Nq=1000, Nk=1000)
+    q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, seed=6)
+    o = torch.full((w.B, w.Hq, w.Nq, w.d), float("nan"), dtype=torch.bfloat16,
+                   device="cuda")
+    lse = torch.full((w.B, w.Hq, w.Nq), float("nan"), device="cuda")
+    _ops().fa_fwd(dev(q), dev(k), dev(v), causal=w.causal, scale=w.scale,
+                  o=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+def test_splitkv_every_output_written_and_split_invariant():
+    w = workload(4).with_(B=2, Nk=3000)
+    q, k, v = make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, seed=9)
+    Q, K, V = dev(q), dev(k), dev(v)
+    ref = None
+    for S in (1, 2, 7, 94, 200):   # 94 blocks of 32 keys; 200 leaves chunks empty
+        o = torch.full((w.B, w.Hq, 1, w.d), float("nan"), dtype=torch.float32,
+                       device="cuda")
+        lse = torch.full((w.B, w.Hq, 1), float("nan"), device="cuda")
+        _ops().fa_fwd_splitkv(Q, K, V, S, scale=w.scale, out_dtype=torch.float32,
+                              o=o, lse=lse)
+        torch.cuda.synchronize()
+        assert torch.isfinite(o).all() and torch.isfinite(lse).all()
+        if ref is None:
+            ref = (o.clone(), lse.clone())
+        else:
+            # chunks differ only in the reference max against which P is
+            # rounded to bf16 (relative 2^-9 per weight) and in fp32 order
+            assert (o - ref[0]).abs().max().item() <= 2e-3
+            assert (lse - ref[1]).abs().max().item() <= 1e-5
+
+
+def test_key_shift_invariance():
+    """K' = K + 1 u^T with everything on a coarse grid (exact in bf16):
+    O unchanged, lse_i grows by scale * q_i . u."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 200, 64
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, d, seed=10, dist="grid", grid=4)
+    u = (np.arange(d) % 5 - 2).astype(np.float32) / 4.0
+    kf = bf16_bits_to_f64(k) + u
+    from fa_inputs import f32_to_bf16_bits
+    k2 = f32_to_bf16_bits(kf.astype(np.float32))
+    assert np.array_equal(bf16_bits_to_f64(k2), kf)       # exact shift
+    scale = 0.125
+    for causal in (False, True):
+        o1, l1 = _ops().fa_fwd(dev(q), dev(k), dev(v), causal=causal,
+                               scale=scale, out_dtype=torch.float32)
+        o2, l2 = _ops().fa_fwd(dev(q), dev(k2), dev(v), causal=causal,
+                               scale=scale, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        kappa = scale * np.einsum("bhid,d->bhi", bf16_bits_to_f64(q), u)
+        assert np.max(np.abs(host(o2) - host(o1))) <= O_TOL
+        assert np.max(np.abs(host(l2) - (host(l1) + kappa))) <= LSE_TOL
+
+
+def test_one_hot_selection():
+    """Query i equals key i scaled up: each row selects its own V row."""
+    N, d = 256, 64
+    c = 18.0
+    q = np.zeros((1, 1, N, d), np.float32)
+    k = np.zeros((1, 1, N, d), np.float32)
+    for i in range(N):
+        q[0, 0, i, i % d] = c
+        k[0, 0, i, i % d] = c if i < d else 0.0
+    rng = np.random.default_rng(11)
+    v = rng.standard_normal((1, 1, N, d)).astype(np.float32)
+    from fa_inputs import f32_to_bf16_bits
+    qb, kb, vb = (f32_to_bf16_bits(x) for x in (q, k, v))
+    o, lse = _ops().fa_fwd(dev(qb), dev(kb), dev(vb), scale=1.0 / 8.0,
+                           out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O = host(o)
+    vv = f64(vb)
+    # rows i < d: key i is the only one aligned with e_i -> O_i = v_i
+    assert np.max(np.abs(O[0, 0, :d] - vv[0, 0, :d])) <= O_TOL

@@ -55,6 +55,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// acc + lo + hi of a packed bf16 pair, accumulated in fp32
+// (v_dot2c_f32_bf16 against (1, 1)).
+__device__ __forceinline__ float add_bf16x2(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u),
+                                         acc, false);
+}
+
 // Eight fp32 (elements [base, base + 8) of a C fragment) -> a bf16x8
 // operand.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16& c, int base) {

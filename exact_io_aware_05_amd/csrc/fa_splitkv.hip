@@ -84,7 +84,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_o,
-    float2* __restrict__ ws_ml, int Hq, int Hkv, int Nq, int Nk, float c2,
+    f32x4* __restrict__ ws_ml, int Hq, int Hkv, int Nq, int Nk, float c2,
     int n_rowtiles, int num_splits, int blocks_per_split, int n_items) {
   constexpr int NSTEP = D / 16;
   constexpr int CPL = D / 32;
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   f32x16 acc[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = f32x16{};
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, lb = 0.f;
 
   KvRegs<D> cur, nxt;
   if (blk0 < blk1) cur.load(kh, vh, blk0 * KB, Nk, h, col);
@@ -171,18 +171,28 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = exp2_fast(m - m_use);
     m = m_new;
-    float rs = 0.f;
+    // weights rounded to bf16 once: the rounded weights feed the P V
+    // product and their own sum lb (normalises O); the fp32 sum l gives lse
+    u32x4 pk[2];
+    float rs = 0.f, rb = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float p = exp2_fast(fmaf(s[r], c2, -m_use));
-      if (need_mask && !(vis & (1u << r))) p = 0.f;
-      s[r] = p;
-      rs += p;
+    for (int r = 0; r < 16; r += 2) {
+      float pa = exp2_fast(fmaf(s[r], c2, -m_use));
+      float pc = exp2_fast(fmaf(s[r + 1], c2, -m_use));
+      if (need_mask && !(vis & (1u << r))) pa = 0.f;
+      if (need_mask && !(vis & (1u << (r + 1)))) pc = 0.f;
+      rs += pa;
+      rs += pc;
+      const uint32_t w = pack_bf16x2(pa, pc);
+      pk[r >> 3][(r >> 1) & 3] = w;
+      rb = add_bf16x2(w, rb);
     }
     l = alpha * l + rs;
+    lb = alpha * lb + rb;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) acc[i] *= alpha;
-    const bf16x8 p0 = to_bf16x8(s, 0), p1 = to_bf16x8(s, 8);
+    const bf16x8 p0 = __builtin_bit_cast(bf16x8, pk[0]);
+    const bf16x8 p1 = __builtin_bit_cast(bf16x8, pk[1]);
 #pragma unroll
     for (int tt = 0; tt < CPL; ++tt) {
       acc[tt] = mfma32x32x16(cur.vop(0, tt), p0, acc[tt]);
@@ -193,6 +203,7 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
 
   // ---- partial result of this chunk (unnormalised O, max m, sum l)
   const float lt = pair_sum(l);
+  const float lbt = pair_sum(lb);
   if (row_ok) {
     float* op = ws_o + (qrow_id * num_splits + sp) * D;
 #pragma unroll
@@ -210,37 +221,38 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
         }
       }
     }
-    if (h == 0) ws_ml[qrow_id * num_splits + sp] = float2{m, lt};
+    if (h == 0) ws_ml[qrow_id * num_splits + sp] = f32x4{m, lt, lbt, 0.f};
   }
 }
 
 // One wave per output row; each lane owns D/64 columns.
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(NT) void splitkv_merge_kernel(
-    const float* __restrict__ ws_o, const float2* __restrict__ ws_ml,
+    const float* __restrict__ ws_o, const f32x4* __restrict__ ws_ml,
     void* __restrict__ o, float* __restrict__ lse, long long n_rows,
     int num_splits) {
   constexpr int CPL = D / 64;
   const int lane = threadIdx.x & 63;
   const long long row = (long long)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
   if (row >= n_rows) return;
-  const float2* ml = ws_ml + row * num_splits;
+  const f32x4* ml = ws_ml + row * num_splits;
   float M = -INFINITY;
-  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[s].x);
+  for (int s = 0; s < num_splits; ++s) M = fmaxf(M, ml[s][0]);
   const float Mu = (M == -INFINITY) ? 0.f : M;
-  float L = 0.f;
+  float L = 0.f, LB = 0.f;
   float a[CPL];
 #pragma unroll
   for (int i = 0; i < CPL; ++i) a[i] = 0.f;
   const float* op = ws_o + row * num_splits * D + CPL * lane;
   for (int s = 0; s < num_splits; ++s) {
-    const float2 x = ml[s];
-    const float w = exp2_fast(x.x - Mu);  // empty chunk: m = -inf -> 0
-    L += w * x.y;
+    const f32x4 x = ml[s];
+    const float w = exp2_fast(x[0] - Mu);  // empty chunk: m = -inf -> 0
+    L += w * x[1];
+    LB += w * x[2];
 #pragma unroll
     for (int i = 0; i < CPL; ++i) a[i] += w * op[(int64_t)s * D + i];
   }
-  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const float inv = LB > 0.f ? 1.f / LB : 0.f;
   if (OUT_F32) {
     float* dst = static_cast<float*>(o) + row * D + CPL * lane;
 #pragma unroll
@@ -270,7 +282,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   const long long n_items = (long long)s.B * s.Hkv * n_rowtiles * num_splits;
   const long long n_rows = (long long)s.B * s.Hq * s.Nq;
   float* ws_o = static_cast<float*>(ws);
-  float2* ws_ml = reinterpret_cast<float2*>(ws_o + n_rows * num_splits * D);
+  f32x4* ws_ml = reinterpret_cast<f32x4*>(ws_o + n_rows * num_splits * D);
   const float c2 = s.scale * kLog2e;
   const unsigned wpb = NT / 64;
   hipLaunchKernelGGL((splitkv_partial_kernel<D, CAUSAL>),
@@ -291,7 +303,8 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
 }  // namespace
 
 size_t splitkv_workspace_bytes(long long rows, int d, int num_splits) {
-  return (size_t)rows * (size_t)num_splits * ((size_t)d * 4 + 8);
+  // per (row, chunk): d fp32 partial outputs + (m, l, lb, unused)
+  return (size_t)rows * (size_t)num_splits * ((size_t)d * 4 + 16);
 }
 
 hipError_t launch_splitkv(const void* q, const void* k, const void* v,

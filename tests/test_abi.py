@@ -96,10 +96,10 @@ def test_splitkv_invalid_arguments(lib, kw):
 
 
 def test_splitkv_workspace_size(lib):
-    # rows * splits * (d fp32 partial output + (m, l))
+    # rows * splits * (d fp32 partial outputs + (m, l, lb, unused) fp32)
     assert lib.fa_splitkv_workspace_bytes(16, 32, 1, 128, 16) == \
-        16 * 32 * 16 * (128 * 4 + 8)
-    assert lib.fa_splitkv_workspace_bytes(1, 1, 1, 64, 1) == 64 * 4 + 8
+        16 * 32 * 16 * (128 * 4 + 16)
+    assert lib.fa_splitkv_workspace_bytes(1, 1, 1, 64, 1) == 64 * 4 + 16
     assert lib.fa_splitkv_workspace_bytes(0, 1, 1, 64, 1) == 0
     assert lib.fa_splitkv_workspace_bytes(1, 1, 1, 64, 0) == 0
 

@@ -14,7 +14,7 @@ struct Shape {
 };
 
 // Rows of queries per prefill workgroup and keys per streamed K/V block.
-constexpr int kPrefillRows = 128;
+constexpr int kPrefillRows = 256;
 constexpr int kPrefillKeys = 64;
 // Keys per block and query rows per wave in the KV-split kernel.
 constexpr int kSplitKeys = 32;

@@ -1,5 +1,5 @@
 // Tiled attention forward (prefill): one workgroup per (batch, query head,
-// block of 128 query rows), 4 waves of 32 query rows each.
+// block of 256 query rows), 8 waves of 32 query rows each.
 //
 // Method ("FlashAttention Analysis", ryotta.opik.net, section 3 "Tiling +
 // Online Softmax"): the Q block stays resident (in registers, as matrix-core
@@ -28,19 +28,28 @@
 //   LDS through the transposing read ds_read_b64_tr_b16.
 // * K/V tiles move HBM -> LDS with buffer_load ... lds (no staging
 //   registers, no VALU); a buffer resource per head makes reads past the
-//   last key return zeros, so tails need no branches.  LDS rows are padded
-//   (K: 16 bytes, V: 64 bytes) so that the operand reads of a wave hit
-//   distinct banks and every read address is a per-lane base plus an
-//   immediate offset.  Double-buffered: one barrier per 64-key block.
+//   last key return zeros, so tails need no branches.  K is stored
+//   column-major in 16-byte chunks (chunk c of all 64 rows is one
+//   contiguous KiB), V row-major with 8-byte chunks XOR-swizzled by row:
+//   each DMA instruction then reads from a per-lane base plus a scalar
+//   offset, the operand reads of a wave hit distinct banks, and every read
+//   address is a per-lane base plus an immediate.
+// * Matrix cores and vector ALUs are kept busy together by running the two
+//   halves of the workgroup half a block apart ("ping-pong"): waves 0-3 and
+//   waves 4-7 share the SIMDs pairwise, and between two workgroup barriers
+//   one group issues its matrix products (P_{j-1} V_{j-1}, then
+//   S_j = Q K_j^T) while the other group does its softmax, then they swap.
+//   A wave raises its issue priority during its matrix phase.
 // * The output rescale is lazy: the reference max used for the
 //   exponentials only moves when some row's max grew by more than 2^8, so
 //   almost every block skips the 64 multiplies per lane.  The result is the
 //   same real-arithmetic quantity (the factor cancels in O = acc / l).
-// * Causal: K/V blocks past the diagonal are never loaded; waves whose rows
-//   all precede a block skip its math; masking runs only on blocks that
-//   cross the diagonal or the key tail.  Heavy Q blocks (late rows) are
-//   scheduled first, and the query heads of one KV-head group run next to
-//   each other on the same XCD so that they share K/V in its L2.
+// * Causal: K/V blocks past the diagonal are never loaded; a wave whose rows
+//   all precede a block skips its math for that block; masking runs only on
+//   blocks that cross the wave's diagonal or the key tail.  Heavy Q blocks
+//   (late rows) are scheduled first, and the query heads of one KV-head
+//   group run next to each other on the same XCD so that they share K/V in
+//   its L2.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -49,12 +58,15 @@
 namespace fa {
 namespace {
 
-constexpr int BR = kPrefillRows;
-constexpr int BC = kPrefillKeys;
-constexpr int NT = 256;  // 4 waves
+constexpr int BR = kPrefillRows;   // 256 query rows per workgroup
+constexpr int BC = kPrefillKeys;   // 64 keys per K/V block
+constexpr int NW = BR / 32;        // 8 waves
+constexpr int NT = 64 * NW;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
 
 // LDS row position of key j (within a 64-key tile): bits 2 and 3 swapped.
 __device__ __forceinline__ int key_slot(int j) {
@@ -63,19 +75,22 @@ __device__ __forceinline__ int key_slot(int j) {
 
 template <int D>
 struct Layout {
-  static constexpr int ROWB = 2 * D;             // bytes of one K/V row
-  static constexpr int KCH = D / 8 + 1;          // 16-byte chunks per K row
-  static constexpr int VCH = D / 8 + 4;          // ... per V row (padded)
-  static constexpr int KSTRIDE = 16 * KCH;       // 272 (D=128) / 144
-  static constexpr int VSTRIDE = 16 * VCH;       // 320 (D=128) / 192
-  static constexpr int KBYTES = BC * KSTRIDE;
-  static constexpr int VBYTES = BC * VSTRIDE;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int KINS = KCH;               // 1 KiB DMA instructions
-  static constexpr int VINS = VCH;
-  static constexpr int KPW = (KINS + 3) / 4;     // per wave (max)
-  static constexpr int VPW = (VINS + 3) / 4;
+  static constexpr int ROWB = 2 * D;          // bytes of one K/V row
+  static constexpr int KBYTES = BC * ROWB;    // one K buffer (16 KiB at 128)
+  static constexpr int VBYTES = BC * ROWB;    // one V buffer
+  static constexpr int NS = 4;                // ring stages of K and of V
+  static constexpr int VBASE = NS * KBYTES;   // [K0..K3 | V0..V3]
+  static constexpr int TOTAL = NS * (KBYTES + VBYTES);
+  static constexpr int NINS = KBYTES / 1024;  // 1 KiB DMA instructions
+  static constexpr int NTILE = D / 32;        // O^T accumulator tiles
+  static constexpr int NSTEP = D / 16;        // k-steps of the score product
 };
+
+// V swizzle: 8-byte chunk u of row r is stored at u ^ vswz(r).
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return D == 128 ? 8 * (r & 3) : 8 * ((r >> 1) & 1);
+}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base,
                                                        uint32_t bytes) {
@@ -83,51 +98,212 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base,
                                            (int)bytes, 0x00020000);
 }
 
-// Starts the HBM -> LDS copy of K/V block `blk` into LDS stage `stage`:
-// each wave issues its share of 1 KiB buffer_load ... lds instructions.
-// Reads past key Nk return zeros (buffer range check).
+// Starts the HBM -> LDS copy of block `blk` (64 rows) of one K or V head
+// (`head`: its row 0) into the LDS buffer at `dst`, shared by the NW waves:
+// wave w issues 1 KiB buffer_load ... lds instructions i = w, w + NW, ...;
+// instruction i reads from lane offset `lane_off` plus `step * i` bytes.  Rows at or past Nk read as zeros (buffer range check
+// on the per-instruction resource); a block wholly past Nk is a copy of
+// zeros, which keeps the number of copies per loop iteration fixed.
 template <int D>
-__device__ __forceinline__ void issue_dma(char* smem, const char* kh,
-                                          const char* vh, int Nk, int blk,
-                                          int stage, int wave,
-                                          const uint32_t* koff,
-                                          const uint32_t* voff) {
+__device__ __forceinline__ void copy_block(char* dst, const char* head,
+                                           int Nk, int blk, int wave,
+                                           uint32_t lane_off, int step) {
+  // (Nk here: number of rows that may be read; later rows read as zeros)
   using L = Layout<D>;
-  const int kb = blk * BC;
-  const uint32_t rem = (uint32_t)(Nk - kb) * L::ROWB;
-  const __amdgpu_buffer_rsrc_t rk = rsrc(kh + (int64_t)kb * L::ROWB, rem);
-  const __amdgpu_buffer_rsrc_t rv = rsrc(vh + (int64_t)kb * L::ROWB, rem);
-  char* base = smem + stage * L::STAGE;
+  const int kb = min(blk * BC, Nk);
+  const char* base = head + (int64_t)kb * L::ROWB;
+  const int rem = (Nk - kb) * L::ROWB;
 #pragma unroll
-  for (int n = 0; n < L::KPW; ++n) {
-    const int i = wave + 4 * n;
-    if (i < L::KINS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rk, (lds_void*)(base + 1024 * i), 16, koff[n], 0, 0, 0);
-  }
-#pragma unroll
-  for (int n = 0; n < L::VPW; ++n) {
-    const int i = wave + 4 * n;
-    if (i < L::VINS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rv, (lds_void*)(base + L::KBYTES + 1024 * i), 16, voff[n], 0, 0, 0);
+  for (int n = 0; n < L::NINS / NW; ++n) {
+    const int i = wave + NW * n;
+    const __amdgpu_buffer_rsrc_t r =
+        rsrc(base + step * i, (uint32_t)max(rem - step * i, 0));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        r, (lds_void*)(dst + 1024 * i), 16, lane_off, 0, 0, 0);
   }
 }
 
+// s_waitcnt with vmcnt = N (expcnt, lgkmcnt left free); gfx9 encoding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Running softmax state of one lane (one query row, half of its keys).
+struct RowState {
+  float m;   // reference max in use, log2 units
+  float l;   // sum of the fp32 weights (gives lse)
+  float lb;  // sum of the bf16-rounded weights (normalises O)
+};
+
+// Matrix phase of one wave for block j: O^T += V_{j-1}^T P_{j-1}^T (if
+// PV), then S_j^T = K_j Q^T (if QK), 32-key halves into s0 / s1.
+//   kp: lane K read address in buffer j;  vp: lane V read addresses (per
+//   output tile) in buffer j - 1.
+// The operand reads run DEPTH matrix products ahead of their use (the
+// order is pinned with sched_barrier): in this phase only one wave per SIMD
+// issues matrix products, so an exposed LDS round trip would idle the
+// matrix core.
+template <int D, bool PV, bool QK>
+__device__ __forceinline__ void matrix_phase(const char* kp,
+                                             const char* const* vp,
+                                             const bf16x8* qf,
+                                             const u32x4* pk, f32x16* acc,
+                                             f32x16& s0, f32x16& s1) {
+  using L = Layout<D>;
+  constexpr int NPV = PV ? 4 * L::NTILE : 0;  // P V products (s, tile)
+  constexpr int NQK = QK ? 2 * L::NSTEP : 0;  // score products (t, half)
+  constexpr int NOP = NPV + NQK;
+  constexpr int DEPTH = 4;
+  i16x4 vlo[NPV > 0 ? NPV : 1], vhi[NPV > 0 ? NPV : 1];
+  bf16x8 kop[NQK > 0 ? NQK : 1];
+  // Issue order: P V and score products alternate (when both are present)
+  // so that two products on the same accumulator are several slots apart.
+  // Product index i < NPV: P V product i; otherwise score product i - NPV.
+  auto order = [&](int slot) {
+    if (NPV == 0 || NQK == 0) return slot;
+    const int k = slot >> 1;
+    if (NPV == NQK) return (slot & 1) ? NPV + k : k;
+    return slot < 2 * (NPV < NQK ? NPV : NQK) ? ((slot & 1) ? NPV + k : k)
+                                              : slot;  // not reached
+  };
+  // operand read of product i
+  auto read = [&](int i) {
+    if (i < NPV) {
+      const int s = i / L::NTILE, tt = i % L::NTILE;
+      const char* a0 = vp[tt] + s * 16 * L::ROWB;
+      vlo[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)((lds_char*)a0));
+      vhi[i] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)((lds_char*)(a0 + 4 * L::ROWB)));
+    } else {
+      const int q = i - NPV, t = q >> 1, half = q & 1;
+      // chunk 2t + h of LDS rows col (+ 32 for the second half)
+      kop[q] = *reinterpret_cast<const bf16x8*>(kp + 2048 * t + 512 * half);
+    }
+  };
+  if (QK) {
+    s0 = f32x16{};
+    s1 = f32x16{};
+  }
+  static_assert(NPV == 0 || NQK == 0 || NPV == NQK, "product counts");
+#pragma unroll
+  for (int i = 0; i < DEPTH && i < NOP; ++i) read(order(i));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int slot = 0; slot < NOP; ++slot) {
+    if (slot + DEPTH < NOP) read(order(slot + DEPTH));
+    const int i = order(slot);
+    if (i < NPV) {
+      const int s = i / L::NTILE, tt = i % L::NTILE;
+      u32x4 va;
+      va[0] = __builtin_bit_cast(u32x2, vlo[i])[0];
+      va[1] = __builtin_bit_cast(u32x2, vlo[i])[1];
+      va[2] = __builtin_bit_cast(u32x2, vhi[i])[0];
+      va[3] = __builtin_bit_cast(u32x2, vhi[i])[1];
+      acc[tt] = mfma32x32x16(__builtin_bit_cast(bf16x8, va),
+                             __builtin_bit_cast(bf16x8, pk[s]), acc[tt]);
+    } else {
+      const int q = i - NPV, t = q >> 1;
+      if (q & 1)
+        s1 = mfma32x32x16(kop[q], qf[t], s1);
+      else
+        s0 = mfma32x32x16(kop[q], qf[t], s0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Softmax phase of one wave for block j: optional mask (`lim`: last
+// visible key relative to this lane's first key of the block; register r of
+// half 0 holds relative key 16(r/8) + r%8, half 1 adds 32), row max, lazy
+// rescale of the state (returns true, with the factor in `alpha`, when the
+// accumulators must be scaled before the next P V), weights
+// p = 2^(s c2 - m) rounded to bf16 once into pk.  The rounded weights feed P V and their own
+// row sum lb, so O = acc / lb is an exact convex combination of V rows up to
+// fp32 summation; the fp32 sum l of the unrounded weights gives lse.
+template <bool MASK>
+__device__ __forceinline__ bool softmax_phase(const f32x16& s0,
+                                              const f32x16& s1, int lim,
+                                              float c2, RowState& st,
+                                              float& alpha, u32x4* pk) {
+  // The mask never overwrites the score registers (that would make the
+  // masked and unmasked variants rejoin with copies): hidden keys are left
+  // out of the max and get weight 0 after the exponential.
+  auto hide0 = [&](int r) { return MASK && 16 * (r >> 3) + (r & 7) > lim; };
+  auto hide1 = [&](int r) {
+    return MASK && 16 * (r >> 3) + (r & 7) + 32 > lim;
+  };
+  // row max: four independent max3 chains, then combined
+  float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    mq[r & 3] = fmaxf(fmaxf(mq[r & 3], hide0(r) ? -INFINITY : s0[r]),
+                      hide1(r) ? -INFINITY : s1[r]);
+  float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
+  mx = pair_max(mx) * c2;
+  const bool rescale =
+      __builtin_amdgcn_ballot_w64(mx > st.m + kRescaleThreshold) != 0;
+  if (rescale) {
+    const float m_new = fmaxf(st.m, mx);
+    // unchanged rows (including rows with nothing visible yet) keep
+    // factor 1; a first visible key gives 2^-inf = 0
+    alpha = (m_new == st.m) ? 1.f : exp2_fast(st.m - m_new);
+    st.m = m_new;
+    st.l *= alpha;
+    st.lb *= alpha;
+  }
+  const float msub = (st.m == -INFINITY) ? 0.f : st.m;
+  // sums: independent partial chains (fixed order, combined at the end)
+  float rs[4] = {0.f, 0.f, 0.f, 0.f};
+  float rb0 = 0.f, rb1 = 0.f, rb2 = 0.f, rb3 = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    float e0 = exp2_fast(fmaf(s0[r], c2, -msub));
+    float e1 = exp2_fast(fmaf(s0[r + 1], c2, -msub));
+    float e2 = exp2_fast(fmaf(s1[r], c2, -msub));
+    float e3 = exp2_fast(fmaf(s1[r + 1], c2, -msub));
+    if (hide0(r)) e0 = 0.f;
+    if (hide0(r + 1)) e1 = 0.f;
+    if (hide1(r)) e2 = 0.f;
+    if (hide1(r + 1)) e3 = 0.f;
+    rs[0] += e0;
+    rs[1] += e1;
+    rs[2] += e2;
+    rs[3] += e3;
+    const uint32_t a = pack_bf16x2(e0, e1);
+    const uint32_t c = pack_bf16x2(e2, e3);
+    pk[r >> 3][(r >> 1) & 3] = a;
+    pk[2 + (r >> 3)][(r >> 1) & 3] = c;
+    if (r & 2) {
+      rb2 = add_bf16x2(a, rb2);
+      rb3 = add_bf16x2(c, rb3);
+    } else {
+      rb0 = add_bf16x2(a, rb0);
+      rb1 = add_bf16x2(c, rb1);
+    }
+  }
+  st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  st.lb += (rb0 + rb1) + (rb2 + rb3);
+  return rescale;
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(NT, 2) void prefill_kernel(
+__global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, void* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk, float c2,
     int n_qblk, int n_items) {
   using L = Layout<D>;
-  constexpr int NTILE = D / 32;  // O^T accumulator tiles
-  constexpr int NSTEP = D / 16;  // k-steps of the score product
-  __shared__ __attribute__((aligned(1024))) char smem[2 * L::STAGE];
+  constexpr int NTILE = L::NTILE;
+  constexpr int NSTEP = L::NSTEP;
+  __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool group_a = wave < NW / 2;
   const int h = lane >> 5, col = lane & 31;
 
   // ---- work item: (b, kv head, Q block, head in group); heavy blocks first
@@ -151,22 +327,26 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   if (CAUSAL) kv_end = min(Nk, q0 + BR + off);
   const int nblk = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
-  // ---- per-lane DMA source offsets (bytes within a block of 64 rows)
-  uint32_t koff[L::KPW], voff[L::VPW];
-#pragma unroll
-  for (int n = 0; n < L::KPW; ++n) {
-    const int gch = 64 * (wave + 4 * n) + lane;
-    const int row = gch / L::KCH, c = gch % L::KCH;
-    koff[n] = key_slot(row & 63) * L::ROWB + (c < D / 8 ? c : 0) * 16;
+  // this wave's rows: blocks from w_mask on may hide keys from one of them
+  // (past the causal limit of its first row, or past Nk)
+  const int wrow0 = q0 + wave * 32;
+  int w_mask = Nk / BC;
+  if (CAUSAL) w_mask = min(w_mask, max(0, wrow0 + off + 1) / BC);
+
+  // ---- per-lane DMA source offsets.  K: instruction i copies 16-byte
+  // chunk i of all 64 rows (lane = LDS row, holding key key_slot(lane)).
+  // V: instruction i copies the rows of its KiB, lane -> (row, chunk) with
+  // the 16-byte chunk index XOR-swizzled by the row.
+  const uint32_t k_off = key_slot(lane) * L::ROWB;
+  uint32_t v_off;
+  {
+    const int row = lane / (L::ROWB / 16);   // row within the KiB
+    const int p = lane % (L::ROWB / 16);     // physical 16-byte chunk
+    v_off = row * L::ROWB + ((p ^ (vswz<D>(row) >> 1)) * 16);
   }
-#pragma unroll
-  for (int n = 0; n < L::VPW; ++n) {
-    const int gch = 64 * (wave + 4 * n) + lane;
-    const int row = gch / L::VCH, c = gch % L::VCH;
-    voff[n] = (row & 63) * L::ROWB + (c < D / 8 ? c : 0) * 16;
-  }
+
   // ---- Q^T operand fragments: lane holds q[row][16t + 8h .. +7]
-  const int qrow = q0 + wave * 32 + col;
+  const int qrow = wrow0 + col;
   bf16x8 qf[NSTEP];
   {
     const bool ok = qrow < Nq;
@@ -181,150 +361,117 @@ __global__ __launch_bounds__(NT, 2) void prefill_kernel(
   f32x16 acc[NTILE];
 #pragma unroll
   for (int i = 0; i < NTILE; ++i) acc[i] = f32x16{};
-  float m = -INFINITY;  // reference max in use, log2 units
-  float l = 0.f;        // running sum over this lane's keys (fp32 weights)
-  float lb = 0.f;       // same over the bf16-rounded weights
+  RowState st{-INFINITY, 0.f, 0.f};
 
-  // per-lane LDS read bases (bytes from the stage start)
-  const int k_rd = col * L::KSTRIDE + 16 * h;
+  // per-lane LDS read bases.  K: chunk 2t + h of LDS row col sits at
+  // (2t + h) KiB + 16 col.  V (transposing read): 16-lane group lg, lane lp
+  // reads row 8(lg/2) + lp/4 (+16 s, +4), 8-byte chunk 8 tt + 4(lg%2) +
+  // lp%4, swizzled by the row.
+  const int k_rd = 1024 * h + 16 * col;
   const int lg = lane >> 4, lp = lane & 15;
-  const int v_rd = L::KBYTES + (8 * (lg >> 1) + (lp >> 2)) * L::VSTRIDE +
-                   (4 * (lg & 1) + (lp & 3)) * 8;
-
-  if (nblk > 0)
-    issue_dma<D>(smem, kh, vh, Nk, 0, 0, wave, koff, voff);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-
-  const int wrow0 = q0 + wave * 32;  // first query row of this wave
-
-  // One 64-key block.  MASK selects the variant that hides keys past the
-  // causal limit or past Nk; it is only used for the trailing blocks.
-  auto block = [&](int j, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const int kb = j * BC;
-    if (j + 1 < nblk)
-      issue_dma<D>(smem, kh, vh, Nk, j + 1, (j + 1) & 1, wave, koff, voff);
-    const char* st = smem + (j & 1) * L::STAGE;
-
-    // waves whose every row precedes this block's first key skip the math
-    const bool active = !CAUSAL || kb <= wrow0 + 31 + off;
-    if (active) {
-      // ---- S^T = K Q^T for the two 32-key halves
-      f32x16 s0 = f32x16{}, s1 = f32x16{};
-      const char* kp = st + k_rd;
+  int v_rd[NTILE];
+  {
+    const int vrow = 8 * (lg >> 1) + (lp >> 2);
 #pragma unroll
-      for (int t = 0; t < NSTEP; ++t) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kp + 32 * t);
-        const bf16x8 kc = *reinterpret_cast<const bf16x8*>(
-            kp + 32 * L::KSTRIDE + 32 * t);
-        s0 = mfma32x32x16(ka, qf[t], s0);
-        s1 = mfma32x32x16(kc, qf[t], s1);
-      }
-
-      if (MASK) {
-        // key index of register r (half 0): kb + 16(r/8) + 8h + r%8
-        const int lim =
-            (CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1) - kb - 8 * h;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = 16 * (r >> 3) + (r & 7);
-          if (kr > lim) s0[r] = -INFINITY;
-          if (kr + 32 > lim) s1[r] = -INFINITY;
-        }
-      }
-
-      // ---- online softmax, log2 domain, lazy reference max
-      float mx = fmaxf(s0[0], s1[0]);
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(fmaxf(mx, s0[r]), s1[r]);
-      mx = pair_max(mx) * c2;
-      if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold) != 0) {
-        const float m_new = fmaxf(m, mx);
-        // unchanged rows (including rows with nothing visible yet) keep
-        // factor 1; a first visible key gives 2^-inf = 0
-        const float alpha = (m_new == m) ? 1.f : exp2_fast(m - m_new);
-        m = m_new;
-        l *= alpha;
-        lb *= alpha;
-#pragma unroll
-        for (int i = 0; i < NTILE; ++i) acc[i] *= alpha;
-      }
-      // P is rounded to bf16 once.  The rounded weights feed the P V
-      // product and their own row sum lb, so O = acc / lb is an exact
-      // convex combination of V rows up to fp32 summation; the fp32 sum l
-      // of the unrounded weights gives lse.
-      const float msub = (m == -INFINITY) ? 0.f : m;
-      u32x4 pk[4];
-      float rs = 0.f, rb0 = 0.f, rb1 = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float e0 = exp2_fast(fmaf(s0[r], c2, -msub));
-        const float e1 = exp2_fast(fmaf(s0[r + 1], c2, -msub));
-        const float e2 = exp2_fast(fmaf(s1[r], c2, -msub));
-        const float e3 = exp2_fast(fmaf(s1[r + 1], c2, -msub));
-        rs += e0;
-        rs += e1;
-        rs += e2;
-        rs += e3;
-        const uint32_t a = pack_bf16x2(e0, e1);
-        const uint32_t c = pack_bf16x2(e2, e3);
-        pk[r >> 3][(r >> 1) & 3] = a;
-        pk[2 + (r >> 3)][(r >> 1) & 3] = c;
-        rb0 = add_bf16x2(a, rb0);
-        rb1 = add_bf16x2(c, rb1);
-      }
-      l += rs;
-      lb += rb0 + rb1;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pb[i] = __builtin_bit_cast(bf16x8, pk[i]);
-
-      // ---- O^T += V^T P^T
-      const char* vp = st + v_rd;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-#pragma unroll
-        for (int tt = 0; tt < NTILE; ++tt) {
-          const char* a0 = vp + s * 16 * L::VSTRIDE + tt * 64;
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(
-                  (__attribute__((address_space(3))) char*)a0));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) i16x4*)(
-                  (__attribute__((address_space(3))) char*)(
-                      a0 + 4 * L::VSTRIDE)));
-          u32x4 va;
-          va[0] = __builtin_bit_cast(u32x2, lo)[0];
-          va[1] = __builtin_bit_cast(u32x2, lo)[1];
-          va[2] = __builtin_bit_cast(u32x2, hi)[0];
-          va[3] = __builtin_bit_cast(u32x2, hi)[1];
-          acc[tt] = mfma32x32x16(__builtin_bit_cast(bf16x8, va), pb[s],
-                                 acc[tt]);
-        }
-      }
+    for (int tt = 0; tt < NTILE; ++tt) {
+      const int u = 8 * tt + 4 * (lg & 1) + (lp & 3);
+      v_rd[tt] = L::VBASE + vrow * L::ROWB + ((u ^ vswz<D>(vrow)) * 8);
     }
+  }
+  // this lane's row limit relative to its first key of block 0
+  const int lim0 = (CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1) - 8 * h;
 
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // this wave's DMA for block j+1
-    __syncthreads();
+  f32x16 s0, s1;    // scores of the block in flight
+  u32x4 pk[4];      // bf16 weights of the previous block
+
+  // matrix phase for block j: P_{j-1} V_{j-1} (P is zero before block 0),
+  // then the scores of block j when QK
+  bool rescale = false;  // scale acc by alpha before the next P V
+  float alpha = 1.f;
+  auto mphase = [&](int j, auto qk_tag) {
+    if (rescale) {
+#pragma unroll
+      for (int i = 0; i < NTILE; ++i) acc[i] *= alpha;
+    }
+    const char* vp[NTILE];
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt)
+      vp[tt] = smem + ((j + L::NS - 1) % L::NS) * L::VBYTES + v_rd[tt];
+    __builtin_amdgcn_s_setprio(1);
+    matrix_phase<D, true, decltype(qk_tag)::value>(
+        smem + (j % L::NS) * L::KBYTES + k_rd, vp, qf, pk, acc, s0, s1);
+    __builtin_amdgcn_s_setprio(0);
   };
 
-  // Block j needs no mask when (j + 1) * BC <= Nk and, if causal, when its
-  // last key is visible to the workgroup's first row: (j + 1) * BC <=
-  // q0 + off + 1.  Both conditions hold for a prefix of the blocks.
-  int j_mask = Nk / BC;
-  if (CAUSAL) j_mask = min(j_mask, max(0, q0 + off + 1) / BC);
-  j_mask = min(j_mask, nblk);
-  int j = 0;
-  for (; j < j_mask; ++j) block(j, std::false_type{});
-  for (; j < nblk; ++j) block(j, std::true_type{});
+  // ---- K/V ring: NS = 4 stages each; block b's K and V live in stage
+  // b % 4.  In iteration j every wave issues its share of the copies of
+  // K_{j+3} and V_{j+2} at the start of its softmax phase (vector memory
+  // issue then overlaps vector ALU work).  A stage is refilled only after
+  // both groups' last reads of it.  The first reader of K_{j+3} / V_{j+2}
+  // is group A's matrix phase of iteration j+3, so group A (whose softmax
+  // phases end one interval earlier) waits for its copies of iteration j at
+  // the end of iteration j+2, keeping 2 * OPS in flight, and group B at the
+  // end of iteration j+1, keeping OPS in flight.
+  constexpr int OPS = 2 * (L::NINS / NW);  // copy instructions per wave
+  const int kv_rows = max(kv_end, 0);      // rows past this are not needed
+  auto copies = [&](int j) {
+    copy_block<D>(smem + ((j + 3) % L::NS) * L::KBYTES, kh, kv_rows, j + 3,
+                  wave, k_off, 16);
+    copy_block<D>(smem + L::VBASE + ((j + 2) % L::NS) * L::VBYTES, vh,
+                  kv_rows, j + 2, wave, v_off, 1024);
+  };
+  // prologue: K_0, K_1, K_2, V_0, V_1 (all waves), fully waited.  V stage 3
+  // is zeroed: block 0's matrix phase multiplies it by the all-zero
+  // "previous" P, and 0 * (stale NaN/Inf bits) would not be 0.
+#pragma unroll
+  for (int b0 = 0; b0 < 3; ++b0)
+    copy_block<D>(smem + b0 * L::KBYTES, kh, kv_rows, b0, wave, k_off, 16);
+#pragma unroll
+  for (int b0 = 0; b0 < 2; ++b0)
+    copy_block<D>(smem + L::VBASE + b0 * L::VBYTES, vh, kv_rows, b0, wave,
+                  v_off, 1024);
+#pragma unroll
+  for (int i = tid; i < L::VBYTES / 16; i += NT)
+    reinterpret_cast<u32x4*>(smem + L::VBASE + 3 * L::VBYTES)[i] =
+        u32x4{0u, 0u, 0u, 0u};
+  wait_vmcnt<0>();
+  __syncthreads();
 
-  // ---- epilogue: O = O / l, lse = (m + log2 l) ln 2
-  const float lt = pair_sum(l);
-  const float lbt = pair_sum(lb);
+  // ---- main loop.  Every wave runs the same code, one barrier after each
+  // phase; group B enters one barrier late (an extra barrier before the
+  // loop) and group A leaves one late (an extra barrier at the end).
+  // Barrier n of one group then meets barrier n+1 of the other, so while
+  // group A runs the matrix phase of block j, group B runs the softmax of
+  // block j-1, and while A runs the softmax of j, B runs the matrix phase
+  // of j.  A block past all of a wave's rows (causal) goes through the
+  // masked softmax and contributes zero weights.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
+  if (!group_a) __syncthreads();
+  for (int j = 0; j < nblk; ++j) {
+    mphase(j, std::true_type{});
+    __syncthreads();
+    copies(j);
+    if (j >= w_mask)
+      rescale = softmax_phase<true>(s0, s1, lim0 - j * BC, c2, st, alpha, pk);
+    else
+      rescale = softmax_phase<false>(s0, s1, lim0 - j * BC, c2, st, alpha, pk);
+    if (group_a)
+      wait_vmcnt<2 * OPS>();  // own copies of iteration j-2 have landed
+    else
+      wait_vmcnt<OPS>();      // own copies of iteration j-1 have landed
+    __syncthreads();
+  }
+  if (nblk > 0) mphase(nblk, std::false_type{});  // P V of the last block
+  __syncthreads();
+  if (group_a) __syncthreads();
+
+  // ---- epilogue: O = O / lb, lse = (m + log2 l) ln 2
+  const float lt = pair_sum(st.l);
+  const float lbt = pair_sum(st.lb);
   const float inv = lbt > 0.f ? 1.f / lbt : 0.f;
   const float lse_v =
-      lt > 0.f ? (m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+      lt > 0.f ? (st.m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   if (qrow < Nq) {
     const int64_t orow = (qhead + qrow) * D;
 #pragma unroll

@@ -12,7 +12,9 @@ Prints ONE JSON line.
 Default workload: causal GQA prefill shaped like Qwen3-4B attention
 (B=1, Hq=32, Hkv=8, N=8192, d=128), the configuration the headline metric
 is quoted on.  ``--workload decode`` runs the single-query KV-split decode
-(B=16, Hq=32, Hkv=8, Nk=32768, d=128) and reports HBM GB/s instead.
+(B=16, Hq=32, Hkv=8, Nk=32768, d=128) and reports HBM GB/s instead; its
+timed step is the KV-split call with a workspace allocated once (partial
+kernel + merge kernel).
 
 The CPU baseline is the float64 oracle (test infrastructure) timed on the
 host on a bounded sample of the same workload: whole heads of the prefill,
@@ -40,10 +42,40 @@ from exact_io_aware_05_amd.metrics import (  # noqa: E402
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "tiny": 0}
-# HBM bytes per dispatch of the prefill kernel from rocprofv3 PMC counters
-# (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration factor);
-# None until counters have been taken for the current kernel.
-MEASURED_TRAFFIC = {}
+# HBM bytes per launch of each workload's dominant kernel, from two
+# rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch; summaries under profiles/).  Each counter is scaled by what it
+# reads for a plain device copy of known size (``--calibrate-copy``): a
+# 1 GiB copy reads FETCH_SIZE = 524301 KiB and WRITE_SIZE = 1048576 KiB.
+# A figure is reported only while the kernel source still hashes to the
+# value it was taken on; otherwise traffic is null.
+FETCH_SCALE = 1048576.0 / 524301.0
+WRITE_SCALE = 1048576.0 / 1048576.0
+MEASURED_TRAFFIC = {
+    "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
+        "source": "fa_prefill.hip",
+        "sha256": "c73f8cd525a209448786782812b59896fc3e0396d40456b7740b8982be02394d",
+        "fetch_kib": 71335.6, "write_kib": 66560.0},
+    "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
+        "source": "fa_splitkv.hip",
+        "sha256": "306a441bd62b0447f9f16819591f9ebd64c71d1fc8e40208d050919ddc47dc60",
+        "fetch_kib": 1048941.8, "write_kib": 2125.6},
+}
+
+
+def measured_traffic(name):
+    """HBM bytes per launch (counter-based) or None if not measured for the
+    current kernel source."""
+    import hashlib
+    rec = MEASURED_TRAFFIC.get(name)
+    if rec is None:
+        return None
+    path = os.path.join(ROOT, "exact_io_aware_05_amd", "csrc", rec["source"])
+    with open(path, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
+            return None
+    return int(round((rec["fetch_kib"] * FETCH_SCALE +
+                      rec["write_kib"] * WRITE_SCALE) * 1024))
 
 
 def _dev_tensor(bits):
@@ -85,6 +117,29 @@ def cpu_baseline(w, q, k, v, budget_s=10.0):
     }
 
 
+def calibrate_copy(mib, steps, warmup):
+    """Plain device-to-device copy of a known size: each launch reads and
+    writes exactly mib MiB, which calibrates the HBM byte counters."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    print(json.dumps({"calibration": "device copy", "bytes_read": n,
+                      "bytes_written": n, "steps": steps,
+                      "ms_per_copy": round(ms, 4),
+                      "GB/s_read+write": round(2 * n / ms / 1e6, 1)}),
+          flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +147,12 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="gqa_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="decode: KV splits (0: the library's default)")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="time a plain device-to-device copy of MIB MiB "
+                         "instead (the reference kernel for scaling HBM "
+                         "byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -103,6 +164,9 @@ def main(argv=None):
     import torch
     from exact_io_aware_05_amd import ops
 
+    if args.calibrate_copy:
+        return calibrate_copy(args.calibrate_copy, args.steps, args.warmup)
+
     w = workload(WORKLOADS[args.workload])
     q, k, v = make_inputs(w, seed=0)
     Q, K, V = _dev_tensor(q), _dev_tensor(k), _dev_tensor(v)
@@ -110,8 +174,23 @@ def main(argv=None):
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
-        ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
+    if w.Nq == 1:
+        # single-query decode: the KV-split path with a workspace allocated
+        # once, as a serving loop would hold it
+        splits = args.splits or ops.default_num_splits(w.B, w.Hq, w.Hkv, w.Nq,
+                                                       w.Nk, w.d)
+        ws = torch.empty(ops.splitkv_workspace_bytes(w.B, w.Hq, w.Nq, w.d,
+                                                     splits),
+                         dtype=torch.uint8, device="cuda")
+
+        def step():
+            ops.fa_fwd_splitkv(Q, K, V, splits, causal=w.causal, scale=w.scale,
+                               o=o, lse=lse, workspace=ws)
+    else:
+        splits = 0
+
+        def step():
+            ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
 
     for _ in range(args.warmup):
         step()
@@ -130,7 +209,7 @@ def main(argv=None):
 
     flops = attention_fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
     nbytes = attention_fwd_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
-    traffic = MEASURED_TRAFFIC.get(w.name)
+    traffic = measured_traffic(w.name)
     if w.Nq == 1:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit, metric = "GB/s", f"attn decode HBM GB/s ({w.name})"
@@ -164,6 +243,7 @@ def main(argv=None):
         "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
                    "scale": w.scale, "out_dtype": "bf16",
+                   "kv_splits": splits,
                    "kernel_ms": round(kern_ms, 4),
                    "pct_bf16_mfma_peak": round(100 * flops / (kern_ms * 1e-3)
                                                / 1e12 / PEAK_BF16_MFMA_TFLOPS, 2)},

@@ -62,13 +62,15 @@ int check_device() {
 
 // Heuristic for the KV-split form: used when the packed query rows of one
 // KV head (Nq * Hq / Hkv) are few (decode, short chunks); then enough chunks
-// to give about 2048 waves (8 per compute unit), each with >= 4 key blocks.
+// to give about 1024 waves (one per SIMD: the partial kernel holds its K/V
+// prefetch ring in registers and runs one wave per SIMD), each with >= 4
+// key blocks.
 int default_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   const long long R = (long long)Nq * (Hq / Hkv);
   if (R > 64) return 0;
   const long long units = (long long)B * Hkv * ((R + fa::kSplitRows - 1) / fa::kSplitRows);
   const long long nblk = (Nk + fa::kSplitKeys - 1) / fa::kSplitKeys;
-  long long s = (2048 + units - 1) / units;
+  long long s = (1024 + units - 1) / units;
   long long cap = nblk / 4;
   if (cap < 1) cap = 1;
   if (s > cap) s = cap;

@@ -138,13 +138,19 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   for (int i = 0; i < CPL; ++i) acc[i] = f32x16{};
   float m = -INFINITY, l = 0.f, lb = 0.f;
 
-  KvRegs<D> cur, nxt;
-  if (blk0 < blk1) cur.load(kh, vh, blk0 * KB, Nk, h, col);
-  for (int blk = blk0; blk < blk1; ++blk) {
-    const int kb = blk * KB;
-    const bool has_next = blk + 1 < blk1;
-    if (has_next) nxt.load(kh, vh, kb + KB, Nk, h, col);
+  // K/V blocks stream through a ring of PF register buffers: the loads of
+  // the next PF - 1 blocks are in flight while a block is computed (the
+  // step is HBM-bound, and one wave per SIMD needs that many bytes in
+  // flight to cover the memory latency).  The loop is unrolled by PF so
+  // that every buffer index is a compile-time constant.
+  constexpr int PF = 4;
+  KvRegs<D> buf[PF];
+#pragma unroll
+  for (int u = 0; u < PF - 1; ++u)
+    if (blk0 + u < blk1) buf[u].load(kh, vh, (blk0 + u) * KB, Nk, h, col);
 
+  auto compute = [&](const KvRegs<D>& cur, int blk) {
+    const int kb = blk * KB;
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t)
@@ -198,7 +204,19 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
       acc[tt] = mfma32x32x16(cur.vop(0, tt), p0, acc[tt]);
       acc[tt] = mfma32x32x16(cur.vop(1, tt), p1, acc[tt]);
     }
-    if (has_next) cur = nxt;
+  };
+
+  for (int blk = blk0; blk < blk1; blk += PF) {
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      if (blk + u < blk1) {
+        // refill the buffer the previous step consumed
+        if (blk + u + PF - 1 < blk1)
+          buf[(u + PF - 1) % PF].load(kh, vh, (blk + u + PF - 1) * KB, Nk, h,
+                                      col);
+        compute(buf[u], blk + u);
+      }
+    }
   }
 
   // ---- partial result of this chunk (unnormalised O, max m, sum l)

@@ -105,8 +105,9 @@ def test_splitkv_workspace_size(lib):
 
 
 def test_default_split_choice(lib):
-    # single-query decode over a 32K cache, 128 (batch, KV head) pairs
-    assert lib.fa_default_num_splits(16, 32, 8, 1, 32768, 128) == 16
+    # single-query decode over a 32K cache, 128 (batch, KV head) pairs:
+    # one wave per SIMD (1024 waves)
+    assert lib.fa_default_num_splits(16, 32, 8, 1, 32768, 128) == 8
     # prefill shapes use the tiled kernel
     assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 128) == 0
     assert lib.fa_default_num_splits(4, 16, 16, 2048, 2048, 64) == 0

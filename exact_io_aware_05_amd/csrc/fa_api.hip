@@ -141,6 +141,10 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
   if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
     return FA_ERR_UNSUPPORTED;
+  // the prefill kernel's buffer resources span one K/V head in 32-bit
+  // byte offsets
+  if (splits == 0 && (long long)Nk * d * 2 > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != FA_OK) return st;
   const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};

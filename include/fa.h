@@ -53,7 +53,8 @@
  *                       multiple of Hkv, scale not finite or negative, bad
  *                       out_dtype, workspace too small, num_splits < 1.
  *   FA_ERR_UNSUPPORTED  d not 64 or 128, sizes beyond the 64-bit/grid
- *                       limits, or the current device is not gfx950.
+ *                       limits or the 32-bit per-head K/V range of the
+ *                       prefill form, or the current device is not gfx950.
  *   FA_ERR_HIP          a HIP runtime or launch error; the hipError_t is
  *                       available from fa_last_hip_error() on the same
  *                       thread.  Outputs are then undefined.
@@ -81,9 +82,11 @@ enum { FA_OUT_BF16 = 0, FA_OUT_F32 = 1 };
 
 /*
  * Attention forward.  Picks the execution form by shape: the tiled prefill
- * kernel (a workgroup per block of 128 query rows of one head) when there
+ * kernel (a workgroup per block of 256 query rows of one head) when there
  * are enough query rows to fill the GPU, otherwise the KV-split form with
- * fa_default_num_splits() chunks.  The KV-split form needs a temporary fp32
+ * fa_default_num_splits() chunks.  The prefill form addresses one K or V
+ * head with 32-bit byte offsets, so Nk * d * 2 must stay below 2^31
+ * (FA_ERR_UNSUPPORTED otherwise; Nk < 8388608 at d = 128).  The KV-split form needs a temporary fp32
  * workspace (fa_splitkv_workspace_bytes), which this call takes with
  * hipMallocAsync on `stream` and returns with hipFreeAsync on the same
  * stream.  `stream` may be NULL (the null stream).

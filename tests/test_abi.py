@@ -88,6 +88,15 @@ def test_fwd_unsupported_head_dim(lib, d):
     assert _fwd(lib, d=d) == _lib.FA_ERR_UNSUPPORTED
 
 
+def test_fwd_prefill_kv_head_range(lib):
+    # one K/V head of the prefill form must span < 2^31 bytes
+    assert _fwd(lib, Hq=1, Hkv=1, Nq=4096, Nk=1 << 23, d=128) == \
+        _lib.FA_ERR_UNSUPPORTED
+    assert _fwd(lib, Hq=1, Hkv=1, Nq=4096, Nk=1 << 24, d=64) == \
+        _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+
+
 @pytest.mark.parametrize("kw", INVALID + [dict(S=0), dict(S=5000), dict(ws=None),
                                           dict(ws=P + 4), dict(wsb=16)],
                          ids=lambda k: str(k))

@@ -40,10 +40,13 @@
 //   one group issues its matrix products (P_{j-1} V_{j-1}, then
 //   S_j = Q K_j^T) while the other group does its softmax, then they swap.
 //   A wave raises its issue priority during its matrix phase.
-// * The output rescale is lazy: the reference max used for the
-//   exponentials only moves when some row's max grew by more than 2^8, so
-//   almost every block skips the 64 multiplies per lane.  The result is the
-//   same real-arithmetic quantity (the factor cancels in O = acc / l).
+// * The rescale is lazy: the reference max m used for the exponentials
+//   moves only when a block's weights against it would exceed 2^64 (or a
+//   row has no reference yet), so almost every block skips both the row
+//   max and the 64 multiplies per lane of the output rescale.  The result
+//   is the same real-arithmetic quantity: m cancels in O = acc / l and in
+//   lse = m + log l, and weights up to 2^64 keep every sum far inside the
+//   fp32 range.
 // * Causal: K/V blocks past the diagonal are never loaded; a wave whose rows
 //   all precede a block skips its math for that block; masking runs only on
 //   blocks that cross the wave's diagonal or the key tail.  Heavy Q blocks
@@ -62,7 +65,7 @@ constexpr int BR = kPrefillRows;   // 256 query rows per workgroup
 constexpr int BC = kPrefillKeys;   // 64 keys per K/V block
 constexpr int NW = BR / 32;        // 8 waves
 constexpr int NT = 64 * NW;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units
+constexpr float kMaxLaneSum = 1.8446744e19f;  // 2^64
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -217,12 +220,15 @@ __device__ __forceinline__ void matrix_phase(const char* kp,
 
 // Softmax phase of one wave for block j: optional mask (`lim`: last
 // visible key relative to this lane's first key of the block; register r of
-// half 0 holds relative key 16(r/8) + r%8, half 1 adds 32), row max, lazy
-// rescale of the state (returns true, with the factor in `alpha`, when the
-// accumulators must be scaled before the next P V), weights
-// p = 2^(s c2 - m) rounded to bf16 once into pk.  The rounded weights feed P V and their own
-// row sum lb, so O = acc / lb is an exact convex combination of V rows up to
-// fp32 summation; the fp32 sum l of the unrounded weights gives lse.
+// half 0 holds relative key 16(r/8) + r%8, half 1 adds 32), weights
+// p = 2^(s c2 - m) against the reference max m, rounded to bf16 once into
+// pk, and the row sums.  When the weights would grow past 2^64 (or a row
+// has no reference yet) the block is redone with m moved to the row max;
+// then the state is rescaled and true is returned, with the factor in
+// `alpha`, because the accumulators must be scaled before the next P V.
+// The rounded weights feed P V and their own row sum lb, so O = acc / lb
+// is an exact convex combination of V rows up to fp32 summation; the fp32
+// sum l of the unrounded weights gives lse.
 template <bool MASK>
 __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
                                               const f32x16& s1, int lim,
@@ -235,7 +241,59 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
   auto hide1 = [&](int r) {
     return MASK && 16 * (r >> 3) + (r & 7) + 32 > lim;
   };
-  // row max: four independent max3 chains, then combined
+  // weights p = 2^(s c2 - msub) (0 for hidden keys), rounded to bf16 once
+  // into pk; partial sums of the fp32 and of the rounded weights
+  auto weights = [&](float msub, float* rs, float* rb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rs[i] = 0.f;
+      rb[i] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float e0 = exp2_fast(fmaf(s0[r], c2, -msub));
+      float e1 = exp2_fast(fmaf(s0[r + 1], c2, -msub));
+      float e2 = exp2_fast(fmaf(s1[r], c2, -msub));
+      float e3 = exp2_fast(fmaf(s1[r + 1], c2, -msub));
+      if (hide0(r)) e0 = 0.f;
+      if (hide0(r + 1)) e1 = 0.f;
+      if (hide1(r)) e2 = 0.f;
+      if (hide1(r + 1)) e3 = 0.f;
+      rs[0] += e0;
+      rs[1] += e1;
+      rs[2] += e2;
+      rs[3] += e3;
+      const uint32_t a = pack_bf16x2(e0, e1);
+      const uint32_t c = pack_bf16x2(e2, e3);
+      pk[r >> 3][(r >> 1) & 3] = a;
+      pk[2 + (r >> 3)][(r >> 1) & 3] = c;
+      if (r & 2) {
+        rb[2] = add_bf16x2(a, rb[2]);
+        rb[3] = add_bf16x2(c, rb[3]);
+      } else {
+        rb[0] = add_bf16x2(a, rb[0]);
+        rb[1] = add_bf16x2(c, rb[1]);
+      }
+    }
+  };
+  float rs[4], rb[4];
+  // Fast path: the weights against the reference max m in use, without
+  // looking for the block's max.  They are kept when every lane's sum stays
+  // at most 2^64 (so every weight is <= 2^64, and the running sums and
+  // accumulators stay far inside fp32 range); otherwise, and while a row
+  // has no reference max yet, the block is redone below.
+  weights(st.m, rs, rb);
+  const float lsum = (rs[0] + rs[1]) + (rs[2] + rs[3]);
+  const bool redo = __builtin_amdgcn_ballot_w64(!(lsum <= kMaxLaneSum) ||
+                                                st.m == -INFINITY) != 0;
+  if (!redo) {
+    st.l += lsum;
+    st.lb += (rb[0] + rb[1]) + (rb[2] + rb[3]);
+    return false;
+  }
+  // Slow path: the row max of the block (four independent max3 chains,
+  // then combined); the reference moves to it where it grew, the state is
+  // rescaled, and the weights are recomputed.
   float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
   for (int r = 0; r < 16; ++r)
@@ -243,50 +301,17 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
                       hide1(r) ? -INFINITY : s1[r]);
   float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
   mx = pair_max(mx) * c2;
-  const bool rescale =
-      __builtin_amdgcn_ballot_w64(mx > st.m + kRescaleThreshold) != 0;
-  if (rescale) {
-    const float m_new = fmaxf(st.m, mx);
-    // unchanged rows (including rows with nothing visible yet) keep
-    // factor 1; a first visible key gives 2^-inf = 0
-    alpha = (m_new == st.m) ? 1.f : exp2_fast(st.m - m_new);
-    st.m = m_new;
-    st.l *= alpha;
-    st.lb *= alpha;
-  }
-  const float msub = (st.m == -INFINITY) ? 0.f : st.m;
-  // sums: independent partial chains (fixed order, combined at the end)
-  float rs[4] = {0.f, 0.f, 0.f, 0.f};
-  float rb0 = 0.f, rb1 = 0.f, rb2 = 0.f, rb3 = 0.f;
-#pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    float e0 = exp2_fast(fmaf(s0[r], c2, -msub));
-    float e1 = exp2_fast(fmaf(s0[r + 1], c2, -msub));
-    float e2 = exp2_fast(fmaf(s1[r], c2, -msub));
-    float e3 = exp2_fast(fmaf(s1[r + 1], c2, -msub));
-    if (hide0(r)) e0 = 0.f;
-    if (hide0(r + 1)) e1 = 0.f;
-    if (hide1(r)) e2 = 0.f;
-    if (hide1(r + 1)) e3 = 0.f;
-    rs[0] += e0;
-    rs[1] += e1;
-    rs[2] += e2;
-    rs[3] += e3;
-    const uint32_t a = pack_bf16x2(e0, e1);
-    const uint32_t c = pack_bf16x2(e2, e3);
-    pk[r >> 3][(r >> 1) & 3] = a;
-    pk[2 + (r >> 3)][(r >> 1) & 3] = c;
-    if (r & 2) {
-      rb2 = add_bf16x2(a, rb2);
-      rb3 = add_bf16x2(c, rb3);
-    } else {
-      rb0 = add_bf16x2(a, rb0);
-      rb1 = add_bf16x2(c, rb1);
-    }
-  }
+  const float m_new = fmaxf(st.m, mx);
+  // unchanged rows (including rows with nothing visible yet) keep factor
+  // 1; a first visible key gives 2^-inf = 0
+  alpha = (m_new == st.m) ? 1.f : exp2_fast(st.m - m_new);
+  st.m = m_new;
+  st.l *= alpha;
+  st.lb *= alpha;
+  weights((st.m == -INFINITY) ? 0.f : st.m, rs, rb);
   st.l += (rs[0] + rs[1]) + (rs[2] + rs[3]);
-  st.lb += (rb0 + rb1) + (rb2 + rb3);
-  return rescale;
+  st.lb += (rb[0] + rb[1]) + (rb[2] + rb[3]);
+  return true;
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>

@@ -145,3 +145,33 @@ def test_workload_gqa_prefill():
 
 def test_workload_decode():
     _workload_parity(4)
+
+
+def _scaled_keys(B, H, N, d, seed, lo, hi, factor):
+    """Seeded N(0,1) Q/K/V with the keys lo..hi-1 scaled by `factor`
+    (before the bf16 rounding), so the scores jump between K/V blocks."""
+    from fa_inputs import f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    k = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    v = rng.standard_normal((B, H, N, d), dtype=np.float32)
+    k[:, :, lo:hi, :] *= np.float32(factor)
+    return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+@pytest.mark.parametrize("pattern", ["grow", "shrink"])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_scores_jumping_between_blocks(pattern, causal, d):
+    """Scores that grow (or fall) by far more than any reference-max
+    threshold from one K/V block to the next: the running max must move and
+    the accumulated output be rescaled (or later weights underflow)."""
+    N = 400
+    lo, hi = (130, N) if pattern == "grow" else (0, 70)
+    q, k, v = _scaled_keys(1, 2, N, d, seed=11, lo=lo, hi=hi, factor=40.0)
+    scale = 1.0 / math.sqrt(d)
+    O, L = _run(_fa().fa_fwd, q, k, v, causal=causal, scale=scale,
+                out_dtype=torch.float32)
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=causal,
+                                       scale=float(np.float32(scale)))
+    compare(O, L, O_ref, L_ref, what=f"jump {pattern} d{d} causal={causal}")

@@ -1,4 +1,5 @@
-"""float64 CPU oracle for the fused exact attention forward.
+"""float64 CPU oracle for the fused exact attention forward and its
+backward pass.
 
 TEST INFRASTRUCTURE ONLY: imported by the test suite, the package smoke
 check and the benchmark's CPU-baseline leg, never by the GPU library.
@@ -6,4 +7,7 @@ check and the benchmark's CPU-baseline leg, never by the GPU library.
 from .attention import (  # noqa: F401
     visible_mask, kv_head_of, reference_attention, tiled_online_attention,
     splitkv_partials, merge_partials, splitkv_attention, split_bounds,
+)
+from .backward import (  # noqa: F401
+    reference_attention_backward, recompute_backward,
 )

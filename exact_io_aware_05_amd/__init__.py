@@ -1,4 +1,4 @@
-"""Fused exact attention forward for AMD MI355X (gfx950).
+"""Fused exact attention forward and backward for AMD MI355X (gfx950).
 
 The compute lives in ``libfa.so`` (hand-written HIP kernels behind the C
 interface of ``include/fa.h``); ``ops`` is its PyTorch binding.
@@ -8,7 +8,7 @@ import importlib
 from ._lib import FAError, load  # noqa: F401
 
 _LAZY = ("fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
-         "default_num_splits")
+         "default_num_splits", "fa_bwd", "bwd_workspace_bytes")
 
 
 def __getattr__(name):

@@ -162,4 +162,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return hip_status(e2);
 }
 
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq) {
+  if (B < 1 || Hq < 1 || Nq < 1) return 0;
+  return fa::backward_workspace_bytes((long long)B * Hq * Nq);
+}
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+           float scale, int grad_dtype, void* workspace,
+           size_t workspace_bytes, hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        grad_dtype);
+  if (st != FA_OK) return st;
+  if (!dout || !dq || !dk || !dv || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  const long long rows = (long long)B * Hq * Nq;
+  if (workspace_bytes < fa::backward_workspace_bytes(rows))
+    return FA_ERR_INVALID_ARG;
+  // grids: one workgroup per 128 keys of a KV head, per 128 rows of a
+  // query head, and per 256 threads of the row preprocessing
+  if ((long long)B * Hkv * ((Nk + 127) / 128) > (1LL << 31) - 1 ||
+      (long long)B * Hq * ((Nq + 127) / 128) > (1LL << 31) - 1 ||
+      rows * (d / 8) / 256 > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  return hip_status(fa::launch_backward(q, k, v, o, lse, dout, dq, dk, dv, s,
+                                        grad_dtype == FA_OUT_F32, workspace,
+                                        stream));
+}
+
 }  // extern "C"

@@ -32,4 +32,13 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
 
 size_t splitkv_workspace_bytes(long long rows, int d, int num_splits);
 
+// Backward pass: D and lse * log2(e) per query row in `workspace`, then the
+// dK/dV and dQ kernels.  `o` and `dout` are bf16.
+hipError_t launch_backward(const void* q, const void* k, const void* v,
+                           const void* o, const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv, const Shape& s,
+                           bool out_f32, void* workspace, hipStream_t stream);
+
+size_t backward_workspace_bytes(long long rows);
+
 }  // namespace fa

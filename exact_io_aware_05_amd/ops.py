@@ -6,6 +6,8 @@ current HIP stream; every step of the computation runs in the HIP kernels of
 
     q [B, Hq, Nq, d] bf16,  k, v [B, Hkv, Nk, d] bf16
     o [B, Hq, Nq, d] bf16 or fp32,  lse [B, Hq, Nq] fp32 (natural log)
+    backward: do [B, Hq, Nq, d] bf16; dq like q, dk and dv like k, in bf16
+    or fp32
 """
 from __future__ import annotations
 
@@ -16,7 +18,7 @@ import torch
 from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
-           "default_num_splits"]
+           "default_num_splits", "fa_bwd", "bwd_workspace_bytes"]
 
 
 def _dims(q, k, v):
@@ -96,3 +98,50 @@ def fa_fwd_splitkv(q, k, v, num_splits, causal=False, scale=None,
         int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q))
     check(st, "fa_fwd_splitkv")
     return o, lse
+
+
+def bwd_workspace_bytes(B, Hq, Nq) -> int:
+    return int(load().fa_bwd_workspace_bytes(B, Hq, Nq))
+
+
+def _grad(name, t, shape, dtype, like):
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} has the wrong dtype, shape or layout")
+    return t
+
+
+def fa_bwd(q, k, v, o, lse, do, causal=False, scale=None,
+           grad_dtype=torch.bfloat16, dq=None, dk=None, dv=None,
+           workspace=None):
+    """Attention backward through ``fa_bwd`` from the forward inputs, its
+    bf16 output ``o`` and ``lse``, and the incoming gradient ``do``;
+    returns ``(dq, dk, dv)``."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    for name, t in (("o", o), ("do", do)):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16
+                or tuple(t.shape) != (B, Hq, Nq, d) or not t.is_contiguous()
+                or not t.is_cuda):
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor "
+                             "shaped like q")
+    if (not isinstance(lse, torch.Tensor) or lse.dtype != torch.float32
+            or tuple(lse.shape) != (B, Hq, Nq) or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous fp32 tensor [B, Hq, Nq]")
+    if grad_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("grad_dtype must be torch.bfloat16 or torch.float32")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = _grad("dq", dq, q.shape, grad_dtype, q)
+    dk = _grad("dk", dk, k.shape, grad_dtype, q)
+    dv = _grad("dv", dv, k.shape, grad_dtype, q)
+    need = bwd_workspace_bytes(B, Hq, Nq)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = load().fa_bwd(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+        FA_OUT_F32 if grad_dtype == torch.float32 else FA_OUT_BF16,
+        workspace.data_ptr(), workspace.numel(), _stream(q))
+    check(st, "fa_bwd")
+    return dq, dk, dv

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the fused attention forward, shared by the
+"""Seeded synthetic inputs for the fused attention forward and backward, shared by the
 oracle side and the GPU side.
 
 This module holds no attention arithmetic.  It only
@@ -16,7 +16,9 @@ draw Q, K, V in that order with ``standard_normal(dtype=float32)``; for the
 outlier workload then draw the Q mask and the K mask as
 ``random() < 0.01`` (independent Bernoulli(0.01) per element) and multiply
 the selected entries by 8 (a power of two, so exact before or after the
-bf16 rounding); finally round every fp32 value to bf16.
+bf16 rounding); finally round every fp32 value to bf16.  The incoming
+gradient dO of the backward pass is drawn N(0, 1) the same way from
+``default_rng([seed, 0x64])``.
 """
 from __future__ import annotations
 
@@ -26,7 +28,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv",
+    "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv", "make_dout",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
 ]
 
@@ -133,6 +135,15 @@ def make_qkv(B, Hq, Hkv, Nq, Nk, d, *, seed=0, outliers=False,
         q = np.where(mq, q * np.float32(8.0), q).astype(np.float32)
         k = np.where(mk, k * np.float32(8.0), k).astype(np.float32)
     return f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v)
+
+
+def make_dout(B, Hq, Nq, d, *, seed=0):
+    """The incoming gradient dO of the backward pass: i.i.d. N(0, 1) fp32
+    cast to bf16 (bit patterns), from a stream of its own so that it is
+    independent of Q, K, V drawn with the same seed."""
+    rng = np.random.default_rng([seed, 0x64])
+    return f32_to_bf16_bits(rng.standard_normal((B, Hq, Nq, d),
+                                                dtype=np.float32))
 
 
 def make_inputs(w, seed=0):

@@ -1,5 +1,5 @@
 /*
- * fa.h - fused exact attention forward for AMD MI355X (gfx950).
+ * fa.h - fused exact attention forward and backward for AMD MI355X (gfx950).
  *
  * The library computes, for every batch b and query head hq,
  *
@@ -122,6 +122,41 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
  * HIP call.  Returns 0 for invalid sizes as well.
  */
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
+
+/*
+ * Attention backward pass by recomputation ("FlashAttention Analysis",
+ * ryotta.opik.net, section 4 "Recomputation"; the per-row logsumexp kept
+ * for it: cost guide, section on attention memory during training).  Given
+ * the forward inputs, the forward output `o` (bf16) and `lse` of fa_fwd
+ * for the same arguments, and the incoming gradient `dout` (bf16, the
+ * layout of o), computes
+ *
+ *     D_i = dout_i . o_i,   P = exp(scale q k^T - lse) on visible keys,
+ *     dv = P^T dout,   ds = P (dout v^T - D),
+ *     dq = scale ds k,   dk = scale ds^T q,
+ *
+ * the scores and probabilities recomputed tile by tile and never stored.
+ * With grouped-query attention dk and dv of a KV head are the sums over the
+ * Hq/Hkv query heads that read it.  Rows whose lse is -inf (no visible key)
+ * contribute nothing.
+ *   dq       [B, Hq,  Nq, d]   written, not accumulated into
+ *   dk, dv   [B, Hkv, Nk, d]   written, not accumulated into
+ * in bf16 (grad_dtype FA_OUT_BF16) or fp32 (FA_OUT_F32); all device
+ * pointers, 16-byte aligned (lse 4-byte).  `workspace` is a device buffer of
+ * at least fa_bwd_workspace_bytes(B, Hq, Nq) bytes (two fp32 per query
+ * row), 16-byte aligned, scratch on return.  Three kernels are enqueued on
+ * `stream`; each output element is written by exactly one workgroup (no
+ * atomics), so results are deterministic.  Argument checks and status
+ * codes as for fa_fwd (d 64 or 128); FA_ERR_INVALID_ARG also for a missing
+ * or small workspace.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq);
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o,
+           const float* lse, const void* dout, void* dq, void* dk, void* dv,
+           int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
+           float scale, int grad_dtype, void* workspace,
+           size_t workspace_bytes, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);

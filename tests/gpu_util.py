@@ -46,3 +46,31 @@ def compare(O, lse, O_ref, lse_ref, o_tol=O_TOL, lse_tol=LSE_TOL, what=""):
             f"got {O[idx]:.6f}, oracle {O_ref[idx]:.6f}")
     assert el <= lse_tol, f"{what}: max |dlse| = {el:.3e} > {lse_tol}"
     return eo, el
+
+
+# Gradients: max |g - g_ref| <= GRAD_TOL * max |g_ref| + GRAD_ATOL per
+# tensor.  Every gradient is a sum of products in which one factor (P or
+# dS) was rounded to bf16 (relative error <= 2^-9) and D = dO . O uses the
+# bf16 O; the relative bound is the O tolerance of the forward with the
+# gradient's own scale in place of the unit scale of O.  The absolute term
+# covers gradients that cancel to zero in exact arithmetic (a single key,
+# uniform weights): dP - D is then the difference of two fp32 sums of
+# terms below 100 in magnitude for unit-normal inputs (residue ~1e-6),
+# times scale * |k| or |q|.
+GRAD_TOL = 1e-2
+GRAD_ATOL = 1e-5
+
+
+def compare_grad(g, ref, tol=GRAD_TOL, atol=GRAD_ATOL, what=""):
+    assert g.shape == ref.shape, (what, g.shape, ref.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite gradient"
+    if g.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(g - ref)))
+    if err > tol * scale + atol:
+        idx = np.unravel_index(np.argmax(np.abs(g - ref)), g.shape)
+        raise AssertionError(
+            f"{what}: max |err| = {err:.3e} > {tol} * {scale:.3e} + {atol} at "
+            f"{tuple(map(int, idx))}: got {g[idx]:.6f}, oracle {ref[idx]:.6f}")
+    return err / scale if scale > 0 else err

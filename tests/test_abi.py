@@ -128,7 +128,42 @@ def test_default_split_choice(lib):
     assert lib.fa_default_num_splits(1, 1, 1, 1, 64, 80) == 0
 
 
+def _bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4,
+             Hkv=2, Nq=16, Nk=16, d=64, causal=0, scale=0.125, out=0, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"],
+                      a["dq"], a["dk"], a["dv"], a["B"], a["Hq"], a["Hkv"],
+                      a["Nq"], a["Nk"], a["d"], a["causal"], a["scale"],
+                      a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize(
+    "kw", INVALID + [dict(do=None), dict(dq=None), dict(dk=None), dict(dv=None),
+                     dict(do=P + 8), dict(dq=P + 2), dict(dk=P + 4),
+                     dict(dv=P + 1), dict(ws=None), dict(ws=P + 4),
+                     dict(wsb=4 * 16 * 8 - 1)],
+    ids=lambda k: str(k))
+def test_bwd_invalid_arguments(lib, kw):
+    assert _bwd(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_bwd_unsupported_head_dim(lib, d):
+    assert _bwd(lib, d=d) == _lib.FA_ERR_UNSUPPORTED
+
+
+def test_bwd_workspace_size(lib):
+    # D and lse * log2(e): two fp32 per query row
+    assert lib.fa_bwd_workspace_bytes(1, 32, 8192) == 32 * 8192 * 8
+    assert lib.fa_bwd_workspace_bytes(2, 3, 5) == 2 * 3 * 5 * 8
+    assert lib.fa_bwd_workspace_bytes(0, 1, 1) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 1, 0) == 0
+
+
 def test_no_hip_error_recorded_by_validation(lib):
     _fwd(lib, q=None)
     _split(lib, S=0)
+    _bwd(lib, ws=None)
     assert lib.fa_last_hip_error() == 0

@@ -14,7 +14,10 @@ Default workload: causal GQA prefill shaped like Qwen3-4B attention
 is quoted on.  ``--workload decode`` runs the single-query KV-split decode
 (B=16, Hq=32, Hkv=8, Nk=32768, d=128) and reports HBM GB/s instead; its
 timed step is the KV-split call with a workspace allocated once (partial
-kernel + merge kernel).
+kernel + merge kernel).  ``--workload gqa_prefill_bwd`` times the backward
+pass of the GQA prefill: one ``fa_bwd`` call (row preprocessing, dK/dV
+kernel, dQ kernel) per step, from the O and lse of one untimed forward,
+priced at 2.5 times the forward FLOPs; its roofline covers the whole call.
 
 The CPU baseline is the float64 oracle (test infrastructure) timed on the
 host on a bounded sample of the same workload: whole heads of the prefill,
@@ -34,14 +37,14 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from fa_inputs import make_inputs, workload  # noqa: E402
+from fa_inputs import make_dout, make_inputs, workload  # noqa: E402
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
-    PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_fwd_bytes,
-    attention_fwd_flops)
+    PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_bwd_flops,
+    attention_fwd_bytes, attention_fwd_flops)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
-             "tiny": 0}
+             "tiny": 0, "gqa_prefill_bwd": 3}
 # HBM bytes per launch of each workload's dominant kernel, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch; summaries under profiles/).  Each counter is scaled by what it
@@ -83,10 +86,11 @@ def _dev_tensor(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def cpu_baseline(w, q, k, v, budget_s=10.0):
-    """Oracle TFLOP/s on whole heads of batch 0, one head at a time."""
+def cpu_baseline(w, q, k, v, budget_s=10.0, do=None):
+    """Oracle TFLOP/s on whole heads of batch 0, one head at a time (the
+    gradient oracle when ``do`` is given)."""
     from fa_inputs import bf16_bits_to_f64
-    from oracle import reference_attention
+    from oracle import reference_attention, reference_attention_backward
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()
@@ -103,16 +107,23 @@ def cpu_baseline(w, q, k, v, budget_s=10.0):
         kh = bf16_bits_to_f64(k[:1, h // G:h // G + 1])
         vh = bf16_bits_to_f64(v[:1, h // G:h // G + 1])
         t0 = time.perf_counter()
-        reference_attention(qh, kh, vh, causal=w.causal, scale=scale)
+        if do is None:
+            reference_attention(qh, kh, vh, causal=w.causal, scale=scale)
+        else:
+            reference_attention_backward(
+                qh, kh, vh, bf16_bits_to_f64(do[:1, h:h + 1]),
+                causal=w.causal, scale=scale)
         t_total += time.perf_counter() - t0
         done += 1
-    flops = attention_fwd_flops(1, done, w.Nq, w.Nk, w.d, w.causal)
+    count = attention_fwd_flops if do is None else attention_bwd_flops
+    flops = count(1, done, w.Nq, w.Nk, w.d, w.causal)
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{done} of {w.B * w.Hq} heads (batch 0, heads 0..{done - 1}), "
+        "sample": f"{'gradients of ' if do is not None else ''}"
+                  f"{done} of {w.B * w.Hq} heads (batch 0, heads 0..{done - 1}), "
                   f"all {w.Nq} query rows each, float64 numpy; {t_total:.1f} s",
     }
 
@@ -168,6 +179,7 @@ def main(argv=None):
         return calibrate_copy(args.calibrate_copy, args.steps, args.warmup)
 
     w = workload(WORKLOADS[args.workload])
+    backward = args.workload.endswith("_bwd")
     q, k, v = make_inputs(w, seed=0)
     Q, K, V = _dev_tensor(q), _dev_tensor(k), _dev_tensor(v)
     o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
@@ -186,6 +198,20 @@ def main(argv=None):
         def step():
             ops.fa_fwd_splitkv(Q, K, V, splits, causal=w.causal, scale=w.scale,
                                o=o, lse=lse, workspace=ws)
+    elif backward:
+        splits = 0
+        do = make_dout(w.B, w.Hq, w.Nq, w.d, seed=0)
+        DO = _dev_tensor(do)
+        ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
+        dq = torch.empty_like(Q)
+        dk = torch.empty_like(K)
+        dv = torch.empty_like(V)
+        ws = torch.empty(ops.bwd_workspace_bytes(w.B, w.Hq, w.Nq),
+                         dtype=torch.uint8, device="cuda")
+
+        def step():
+            ops.fa_bwd(Q, K, V, o, lse, DO, causal=w.causal, scale=w.scale,
+                       dq=dq, dk=dk, dv=dv, workspace=ws)
     else:
         splits = 0
 
@@ -207,9 +233,10 @@ def main(argv=None):
     kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
-    flops = attention_fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    count = attention_bwd_flops if backward else attention_fwd_flops
+    flops = count(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
     nbytes = attention_fwd_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
-    traffic = measured_traffic(w.name)
+    traffic = measured_traffic(args.workload if backward else w.name)
     if w.Nq == 1:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit, metric = "GB/s", f"attn decode HBM GB/s ({w.name})"
@@ -219,8 +246,13 @@ def main(argv=None):
                 "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
     else:
         value = flops / (ms_per_step * 1e-3) / 1e12
-        unit, metric = "TFLOP/s", METRIC if w.name == workload(3).name else \
-            f"attn fwd TFLOP/s ({w.name})"
+        if backward:
+            metric = f"attn bwd TFLOP/s ({w.name})"
+        elif w.name == workload(3).name:
+            metric = METRIC
+        else:
+            metric = f"attn fwd TFLOP/s ({w.name})"
+        unit = "TFLOP/s"
         achieved = flops / (kern_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
@@ -240,9 +272,11 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) fp32 rounded to bf16)",
-        "config": {"workload": w.name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+        "config": {"workload": w.name + ("_backward" if backward else ""),
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
-                   "scale": w.scale, "out_dtype": "bf16",
+                   "scale": w.scale,
+                   ("grad_dtype" if backward else "out_dtype"): "bf16",
                    "kv_splits": splits,
                    "kernel_ms": round(kern_ms, 4),
                    "pct_bf16_mfma_peak": round(100 * flops / (kern_ms * 1e-3)
@@ -251,7 +285,8 @@ def main(argv=None):
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, q, k, v)
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v,
+                                           do=do if backward else None)
         if w.Nq == 1:
             cb = out["cpu_baseline"]
             cb["note"] = "oracle TFLOP/s (decode bytes are not a CPU metric)"

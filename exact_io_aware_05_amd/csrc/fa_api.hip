@@ -182,6 +182,11 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
   const long long rows = (long long)B * Hq * Nq;
   if (workspace_bytes < fa::backward_workspace_bytes(rows))
     return FA_ERR_INVALID_ARG;
+  // the kernels address one head of Q / dO (and of K / V) with 32-bit byte
+  // offsets, up to one 128-row step past its end
+  if (((long long)Nq + 128) * d * 2 > (1LL << 31) - 1 ||
+      ((long long)Nk + 128) * d * 2 > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
   // grids: one workgroup per 128 keys of a KV head, per 128 rows of a
   // query head, and per 256 threads of the row preprocessing
   if ((long long)B * Hkv * ((Nk + 127) / 128) > (1LL << 31) - 1 ||

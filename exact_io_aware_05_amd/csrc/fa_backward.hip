@@ -147,6 +147,71 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Register prefetch of the next pair of row tiles (R rows each, R = one
+// wave's lanes: Q and dO, or K and V) and, with STATS, the lse2 and D
+// values of the rows; stored to an LDS buffer laid out as [first tile |
+// second tile | lse2[R] | D[R]] after the current step's products.  The
+// loads go through buffer resources spanning one head, so rows past its
+// end read as zeros.
+template <int D, int R, bool STATS>
+struct TilePrefetch {
+  using T = Tiles<D>;
+  static constexpr int CPR = D / 8;               // 16-byte chunks per row
+  static constexpr int N = 2 * R * CPR / NT;      // chunks per thread
+  static constexpr int BYTES = 2 * R * T::ROWP + (STATS ? 2 * R * 4 : 0);
+  static_assert(N * NT == 2 * R * CPR && N % 2 == 0 && R == 64, "tile split");
+  u32x4 x[N];
+  float st;
+
+  // ra, rb: the two tiles' heads (rows of D bf16)
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra,
+                                       __amdgpu_buffer_rsrc_t rb, int r0) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = threadIdx.x + NT * (j % (N / 2));
+      const int r = i / CPR, c = i % CPR;
+      x[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     j < N / 2 ? ra : rb, (r0 + r) * (2 * D) + 16 * c, 0, 0));
+    }
+  }
+  // rl, rv: lse2 and D of the head; waves 0 and 1 fetch one each (a
+  // wave-uniform choice)
+  __device__ __forceinline__ void load_stats(__amdgpu_buffer_rsrc_t rl,
+                                             __amdgpu_buffer_rsrc_t rv,
+                                             int r0) {
+    if (threadIdx.x < R)
+      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         rl, (r0 + threadIdx.x) * 4, 0, 0));
+    else if (threadIdx.x < 2 * R)
+      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                         rv, (r0 + threadIdx.x - R) * 4, 0, 0));
+  }
+  __device__ __forceinline__ void store(char* buf) const {
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      const int i = threadIdx.x + NT * (j % (N / 2));
+      const int r = i / CPR, c = i % CPR;
+      *reinterpret_cast<u32x4*>(buf + (j < N / 2 ? 0 : R * T::ROWP) +
+                                r * T::ROWP + 16 * c) = x[j];
+    }
+    if (STATS && threadIdx.x < 2 * R)
+      reinterpret_cast<float*>(buf + 2 * R * T::ROWP)[threadIdx.x] = st;
+  }
+};
+
+// lse2 / D of the 16 score registers of one 32-row half (register i holds
+// tile row 16(i/8) + 8h + i%8 of the half)
+__device__ __forceinline__ void row_stats(const float* v, int h, float* out) {
+#pragma unroll
+  for (int i = 0; i < 16; i += 4) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(v + 16 * (i >> 3) + 8 * h +
+                                                    (i & 7));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[i + e] = a[e];
+  }
+}
+
 template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -156,11 +221,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
     int Nk, float c2, float scale, int n_kblk) {
   using T = Tiles<D>;
   constexpr int NSTEP = T::NSTEP, NTILE = T::NTILE;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 32 * T::ROWP + 256];
-  char* qt = smem;                    // Q tile, 32 rows
-  char* dt = smem + 32 * T::ROWP;     // dO tile
-  float* ls = reinterpret_cast<float*>(smem + 2 * 32 * T::ROWP);  // lse2[32]
-  float* dd = ls + 32;                                             // D[32]
+  constexpr int QR = 64;  // query rows per step
+  using Pf = TilePrefetch<D, QR, true>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Pf::BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -169,14 +232,13 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
   // work item: (b, kv head, key block of 128); causal: early keys (more
   // query rows to visit) first
   const int item = xcd_contiguous(blockIdx.x, gridDim.x);
-  const int jb = item % n_kblk;
+  const int kblk = item % n_kblk;
   const int bh = item / n_kblk;  // b * Hkv + hkv
-  const int kblk = jb;
   const int b = bh / Hkv, hkv = bh % Hkv;
   const int G = Hq / Hkv;
   const int off = Nk - Nq;
-  const int key0 = kblk * 128 + wave * 32;  // this wave's first key
-  const int key = key0 + col;               // this lane's key
+  const int kfirst = kblk * 128;
+  const int key = kfirst + wave * 32 + col;  // this lane's key
 
   // K and V of the wave's keys as B operands: lane (col, h) holds
   // [key][16t + 8h .. +7]
@@ -198,71 +260,102 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
     dvt[i] = f32x16{};
   }
 
-  // query rows that can see a key of this workgroup: causal rows i with
-  // i + off >= first key
-  const int kfirst = kblk * 128;
-  const int q_begin = CAUSAL ? max(0, kfirst - off) : 0;
-  const int t_begin = q_begin / 32;
-  const int n_qt = (Nq + 31) / 32;
+  // query rows that can see a key of this workgroup (causal: rows i with
+  // i + off >= its first key), in steps of QR rows, for each of the G query
+  // heads of the group
+  const int t_begin = CAUSAL ? max(0, kfirst - off) / QR : 0;
+  const int t_end = (Nq + QR - 1) / QR;
+  const int n_it = G * (t_end - t_begin);
+  const bool keys_in = kfirst + 128 <= Nk;
   const int arow = row_slot(col);  // tile row read for operand row col
+  const uint32_t head_bytes = (uint32_t)Nq * (2 * D);
 
-  for (int g = 0; g < G; ++g) {
-    const int hq = hkv * G + g;
-    const int64_t qhead = (int64_t)(b * Hq + hq) * Nq;
-    for (int tq = t_begin; tq < n_qt; ++tq) {
-      const int q0 = tq * 32;
-      __syncthreads();  // previous tile fully read
-      stage_rows<D, 32>(qt, q + qhead * D, q0, Nq);
-      stage_rows<D, 32>(dt, dout + qhead * D, q0, Nq);
-      if (threadIdx.x < 32) {
-        const int r = q0 + threadIdx.x;
-        ls[threadIdx.x] = r < Nq ? lse2[qhead + r] : 0.f;
-        dd[threadIdx.x] = r < Nq ? dvec[qhead + r] : 0.f;
-      }
-      __syncthreads();
-      // S = Q K^T and dP = dO V^T: C row 8(i/4) + 4h + i%4 is tile row
-      // row_slot of it = 16(i/8) + 8h + i%8 (register i), column = key
+  // (g, t): query head within the group and row step of the next prefetch
+  int pg = 0, pt = t_begin;
+  Pf pf;
+  auto prefetch = [&]() {
+    const int64_t qh = (int64_t)(b * Hq + hkv * G + pg) * Nq;
+    pf.load(buffer_rsrc(q + qh * D, head_bytes),
+            buffer_rsrc(dout + qh * D, head_bytes), pt * QR);
+    pf.load_stats(buffer_rsrc(lse2 + qh, (uint32_t)Nq * 4),
+                  buffer_rsrc(dvec + qh, (uint32_t)Nq * 4), pt * QR);
+    if (++pt == t_end) {
+      pt = t_begin;
+      ++pg;
+    }
+  };
+  if (n_it > 0) {
+    prefetch();
+    pf.store(smem);
+  }
+  __syncthreads();
+
+  int ct_row = t_begin;  // row step being computed
+  for (int it = 0; it < n_it; ++it) {
+    const char* buf = smem + (it & 1) * Pf::BYTES;
+    const char* qt = buf;
+    const char* dt = buf + QR * T::ROWP;
+    const float* ls = reinterpret_cast<const float*>(buf + 2 * QR * T::ROWP);
+    const float* dd = ls + QR;
+    const int q0 = ct_row * QR;
+    if (++ct_row == t_end) ct_row = t_begin;
+    if (it + 1 < n_it) prefetch();
+    // every score of the step visible: all rows in range, all keys in
+    // range, and the first row sees the workgroup's last key
+    const bool full = q0 + QR <= Nq && keys_in &&
+                      (!CAUSAL || kfirst + 127 <= q0 + off);
+
+    bf16x8 pop[4], sop[4];  // P and dS operands, k-steps of 16 rows
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // S = Q K^T and dP = dO V^T for rows 32 half .. +31: C row
+      // 8(i/4) + 4h + i%4 reads tile row row_slot of it, i.e. register i
+      // holds row 32 half + 16(i/8) + 8h + i%8, column = key
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int t = 0; t < NSTEP; ++t) {
-        s = mfma32x32x16(row_operand<D>(qt, arow, h, t), kf[t], s);
-        dp = mfma32x32x16(row_operand<D>(dt, arow, h, t), vf[t], dp);
+        s = mfma32x32x16(row_operand<D>(qt, 32 * half + arow, h, t), kf[t], s);
+        dp = mfma32x32x16(row_operand<D>(dt, 32 * half + arow, h, t), vf[t],
+                          dp);
       }
-      // P and dS; the 8 rows of register block i/8 are 16(i/8) + 8h + 0..7
       float lsv[16], ddv[16];
+      row_stats(ls + 32 * half, h, lsv);
+      row_stats(dd + 32 * half, h, ddv);
+      f32x16 p, ds;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; i += 4) {
-        const int r = 16 * (i >> 3) + 8 * h + (i & 7);
-        const f32x4 a = *reinterpret_cast<const f32x4*>(ls + r);
-        const f32x4 c = *reinterpret_cast<const f32x4*>(dd + r);
+        for (int i = 0; i < 16; ++i) {
+          p[i] = exp2_fast(fmaf(s[i], c2, -lsv[i]));
+          ds[i] = p[i] * (dp[i] - ddv[i]);
+        }
+      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lsv[i + e] = a[e];
-          ddv[i + e] = c[e];
+        for (int i = 0; i < 16; ++i) {
+          const int row = q0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
+          bool vis = row < Nq && key < Nk;
+          if (CAUSAL) vis = vis && key <= row + off;
+          // rows that see no key have lse = -inf; their P is 0
+          const float e = exp2_fast(fmaf(s[i], c2, -lsv[i]));
+          p[i] = vis && lsv[i] != -INFINITY ? e : 0.f;
+          ds[i] = p[i] * (dp[i] - ddv[i]);
         }
       }
-      f32x16 p, ds;
+      pop[2 * half] = pack_operand(p, 0);
+      pop[2 * half + 1] = pack_operand(p, 1);
+      sop[2 * half] = pack_operand(ds, 0);
+      sop[2 * half + 1] = pack_operand(ds, 1);
+    }
+    // dV^T += dO^T P, dK^T += Q^T dS (rows = head dims of tile ct)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int row = q0 + 16 * (i >> 3) + 8 * h + (i & 7);
-        bool vis = row < Nq && key < Nk;
-        if (CAUSAL) vis = vis && key <= row + off;
-        // rows that see no key have lse = -inf; their P is 0
-        const float e = exp2_fast(fmaf(s[i], c2, -lsv[i]));
-        p[i] = vis && lsv[i] != -INFINITY ? e : 0.f;
-        ds[i] = p[i] * (dp[i] - ddv[i]);
-      }
-      const bf16x8 p0 = pack_operand(p, 0), p1 = pack_operand(p, 1);
-      const bf16x8 s0 = pack_operand(ds, 0), s1 = pack_operand(ds, 1);
-      // dV^T += dO^T P, dK^T += Q^T dS (rows = head dims of tile ct)
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int ct = 0; ct < NTILE; ++ct) {
-        dvt[ct] = mfma32x32x16(col_operand<D>(dt, ct, 0), p0, dvt[ct]);
-        dvt[ct] = mfma32x32x16(col_operand<D>(dt, ct, 1), p1, dvt[ct]);
-        dkt[ct] = mfma32x32x16(col_operand<D>(qt, ct, 0), s0, dkt[ct]);
-        dkt[ct] = mfma32x32x16(col_operand<D>(qt, ct, 1), s1, dkt[ct]);
+        dvt[ct] = mfma32x32x16(col_operand<D>(dt, ct, ks), pop[ks], dvt[ct]);
+        dkt[ct] = mfma32x32x16(col_operand<D>(qt, ct, ks), sop[ks], dkt[ct]);
       }
     }
+    if (it + 1 < n_it) pf.store(smem + ((it + 1) & 1) * Pf::BYTES);
+    __syncthreads();
   }
 
   // epilogue: lane holds dK^T / dV^T rows 8(i/4) + 4h + i%4 of tile ct
@@ -297,7 +390,7 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
 
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(
+__global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ dvec, const float* __restrict__ lse2,
@@ -305,9 +398,9 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(
     float scale, int n_qblk) {
   using T = Tiles<D>;
   constexpr int NSTEP = T::NSTEP, NTILE = T::NTILE;
-  __shared__ __attribute__((aligned(16))) char smem[2 * 64 * T::ROWP];
-  char* kt = smem;                 // K tile, 64 rows
-  char* vt = smem + 64 * T::ROWP;  // V tile
+  constexpr int KR = 64;  // keys per step
+  using Pf = TilePrefetch<D, KR, false>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * Pf::BYTES];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -326,7 +419,8 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(
   const int hq = hkv * G + gq;
   const int off = Nk - Nq;
   const int64_t qhead = (int64_t)(b * Hq + hq) * Nq;
-  const int qrow = qblk * 128 + wave * 32 + col;  // this lane's query row
+  const int qfirst = qblk * 128;
+  const int qrow = qfirst + wave * 32 + col;  // this lane's query row
   const bool row_ok = qrow < Nq;
 
   // Q^T and dO^T as B operands: lane (col, h) holds row [16t + 8h .. +7]
@@ -350,18 +444,33 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(
 
   const int64_t kvbase = (int64_t)bh * Nk * D;
   int kv_end = Nk;
-  if (CAUSAL) kv_end = min(Nk, qblk * 128 + 128 + off);
-  const int nblk = kv_end > 0 ? (kv_end + 63) / 64 : 0;
+  if (CAUSAL) kv_end = min(Nk, qfirst + 128 + off);
+  const int nblk = kv_end > 0 ? (kv_end + KR - 1) / KR : 0;
   const int arow = row_slot(col);
   // this lane's last visible key
   const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+  // rows all in range (then every row sees key 0 or more)
+  const bool rows_in = qfirst + 128 <= Nq;
+  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + kvbase, (uint32_t)Nk * (2 * D));
+  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + kvbase, (uint32_t)Nk * (2 * D));
+
+  Pf pf;
+  if (nblk > 0) {
+    pf.load(rk, rv, 0);
+    pf.store(smem);
+  }
+  __syncthreads();
 
   for (int j = 0; j < nblk; ++j) {
-    const int k0 = j * 64;
-    __syncthreads();
-    stage_rows<D, 64>(kt, k + kvbase, k0, Nk);
-    stage_rows<D, 64>(vt, v + kvbase, k0, Nk);
-    __syncthreads();
+    const char* buf = smem + (j & 1) * Pf::BYTES;
+    const char* kt = buf;
+    const char* vt = buf + KR * T::ROWP;
+    const int k0 = j * KR;
+    if (j + 1 < nblk) pf.load(rk, rv, k0 + KR);
+    // every score of the step visible: keys in range, rows in range, and
+    // the workgroup's first row sees the step's last key
+    const bool full = k0 + KR <= Nk && rows_in &&
+                      (!CAUSAL || k0 + KR - 1 <= qfirst + off);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       // S^T = K Q^T, dP^T = V dO^T for keys 32 half + row_slot(row):
@@ -375,12 +484,18 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(
                           dp);
       }
       f32x16 ds;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
-        const bool vis = row_ok && key <= lim && l2 != -INFINITY;
-        const float p = vis ? exp2_fast(fmaf(s[i], c2, -l2)) : 0.f;
-        ds[i] = p * (dp[i] - dval);
+        for (int i = 0; i < 16; ++i)
+          ds[i] = exp2_fast(fmaf(s[i], c2, -l2)) * (dp[i] - dval);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
+          const bool vis = row_ok && key <= lim && l2 != -INFINITY;
+          const float p = vis ? exp2_fast(fmaf(s[i], c2, -l2)) : 0.f;
+          ds[i] = p * (dp[i] - dval);
+        }
       }
       // dQ += dS K: A = dS (row = query, k = keys 8h + 0..7 of k-step ks),
       // B = K read transposed (k = key, column = head dim)
@@ -392,13 +507,15 @@ __global__ __launch_bounds__(NT, 1) void bwd_dq_kernel(
             mfma32x32x16(a1, col_operand<D>(kt, ct, 2 * half + 1), acc[ct]);
       }
     }
+    if (j + 1 < nblk) pf.store(smem + ((j + 1) & 1) * Pf::BYTES);
+    __syncthreads();
   }
 
   // epilogue: lane holds dQ rows 8(i/4) + 4h + i%4 of the wave's 32 rows,
   // column 32 ct + col
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
-    const int r = qblk * 128 + wave * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
+    const int r = qfirst + wave * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
     if (r < Nq) {
 #pragma unroll
       for (int ct = 0; ct < NTILE; ++ct) {

@@ -87,4 +87,13 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
+// Buffer resource over [base, base + bytes): loads at byte offsets >= bytes
+// return zeros (the hardware range check), which is how the kernels read
+// past the end of a sequence without branches.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base,
+                                                              uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)bytes, 0x00020000);
+}
+
 }  // namespace fa

@@ -20,6 +20,14 @@ def attention_fwd_flops(B, Hq, Nq, Nk, d, causal) -> float:
     return f / 2.0 if causal else f
 
 
+def attention_bwd_flops(B, Hq, Nq, Nk, d, causal) -> float:
+    """Backward FLOPs: the five N x N x d products of the recomputation
+    form (scores, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q), i.e.
+    2.5 times the forward, the factor the training-cost guide gives; /2 if
+    causal.  Products an implementation repeats are not counted."""
+    return 2.5 * attention_fwd_flops(B, Hq, Nq, Nk, d, causal)
+
+
 def attention_fwd_bytes(B, Hq, Hkv, Nq, Nk, d, out_bytes=2, in_bytes=2) -> float:
     """Algorithmic HBM bytes: Q, K, V read once, O and the fp32 lse written
     once.  Re-reads of K/V by several Q blocks and split-KV partials are an

@@ -148,7 +148,8 @@ int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
  * `stream`; each output element is written by exactly one workgroup (no
  * atomics), so results are deterministic.  Argument checks and status
  * codes as for fa_fwd (d 64 or 128); FA_ERR_INVALID_ARG also for a missing
- * or small workspace.
+ * or small workspace; FA_ERR_UNSUPPORTED also when one head of Q or K
+ * spans 2^31 bytes or more ((N + 128) * d * 2 >= 2^31 for N = Nq or Nk).
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq);
 

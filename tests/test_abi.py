@@ -154,6 +154,16 @@ def test_bwd_unsupported_head_dim(lib, d):
     assert _bwd(lib, d=d) == _lib.FA_ERR_UNSUPPORTED
 
 
+def test_bwd_head_range(lib):
+    # one head of Q (or K) plus one 128-row step must span < 2^31 bytes
+    big = (1 << 23) - 128
+    assert _bwd(lib, Hq=1, Hkv=1, Nq=big + 1, Nk=16, d=128,
+                wsb=1 << 40) == _lib.FA_ERR_UNSUPPORTED
+    assert _bwd(lib, Hq=1, Hkv=1, Nq=16, Nk=big + 1, d=128) == \
+        _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+
+
 def test_bwd_workspace_size(lib):
     # D and lse * log2(e): two fp32 per query row
     assert lib.fa_bwd_workspace_bytes(1, 32, 8192) == 32 * 8192 * 8

@@ -11,24 +11,34 @@
 // Three kernels, no atomics (every output element has one owner):
 // * bwd_pre_kernel: D and lse in log2 units per query row, into the
 //   workspace.
-// * bwd_dkdv_kernel: one workgroup per (batch, KV head, 128 keys), 4 waves
-//   of 32 keys.  K and V of the wave's keys stay in registers as matrix-core
-//   operands; the Q / dO tiles of 32 query rows of every query head of the
-//   group stream through LDS.  Per tile: S = Q K^T and dP = dO V^T
-//   (v_mfma_f32_32x32x16_bf16, lane = one key, 16 query rows), P and dS in
-//   registers, then dV^T += dO^T P and dK^T += Q^T dS with P and dS as the
-//   B operands as they are (the query rows are read in an order, bits 2 and
-//   3 of the row index swapped, that makes a lane's score registers 8
-//   consecutive query rows) and dO^T, Q^T read with the transposing LDS
-//   read ds_read_b64_tr_b16.
-// * bwd_dq_kernel: one workgroup per (batch, query head, 128 query rows),
-//   4 waves of 32 rows, Q and dO in registers; K / V tiles of 64 keys
-//   stream through LDS.  Per tile: S^T = K Q^T and dP^T = V dO^T (lane = one
-//   query row, 16 keys, key order swapped the same way), dS^T in registers,
-//   then dQ += dS K with dS as the A operand as it is and K read
-//   transposed.
-// Tiles are staged through LDS in row-major order with rows padded by 16
-// bytes.  Tails read as zeros and are masked.
+// * bwd_dkdv_kernel: one workgroup of 8 waves per (batch, KV head, 128
+//   keys), in two roles over four groups of 32 keys: waves 0-3 hold K as
+//   matrix-core operands, form S = Q K^T and P = exp2(S c - lse2), and
+//   accumulate dV^T += dO^T P; waves 4-7 hold V, form dP = dO V^T, take P
+//   from the first group through LDS, form dS = P (dP - D) and accumulate
+//   dK^T += Q^T dS.  The two waves of a key group share a SIMD, so one
+//   wave's vector work runs under the other's matrix products.  Tiles of 64
+//   query rows of every query head of the group stream through LDS
+//   (double-buffered).  Scores use v_mfma_f32_32x32x16_bf16 with lane = one
+//   key and 16 query rows; the query rows are read in an order (bits 2 and
+//   3 of the row index swapped) that makes a lane's score registers 8
+//   consecutive rows, so P and dS serve as B operands as they are, and dO^T
+//   and Q^T come from the row-major tiles through the transposing LDS read
+//   ds_read_b64_tr_b16.
+// * bwd_dq_kernel: one workgroup of 4 waves per (batch, query head, 128
+//   query rows), 32 rows per wave with Q and dO in registers; K / V tiles
+//   of 64 keys stream through LDS (double-buffered).  Per half tile:
+//   S^T = K Q^T and dP^T = V dO^T (lane = one query row, 16 keys, key order
+//   swapped the same way), dS^T in registers, then dQ += dS K with dS as
+//   the A operand as it is and K read transposed.
+// Tiles move HBM -> LDS with buffer_load ... lds, issued at the start of the
+// step before the one that reads them; a buffer resource per copy ends at
+// the head's last row, so tails arrive as zeros and are masked.  LDS tiles
+// are row-major with a 16-byte-chunk XOR swizzle (no bank conflicts in
+// either read direction), and operand reads run four products ahead of
+// their matrix products.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_internal.h"
 
@@ -48,26 +58,22 @@ __device__ __forceinline__ int row_slot(int r) {
 
 template <int D>
 struct Tiles {
-  static constexpr int ROWP = 2 * D + 16;  // padded LDS row (bytes)
-  static constexpr int NSTEP = D / 16;     // k-steps over the head dim
-  static constexpr int NTILE = D / 32;     // 32-column tiles of the head dim
+  static constexpr int ROWP = 2 * D;   // LDS row (bytes)
+  static constexpr int NSTEP = D / 16;  // k-steps over the head dim
+  static constexpr int NTILE = D / 32;  // 32-column tiles of the head dim
 };
 
-// Copies rows [r0, r0 + R) of a [N, D] bf16 matrix into LDS (padded rows);
-// rows at or past N are zeros.  All NT threads take part.
-template <int D, int R>
-__device__ __forceinline__ void stage_rows(char* dst, const uint16_t* src,
-                                           int r0, int N) {
-  using T = Tiles<D>;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-  for (int i = threadIdx.x; i < R * CPR; i += NT) {
-    const int r = i / CPR, c = i % CPR;
-    const int row = r0 + r;
-    const u32x4 x = row < N ? ldg16(src + (int64_t)row * D + 8 * c)
-                            : u32x4{0u, 0u, 0u, 0u};
-    *reinterpret_cast<u32x4*>(dst + r * T::ROWP + 16 * c) = x;
-  }
+// LDS tile swizzle: 16-byte chunk c of tile row r is stored at chunk
+// c ^ swz(r).  Tiles are read both along rows (16-byte reads, 16 lanes on
+// 16 different rows) and down columns (transposing 8-byte reads, 32 lanes
+// on 4 rows x 64 bytes); with 64 banks of 4 bytes, swz spreads the 16 rows
+// of the first over all 16 chunk positions of a 256-byte bank line and the
+// 4 rows of the second over the four 64-byte quarters of it, so neither
+// read nor the row-wise tile store has a bank conflict.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3))
+                  : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // A / B operand (8 bf16) of lane (row or column `lr` = lane % 32, half h)
@@ -76,8 +82,8 @@ template <int D>
 __device__ __forceinline__ bf16x8 row_operand(const char* tile, int row,
                                               int h, int t) {
   using T = Tiles<D>;
-  return *reinterpret_cast<const bf16x8*>(tile + row * T::ROWP + 32 * t +
-                                          16 * h);
+  return *reinterpret_cast<const bf16x8*>(
+      tile + row * T::ROWP + 16 * ((2 * t + h) ^ swz<D>(row)));
 }
 
 // Transposing operand read: lane (lr, h) gets the 8 values of column
@@ -90,12 +96,17 @@ __device__ __forceinline__ bf16x8 col_operand(const char* tile, int ct,
   const int lane = threadIdx.x & 63;
   const int lg = lane >> 4, lp = lane & 15;
   const int row = 16 * ks + 8 * (lg >> 1) + (lp >> 2);
-  const int col = 32 * ct + 16 * (lg & 1) + 4 * (lp & 3);
-  const char* a0 = tile + row * T::ROWP + 2 * col;
+  // 16-byte chunk of columns 32 ct + 16 (lg % 2) + 4 (lp % 4) .. +3, and
+  // the 8-byte half of it
+  const int chunk = 4 * ct + 2 * (lg & 1) + ((lp & 3) >> 1);
+  const int part = 8 * (lp & 1);
+  const char* a0 = tile + row * T::ROWP + 16 * (chunk ^ swz<D>(row)) + part;
+  const char* a1 =
+      tile + (row + 4) * T::ROWP + 16 * (chunk ^ swz<D>(row + 4)) + part;
   const i16x4 lo =
       __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_char*)a0));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_i16x4*)((lds_char*)(a0 + 4 * T::ROWP)));
+  const i16x4 hi =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)((lds_char*)a1));
   u32x4 va;
   va[0] = __builtin_bit_cast(u32x2, lo)[0];
   va[1] = __builtin_bit_cast(u32x2, lo)[1];
@@ -108,6 +119,23 @@ __device__ __forceinline__ bf16x8 col_operand(const char* tile, int ct,
 // 8 ks + 7.
 __device__ __forceinline__ bf16x8 pack_operand(const f32x16& c, int ks) {
   return to_bf16x8(c, 8 * ks);
+}
+
+// Runs N matrix products in program order; product i gets one operand from
+// LDS through read(i), issued DEPTH products before its use so that LDS
+// latency hides under the products in between.
+template <int N, int DEPTH, class Read, class Mfma>
+__device__ __forceinline__ void lds_pipeline(Read read, Mfma mfma) {
+  bf16x8 ring[DEPTH];
+#pragma unroll
+  for (int i = 0; i < DEPTH && i < N; ++i) ring[i] = read(i);
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bf16x8 a = ring[i % DEPTH];
+    if (i + DEPTH < N) ring[i % DEPTH] = read(i + DEPTH);
+    mfma(i, a);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -147,56 +175,51 @@ __global__ __launch_bounds__(NT) void bwd_pre_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Register prefetch of the next pair of row tiles (R rows each, R = one
-// wave's lanes: Q and dO, or K and V) and, with STATS, the lse2 and D
-// values of the rows; stored to an LDS buffer laid out as [first tile |
-// second tile | lse2[R] | D[R]] after the current step's products.  The
-// loads go through buffer resources spanning one head, so rows past its
-// end read as zeros.
-template <int D, int R, bool STATS>
-struct TilePrefetch {
-  using T = Tiles<D>;
-  static constexpr int CPR = D / 8;               // 16-byte chunks per row
-  static constexpr int N = 2 * R * CPR / NT;      // chunks per thread
-  static constexpr int BYTES = 2 * R * T::ROWP + (STATS ? 2 * R * 4 : 0);
-  static_assert(N * NT == 2 * R * CPR && N % 2 == 0 && R == 64, "tile split");
-  u32x4 x[N];
-  float st;
+typedef __attribute__((address_space(3))) void lds_void;
 
-  // ra, rb: the two tiles' heads (rows of D bf16)
-  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t ra,
-                                       __amdgpu_buffer_rsrc_t rb, int r0) {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int i = threadIdx.x + NT * (j % (N / 2));
-      const int r = i / CPR, c = i % CPR;
-      x[j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                     j < N / 2 ? ra : rb, (r0 + r) * (2 * D) + 16 * c, 0, 0));
-    }
+// s_waitcnt vmcnt(0) alone (expcnt, lgkmcnt left free); gfx9 encoding.
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// HBM -> LDS copies of 64-row tiles with buffer_load ... lds (no staging
+// registers).  Instruction n of a tile fills LDS bytes [1 KiB n, 1 KiB
+// (n + 1)) = tile rows RPK n .. RPK n + RPK - 1; lane j writes the 16 bytes
+// at 16 j, so it reads the logical chunk that the swizzle puts there.  The
+// buffer resource of each instruction starts at its first row and ends at
+// the head's last row, so rows past the end arrive as zeros.
+template <int D>
+struct TileDma {
+  static constexpr int RPK = 1024 / (2 * D);  // rows per instruction
+  static constexpr int NI = 64 / RPK;         // instructions per tile
+  static constexpr int CPR = 2 * D / 16;      // 16-byte chunks per row
+  // source offset of this lane within instruction n (depends on n only
+  // through n % (16 / RPK))
+  static __device__ __forceinline__ uint32_t lane_off(int n) {
+    const int lane = threadIdx.x & 63;
+    const int r = lane / CPR, p = lane % CPR;
+    return (uint32_t)(r * (2 * D) + 16 * (p ^ swz<D>(RPK * n + r)));
   }
-  // rl, rv: lse2 and D of the head; waves 0 and 1 fetch one each (a
-  // wave-uniform choice)
-  __device__ __forceinline__ void load_stats(__amdgpu_buffer_rsrc_t rl,
-                                             __amdgpu_buffer_rsrc_t rv,
-                                             int r0) {
-    if (threadIdx.x < R)
-      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         rl, (r0 + threadIdx.x) * 4, 0, 0));
-    else if (threadIdx.x < 2 * R)
-      st = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                         rv, (r0 + threadIdx.x - R) * 4, 0, 0));
+  // instruction n of the tile of rows r0 .. r0 + 63 of `head` (`rows` rows
+  // of 2D bytes) into the LDS tile `dst`
+  static __device__ __forceinline__ void issue(char* dst, const char* head,
+                                               int rows, int r0, int n,
+                                               uint32_t loff) {
+    const int64_t start = (int64_t)(r0 + RPK * n) * (2 * D);
+    const int64_t total = (int64_t)rows * (2 * D);
+    const uint32_t rem = start < total ? (uint32_t)(total - start) : 0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        buffer_rsrc(head + start, rem), (lds_void*)(dst + 1024 * n), 16, loff,
+        0, 0, 0);
   }
-  __device__ __forceinline__ void store(char* buf) const {
-#pragma unroll
-    for (int j = 0; j < N; ++j) {
-      const int i = threadIdx.x + NT * (j % (N / 2));
-      const int r = i / CPR, c = i % CPR;
-      *reinterpret_cast<u32x4*>(buf + (j < N / 2 ? 0 : R * T::ROWP) +
-                                r * T::ROWP + 16 * c) = x[j];
-    }
-    if (STATS && threadIdx.x < 2 * R)
-      reinterpret_cast<float*>(buf + 2 * R * T::ROWP)[threadIdx.x] = st;
+  // 64 fp32 values v[r0 .. r0 + 63] (zeros past `rows`) into `dst`; one
+  // wave's instruction
+  static __device__ __forceinline__ void issue_vec(float* dst, const float* v,
+                                                   int rows, int r0) {
+    const uint32_t rem = r0 < rows ? (uint32_t)(rows - r0) * 4u : 0u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        buffer_rsrc(v + r0, rem), (lds_void*)dst, 4,
+        (uint32_t)(threadIdx.x & 63) * 4u, 0, 0, 0);
   }
 };
 
@@ -212,8 +235,15 @@ __device__ __forceinline__ void row_stats(const float* v, int h, float* out) {
   }
 }
 
+// dK/dV kernel: 8 waves in two roles over the same 4 groups of 32 keys.
+// Waves 0-3 hold K and accumulate dV (they form P); waves 4-7 hold V and
+// accumulate dK (they form dP and dS).  A P wave and the dS wave of the same
+// keys share a SIMD, so one wave's vector work runs under the other's
+// matrix products.
+constexpr int NT2 = 512;
+
 template <int D, bool CAUSAL, bool OUT_F32>
-__global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ dvec, const float* __restrict__ lse2,
@@ -222,12 +252,21 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
   using T = Tiles<D>;
   constexpr int NSTEP = T::NSTEP, NTILE = T::NTILE;
   constexpr int QR = 64;  // query rows per step
-  using Pf = TilePrefetch<D, QR, true>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Pf::BYTES];
+  using Dma = TileDma<D>;
+  // one stage: [Q tile | dO tile | lse2[64] | D[64]]
+  constexpr int STAGE = 2 * QR * T::ROWP + 2 * QR * 4;
+  // P handed from the P waves to the dS waves, fp32: per key group 2 halves
+  // x 4 chunks x 64 lanes x 4 values, chunk-major (conflict-free)
+  constexpr int XFLOATS = 2 * 4 * 64 * 4;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE +
+                                                      4 * XFLOATS * 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int h = lane >> 5, col = lane & 31;
+  const bool pw = wave < 4;  // P wave (K, dV) or dS wave (V, dK)
+  const int kw = wave & 3;   // key group
+  float* xw = reinterpret_cast<float*>(smem + 2 * STAGE) + kw * XFLOATS;
 
   // work item: (b, kv head, key block of 128); causal: early keys (more
   // query rows to visit) first
@@ -238,27 +277,21 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
   const int G = Hq / Hkv;
   const int off = Nk - Nq;
   const int kfirst = kblk * 128;
-  const int key = kfirst + wave * 32 + col;  // this lane's key
+  const int key = kfirst + kw * 32 + col;  // this lane's key
 
-  // K and V of the wave's keys as B operands: lane (col, h) holds
-  // [key][16t + 8h .. +7]
-  const uint16_t* kh = k + (int64_t)bh * Nk * D;
-  const uint16_t* vh = v + (int64_t)bh * Nk * D;
-  bf16x8 kf[NSTEP], vf[NSTEP];
+  // K (P waves) or V (dS waves) of the group's keys as B operands: lane
+  // (col, h) holds [key][16t + 8h .. +7]
+  bf16x8 kv[NSTEP];
+  {
+    const uint16_t* src = (pw ? k : v) + ((int64_t)bh * Nk + key) * D + 8 * h;
 #pragma unroll
-  for (int t = 0; t < NSTEP; ++t) {
-    const bool ok = key < Nk;
-    kf[t] = __builtin_bit_cast(bf16x8, ok ? ldg16(kh + (int64_t)key * D + 16 * t + 8 * h)
-                                          : u32x4{0u, 0u, 0u, 0u});
-    vf[t] = __builtin_bit_cast(bf16x8, ok ? ldg16(vh + (int64_t)key * D + 16 * t + 8 * h)
-                                          : u32x4{0u, 0u, 0u, 0u});
+    for (int t = 0; t < NSTEP; ++t)
+      kv[t] = __builtin_bit_cast(bf16x8, key < Nk ? ldg16(src + 16 * t)
+                                                  : u32x4{0u, 0u, 0u, 0u});
   }
-  f32x16 dkt[NTILE], dvt[NTILE];
+  f32x16 acc[NTILE];  // dV^T (P waves) or dK^T / scale (dS waves)
 #pragma unroll
-  for (int i = 0; i < NTILE; ++i) {
-    dkt[i] = f32x16{};
-    dvt[i] = f32x16{};
-  }
+  for (int i = 0; i < NTILE; ++i) acc[i] = f32x16{};
 
   // query rows that can see a key of this workgroup (causal: rows i with
   // i + off >= its first key), in steps of QR rows, for each of the G query
@@ -268,120 +301,158 @@ __global__ __launch_bounds__(NT, 1) void bwd_dkdv_kernel(
   const int n_it = G * (t_end - t_begin);
   const bool keys_in = kfirst + 128 <= Nk;
   const int arow = row_slot(col);  // tile row read for operand row col
-  const uint32_t head_bytes = (uint32_t)Nq * (2 * D);
 
-  // (g, t): query head within the group and row step of the next prefetch
-  int pg = 0, pt = t_begin;
-  Pf pf;
-  auto prefetch = [&]() {
+  // copies of one step: 2 * NI tile instructions spread over the 8 waves
+  // (instruction i = wave + 8 m: tile i / NI, part i % NI, the same part
+  // modulo the swizzle period for every m), lse2 by wave 0, D by wave 1
+  static_assert((2 * Dma::NI) % 8 == 0, "copy split");
+  const uint32_t loff = Dma::lane_off(wave);
+  int pg = 0, pt = t_begin;  // query head and row step of the next copy
+  auto copy_step = [&](char* dst) {
     const int64_t qh = (int64_t)(b * Hq + hkv * G + pg) * Nq;
-    pf.load(buffer_rsrc(q + qh * D, head_bytes),
-            buffer_rsrc(dout + qh * D, head_bytes), pt * QR);
-    pf.load_stats(buffer_rsrc(lse2 + qh, (uint32_t)Nq * 4),
-                  buffer_rsrc(dvec + qh, (uint32_t)Nq * 4), pt * QR);
+    const int r0 = pt * QR;
+#pragma unroll
+    for (int m = 0; m < 2 * Dma::NI / 8; ++m) {
+      const int i = wave + 8 * m;
+      const bool second = i >= Dma::NI;
+      Dma::issue(dst + (second ? QR * T::ROWP : 0),
+                 reinterpret_cast<const char*>((second ? dout : q) + qh * D),
+                 Nq, r0, i % Dma::NI, loff);
+    }
+    float* st = reinterpret_cast<float*>(dst + 2 * QR * T::ROWP);
+    if (wave == 0) Dma::issue_vec(st, lse2 + qh, Nq, r0);
+    if (wave == 1) Dma::issue_vec(st + QR, dvec + qh, Nq, r0);
     if (++pt == t_end) {
       pt = t_begin;
       ++pg;
     }
   };
-  if (n_it > 0) {
-    prefetch();
-    pf.store(smem);
-  }
+  if (n_it > 0) copy_step(smem);
+  wait_vmcnt0();
   __syncthreads();
 
   int ct_row = t_begin;  // row step being computed
-  for (int it = 0; it < n_it; ++it) {
-    const char* buf = smem + (it & 1) * Pf::BYTES;
-    const char* qt = buf;
-    const char* dt = buf + QR * T::ROWP;
-    const float* ls = reinterpret_cast<const float*>(buf + 2 * QR * T::ROWP);
+  // one step on stage PAR (a compile-time constant, so that every LDS
+  // address of the step is a per-lane base plus an immediate)
+  auto step = [&](int it, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const char* qt = smem + PAR * STAGE;
+    const char* dt = qt + QR * T::ROWP;
+    const float* ls = reinterpret_cast<const float*>(qt + 2 * QR * T::ROWP);
     const float* dd = ls + QR;
     const int q0 = ct_row * QR;
     if (++ct_row == t_end) ct_row = t_begin;
-    if (it + 1 < n_it) prefetch();
-    // every score of the step visible: all rows in range, all keys in
-    // range, and the first row sees the workgroup's last key
-    const bool full = q0 + QR <= Nq && keys_in &&
-                      (!CAUSAL || kfirst + 127 <= q0 + off);
+    if (it + 1 < n_it) copy_step(smem + (1 - PAR) * STAGE);
 
-    bf16x8 pop[4], sop[4];  // P and dS operands, k-steps of 16 rows
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // S = Q K^T and dP = dO V^T for rows 32 half .. +31: C row
-      // 8(i/4) + 4h + i%4 reads tile row row_slot of it, i.e. register i
-      // holds row 32 half + 16(i/8) + 8h + i%8, column = key
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < NSTEP; ++t) {
-        s = mfma32x32x16(row_operand<D>(qt, 32 * half + arow, h, t), kf[t], s);
-        dp = mfma32x32x16(row_operand<D>(dt, 32 * half + arow, h, t), vf[t],
-                          dp);
-      }
-      float lsv[16], ddv[16];
-      row_stats(ls + 32 * half, h, lsv);
-      row_stats(dd + 32 * half, h, ddv);
-      f32x16 p, ds;
-      if (full) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          p[i] = exp2_fast(fmaf(s[i], c2, -lsv[i]));
-          ds[i] = p[i] * (dp[i] - ddv[i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = q0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
-          bool vis = row < Nq && key < Nk;
-          if (CAUSAL) vis = vis && key <= row + off;
-          // rows that see no key have lse = -inf; their P is 0
-          const float e = exp2_fast(fmaf(s[i], c2, -lsv[i]));
-          p[i] = vis && lsv[i] != -INFINITY ? e : 0.f;
-          ds[i] = p[i] * (dp[i] - ddv[i]);
-        }
-      }
-      pop[2 * half] = pack_operand(p, 0);
-      pop[2 * half + 1] = pack_operand(p, 1);
-      sop[2 * half] = pack_operand(ds, 0);
-      sop[2 * half + 1] = pack_operand(ds, 1);
+    // Products on rows 32 half .. +31 of the step: C row 8(i/4) + 4h + i%4
+    // reads tile row row_slot of it, so register i holds row
+    // 32 half + 16(i/8) + 8h + i%8 and the column is the lane's key.
+    bf16x8 op[4];  // P or dS operands, k-steps of 16 rows
+    // S = Q K^T (P waves) or dP = dO V^T (dS waves) for both halves,
+    // products alternating between the two accumulators
+    f32x16 sp[2] = {f32x16{}, f32x16{}};
+    {
+      const char* at = pw ? qt : dt;
+      lds_pipeline<2 * NSTEP, 4>(
+          [&](int i) {
+            return row_operand<D>(at, 32 * (i & 1) + arow, h, i >> 1);
+          },
+          [&](int i, bf16x8 a) {
+            sp[i & 1] = mfma32x32x16(a, kv[i >> 1], sp[i & 1]);
+          });
     }
-    // dV^T += dO^T P, dK^T += Q^T dS (rows = head dims of tile ct)
+    if (pw) {
+      // every score of the step visible: all rows in range, all keys in
+      // range, and the first row sees the workgroup's last key
+      const bool full = q0 + QR <= Nq && keys_in &&
+                        (!CAUSAL || kfirst + 127 <= q0 + off);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
+      for (int half = 0; half < 2; ++half) {
+        float lsv[16];
+        row_stats(ls + 32 * half, h, lsv);
+        f32x16 p;
+        if (full) {
 #pragma unroll
-      for (int ct = 0; ct < NTILE; ++ct) {
-        dvt[ct] = mfma32x32x16(col_operand<D>(dt, ct, ks), pop[ks], dvt[ct]);
-        dkt[ct] = mfma32x32x16(col_operand<D>(qt, ct, ks), sop[ks], dkt[ct]);
+          for (int i = 0; i < 16; ++i)
+            p[i] = exp2_fast(fmaf(sp[half][i], c2, -lsv[i]));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int row = q0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
+            bool vis = row < Nq && key < Nk;
+            if (CAUSAL) vis = vis && key <= row + off;
+            // rows that see no key have lse = -inf; their P is 0
+            const float e = exp2_fast(fmaf(sp[half][i], c2, -lsv[i]));
+            p[i] = vis && lsv[i] != -INFINITY ? e : 0.f;
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          *reinterpret_cast<f32x4*>(xw + (4 * half + e) * 256 + 4 * lane) =
+              f32x4{p[4 * e], p[4 * e + 1], p[4 * e + 2], p[4 * e + 3]};
+        op[2 * half] = pack_operand(p, 0);
+        op[2 * half + 1] = pack_operand(p, 1);
       }
     }
-    if (it + 1 < n_it) pf.store(smem + ((it + 1) & 1) * Pf::BYTES);
+    __syncthreads();  // P of the step visible to the dS waves
+    if (!pw) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        float ddv[16];
+        row_stats(dd + 32 * half, h, ddv);
+        f32x16 ds;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const f32x4 p = *reinterpret_cast<const f32x4*>(
+              xw + (4 * half + e) * 256 + 4 * lane);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            ds[4 * e + u] = p[u] * (sp[half][4 * e + u] - ddv[4 * e + u]);
+        }
+        op[2 * half] = pack_operand(ds, 0);
+        op[2 * half + 1] = pack_operand(ds, 1);
+      }
+    }
+    // dV^T += dO^T P (P waves), dK^T += Q^T dS (dS waves); rows = head
+    // dims of tile ct; product i: k-step i / NTILE, tile i % NTILE
+    {
+      const char* at = pw ? dt : qt;
+      lds_pipeline<4 * NTILE, 4>(
+          [&](int i) { return col_operand<D>(at, i % NTILE, i / NTILE); },
+          [&](int i, bf16x8 a) {
+            acc[i % NTILE] = mfma32x32x16(a, op[i / NTILE], acc[i % NTILE]);
+          });
+    }
+    wait_vmcnt0();  // this wave's copies for the next step have landed
     __syncthreads();
+  };
+  int it = 0;
+  for (; it + 2 <= n_it; it += 2) {
+    step(it, std::integral_constant<int, 0>{});
+    step(it + 1, std::integral_constant<int, 1>{});
   }
+  if (it < n_it) step(it, std::integral_constant<int, 0>{});
 
-  // epilogue: lane holds dK^T / dV^T rows 8(i/4) + 4h + i%4 of tile ct
+  // epilogue: lane holds dV^T or dK^T rows 8(i/4) + 4h + i%4 of tile ct
   // (head dims), column = its key
   if (key < Nk) {
     const int64_t base = ((int64_t)bh * Nk + key) * D;
+    const float sc = pw ? 1.f : scale;
+    void* out = pw ? dv : dk;
 #pragma unroll
     for (int ct = 0; ct < NTILE; ++ct) {
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int c = 32 * ct + 8 * gg + 4 * h;
-        const f32x16& a = dkt[ct];
-        const f32x16& w = dvt[ct];
+        const f32x16& a = acc[ct];
         if (OUT_F32) {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(dk) + base + c) =
-              f32x4{a[4 * gg] * scale, a[4 * gg + 1] * scale,
-                    a[4 * gg + 2] * scale, a[4 * gg + 3] * scale};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(dv) + base + c) =
-              f32x4{w[4 * gg], w[4 * gg + 1], w[4 * gg + 2], w[4 * gg + 3]};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out) + base + c) =
+              f32x4{a[4 * gg] * sc, a[4 * gg + 1] * sc, a[4 * gg + 2] * sc,
+                    a[4 * gg + 3] * sc};
         } else {
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dk) + base + c) =
-              u32x2{pack_bf16x2(a[4 * gg] * scale, a[4 * gg + 1] * scale),
-                    pack_bf16x2(a[4 * gg + 2] * scale, a[4 * gg + 3] * scale)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(dv) + base + c) =
-              u32x2{pack_bf16x2(w[4 * gg], w[4 * gg + 1]),
-                    pack_bf16x2(w[4 * gg + 2], w[4 * gg + 3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + base + c) =
+              u32x2{pack_bf16x2(a[4 * gg] * sc, a[4 * gg + 1] * sc),
+                    pack_bf16x2(a[4 * gg + 2] * sc, a[4 * gg + 3] * sc)};
         }
       }
     }
@@ -399,8 +470,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
   using T = Tiles<D>;
   constexpr int NSTEP = T::NSTEP, NTILE = T::NTILE;
   constexpr int KR = 64;  // keys per step
-  using Pf = TilePrefetch<D, KR, false>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * Pf::BYTES];
+  using Dma = TileDma<D>;
+  constexpr int STAGE = 2 * KR * T::ROWP;  // [K tile | V tile]
+  __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -451,22 +523,35 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
   const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
   // rows all in range (then every row sees key 0 or more)
   const bool rows_in = qfirst + 128 <= Nq;
-  const __amdgpu_buffer_rsrc_t rk = buffer_rsrc(k + kvbase, (uint32_t)Nk * (2 * D));
-  const __amdgpu_buffer_rsrc_t rv = buffer_rsrc(v + kvbase, (uint32_t)Nk * (2 * D));
+  const char* kh = reinterpret_cast<const char*>(k + kvbase);
+  const char* vh = reinterpret_cast<const char*>(v + kvbase);
 
-  Pf pf;
-  if (nblk > 0) {
-    pf.load(rk, rv, 0);
-    pf.store(smem);
-  }
+  // copies of one step: 2 * NI tile instructions spread over the 4 waves
+  // (instruction i = wave + 4 m: tile i / NI, part i % NI, the same part
+  // modulo the swizzle period for every m)
+  static_assert((2 * Dma::NI) % 4 == 0, "copy split");
+  const uint32_t loff = Dma::lane_off(wave);
+  auto copy_step = [&](char* dst, int k0) {
+#pragma unroll
+    for (int m = 0; m < 2 * Dma::NI / 4; ++m) {
+      const int i = wave + 4 * m;
+      const bool second = i >= Dma::NI;
+      Dma::issue(dst + (second ? KR * T::ROWP : 0), second ? vh : kh, Nk, k0,
+                 i % Dma::NI, loff);
+    }
+  };
+  if (nblk > 0) copy_step(smem, 0);
+  wait_vmcnt0();
   __syncthreads();
 
-  for (int j = 0; j < nblk; ++j) {
-    const char* buf = smem + (j & 1) * Pf::BYTES;
-    const char* kt = buf;
-    const char* vt = buf + KR * T::ROWP;
+  // one step on stage PAR (compile-time, so LDS addresses are a per-lane
+  // base plus an immediate)
+  auto step = [&](int j, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    const char* kt = smem + PAR * STAGE;
+    const char* vt = kt + KR * T::ROWP;
     const int k0 = j * KR;
-    if (j + 1 < nblk) pf.load(rk, rv, k0 + KR);
+    if (j + 1 < nblk) copy_step(smem + (1 - PAR) * STAGE, k0 + KR);
     // every score of the step visible: keys in range, rows in range, and
     // the workgroup's first row sees the step's last key
     const bool full = k0 + KR <= Nk && rows_in &&
@@ -474,42 +559,53 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       // S^T = K Q^T, dP^T = V dO^T for keys 32 half + row_slot(row):
-      // register i holds key 32 half + 16(i/8) + 8h + i%8, column = query
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int t = 0; t < NSTEP; ++t) {
-        s = mfma32x32x16(row_operand<D>(kt, 32 * half + arow, h, t), qf[t],
-                         s);
-        dp = mfma32x32x16(row_operand<D>(vt, 32 * half + arow, h, t), df[t],
-                          dp);
-      }
+      // register i holds key 32 half + 16(i/8) + 8h + i%8, column = query;
+      // products alternate between the two accumulators
+      f32x16 sp[2] = {f32x16{}, f32x16{}};
+      lds_pipeline<2 * NSTEP, 4>(
+          [&](int i) {
+            return row_operand<D>((i & 1) ? vt : kt, 32 * half + arow, h,
+                                  i >> 1);
+          },
+          [&](int i, bf16x8 a) {
+            sp[i & 1] = mfma32x32x16(a, (i & 1) ? df[i >> 1] : qf[i >> 1],
+                                     sp[i & 1]);
+          });
       f32x16 ds;
       if (full) {
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          ds[i] = exp2_fast(fmaf(s[i], c2, -l2)) * (dp[i] - dval);
+          ds[i] = exp2_fast(fmaf(sp[0][i], c2, -l2)) * (sp[1][i] - dval);
       } else {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
           const bool vis = row_ok && key <= lim && l2 != -INFINITY;
-          const float p = vis ? exp2_fast(fmaf(s[i], c2, -l2)) : 0.f;
-          ds[i] = p * (dp[i] - dval);
+          const float p = vis ? exp2_fast(fmaf(sp[0][i], c2, -l2)) : 0.f;
+          ds[i] = p * (sp[1][i] - dval);
         }
       }
       // dQ += dS K: A = dS (row = query, k = keys 8h + 0..7 of k-step ks),
-      // B = K read transposed (k = key, column = head dim)
-      const bf16x8 a0 = pack_operand(ds, 0), a1 = pack_operand(ds, 1);
-#pragma unroll
-      for (int ct = 0; ct < NTILE; ++ct) {
-        acc[ct] = mfma32x32x16(a0, col_operand<D>(kt, ct, 2 * half), acc[ct]);
-        acc[ct] =
-            mfma32x32x16(a1, col_operand<D>(kt, ct, 2 * half + 1), acc[ct]);
-      }
+      // B = K read transposed (k = key, column = head dim); product i:
+      // k-step i / NTILE, tile i % NTILE
+      const bf16x8 a2[2] = {pack_operand(ds, 0), pack_operand(ds, 1)};
+      lds_pipeline<2 * NTILE, 4>(
+          [&](int i) {
+            return col_operand<D>(kt, i % NTILE, 2 * half + i / NTILE);
+          },
+          [&](int i, bf16x8 b2) {
+            acc[i % NTILE] = mfma32x32x16(a2[i / NTILE], b2, acc[i % NTILE]);
+          });
     }
-    if (j + 1 < nblk) pf.store(smem + ((j + 1) & 1) * Pf::BYTES);
+    wait_vmcnt0();  // this wave's copies for the next step have landed
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 2 <= nblk; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    step(j + 1, std::integral_constant<int, 1>{});
   }
+  if (j < nblk) step(j, std::integral_constant<int, 0>{});
 
   // epilogue: lane holds dQ rows 8(i/4) + 4h + i%4 of the wave's 32 rows,
   // column 32 ct + col
@@ -554,7 +650,7 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v,
     const int n_kblk = (s.Nk + 127) / 128;
     const long long items = (long long)s.B * s.Hkv * n_kblk;
     hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT_F32>),
-                       dim3((unsigned)items), dim3(NT), 0, stream,
+                       dim3((unsigned)items), dim3(NT2), 0, stream,
                        static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v),

@@ -307,7 +307,10 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
   // modulo the swizzle period for every m), lse2 by wave 0, D by wave 1
   static_assert((2 * Dma::NI) % 8 == 0, "copy split");
   const uint32_t loff = Dma::lane_off(wave);
-  int pg = 0, pt = t_begin;  // query head and row step of the next copy
+  // Row steps run from the last one down, so that the workgroups of one KV
+  // head (which start at different rows under the causal mask) sweep the
+  // same Q / dO tiles at about the same time and share them in L2.
+  int pg = 0, pt = t_end - 1;  // query head and row step of the next copy
   auto copy_step = [&](char* dst) {
     const int64_t qh = (int64_t)(b * Hq + hkv * G + pg) * Nq;
     const int r0 = pt * QR;
@@ -322,8 +325,8 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
     float* st = reinterpret_cast<float*>(dst + 2 * QR * T::ROWP);
     if (wave == 0) Dma::issue_vec(st, lse2 + qh, Nq, r0);
     if (wave == 1) Dma::issue_vec(st + QR, dvec + qh, Nq, r0);
-    if (++pt == t_end) {
-      pt = t_begin;
+    if (--pt < t_begin) {
+      pt = t_end - 1;
       ++pg;
     }
   };
@@ -331,7 +334,7 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
   wait_vmcnt0();
   __syncthreads();
 
-  int ct_row = t_begin;  // row step being computed
+  int ct_row = t_end - 1;  // row step being computed
   // one step on stage PAR (a compile-time constant, so that every LDS
   // address of the step is a per-lane base plus an immediate)
   auto step = [&](int it, auto par) {
@@ -341,7 +344,7 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
     const float* ls = reinterpret_cast<const float*>(qt + 2 * QR * T::ROWP);
     const float* dd = ls + QR;
     const int q0 = ct_row * QR;
-    if (++ct_row == t_end) ct_row = t_begin;
+    if (--ct_row < t_begin) ct_row = t_end - 1;
     if (it + 1 < n_it) copy_step(smem + (1 - PAR) * STAGE);
 
     // Products on rows 32 half .. +31 of the step: C row 8(i/4) + 4h + i%4

@@ -57,12 +57,17 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "c73f8cd525a209448786782812b59896fc3e0396d40456b7740b8982be02394d",
-        "fetch_kib": 71335.6, "write_kib": 66560.0},
+        "sha256": "b2d0b27edc9ab6dc8c0d04ec40045f448aac4dd87911d2ce700dc0169683b4b3",
+        "fetch_kib": 71224.3, "write_kib": 66560.1},
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
         "sha256": "306a441bd62b0447f9f16819591f9ebd64c71d1fc8e40208d050919ddc47dc60",
         "fetch_kib": 1048941.8, "write_kib": 2125.6},
+    # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
+    "gqa_prefill_bwd": {
+        "source": "fa_backward.hip",
+        "sha256": "119116b2d718856d937ba34058a877868267ec6ac6256c961bbe44f022ce1fc0",
+        "fetch_kib": 548263.1, "write_kib": 123563.3},
 }
 
 

@@ -5,9 +5,9 @@
 
 A step is one ``fa_fwd`` call over the whole workload with inputs resident
 in HBM.  W untimed steps, then exactly K timed steps bracketed by device
-synchronisation; each launch is also bracketed by HIP events on the stream
-it runs on, which gives the average kernel duration used for the roofline.
-Prints ONE JSON line.
+synchronisation; a pair of HIP events on the stream the kernels run on
+brackets the K steps too, which gives the average device time of a step
+used for the roofline.  Prints ONE JSON line.
 
 Default workload: causal GQA prefill shaped like Qwen3-4B attention
 (B=1, Hq=32, Hkv=8, N=8192, d=128), the configuration the headline metric
@@ -61,8 +61,8 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 71224.3, "write_kib": 66560.1},
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "306a441bd62b0447f9f16819591f9ebd64c71d1fc8e40208d050919ddc47dc60",
-        "fetch_kib": 1048941.8, "write_kib": 2125.6},
+        "sha256": "b7f66908ccadcd721fedbd707a472bd6009b5aa149773822b4b614e31865197f",
+        "fetch_kib": 1049002.2, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",
@@ -160,7 +160,7 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gqa_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0,
@@ -226,16 +226,18 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    # one HIP event pair on the launch stream around the K timed steps: the
+    # average device time of a step, back to back as a real loop runs them
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(args.steps):
         step()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_ms = sum(s.elapsed_time(e) for s, e in zip(starts, ends)) / args.steps
+    kern_ms = start.elapsed_time(end) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     count = attention_bwd_flops if backward else attention_fwd_flops

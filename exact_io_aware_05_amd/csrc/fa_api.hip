@@ -119,6 +119,8 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
   if (workspace_bytes < fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d,
                                                     num_splits))
     return FA_ERR_INVALID_ARG;
+  // the partial kernel addresses one K or V head with 32-bit byte offsets
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   const long long rowtiles = ((long long)Nq * (Hq / Hkv) + fa::kSplitRows - 1) /
                              fa::kSplitRows;
   if ((long long)B * Hkv * rowtiles * num_splits > (1LL << 31) - 64)
@@ -141,10 +143,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
   if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
     return FA_ERR_UNSUPPORTED;
-  // the prefill kernel's buffer resources span one K/V head in 32-bit
-  // byte offsets
-  if (splits == 0 && (long long)Nk * d * 2 > (1LL << 31) - 1)
-    return FA_ERR_UNSUPPORTED;
+  // both kernels address one K/V head with 32-bit byte offsets
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != FA_OK) return st;
   const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};

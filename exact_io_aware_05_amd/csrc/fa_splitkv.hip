@@ -8,19 +8,26 @@
 // Partial kernel: one wave per (batch, KV head, block of 32 packed query
 // rows, chunk).  The packed rows are the (query, head-in-group) pairs of
 // one KV head, so the Hq/Hkv query heads that share a KV head read each
-// K/V byte once.  The step is HBM-bound, so K and V are read straight into
-// matrix-core operand registers with no LDS round trip and no barrier, the
-// next 32-key block is fetched while the current one is computed, and the
-// transposition V needs for the P V product is done in registers:
-// * S^T = K Q^T on v_mfma_f32_32x32x16_bf16.  The contraction index (head
-//   dimension) is permuted so that each lane reads one contiguous half row
-//   of K (16 bytes per step); Q uses the same permutation.  Score register
+// K/V byte once.  The step is HBM-bound; the waves of a workgroup are
+// independent (no barrier), each streaming its 32-key blocks through a
+// ring of 4 (the loads of the next 3 blocks in flight while one is
+// computed), with non-temporal loads:
+// * K moves HBM -> LDS with buffer_load ... lds, each instruction reading
+//   four whole rows (coalesced), into a per-wave LDS slot in a swizzled
+//   row-major layout; S^T = K Q^T on v_mfma_f32_32x32x16_bf16 then reads
+//   its A operands from LDS without bank conflicts.  The contraction index
+//   (head dimension) is permuted so that a lane's operands are one
+//   contiguous half row of K; Q uses the same permutation.  Score register
 //   r of a lane holds key 16(r/8) + 8h + r%8 (the A-operand row order is
 //   chosen for that), which is the B-operand layout of P for the P V step.
 // * O^T = V^T P^T: a lane loads 8 consecutive V rows at head-dimension
-//   columns 4 col .. 4 col + 3 (whole rows are read per instruction) and
-//   v_perm_b32 repacks them into the A operands of 4 output tiles, where
-//   tile t, operand row a is head-dimension column 4a + t.
+//   columns 4 col .. 4 col + 3 into registers (whole rows per
+//   instruction) and v_perm_b32 repacks them into the A operands of 4
+//   output tiles, where tile t, operand row a is head-dimension column
+//   4a + t.
+// * Every load is issued unconditionally through buffer resources that end
+//   at the chunk's last key, so the number of loads in flight is the same
+//   on every path and the compiler waits for exactly the block it needs.
 // Merge kernel: one wave per output row, chunks visited in order.
 #include "fa_device.h"
 #include "fa_internal.h"
@@ -30,41 +37,88 @@ namespace {
 
 constexpr int KB = kSplitKeys;  // 32 keys per block
 constexpr int NT = 256;         // 4 independent waves per workgroup
+// Cache policy of the K/V loads: non-temporal (each cached byte is read
+// once per KV head, so keeping it in the caches only evicts other data).
+constexpr int kStreamAux = 2;
 
-// Per-wave register state of one 32-key block.
+typedef __attribute__((address_space(3))) void lds_void;
+
+// K of one 32-key block sits in a per-wave LDS slot, row-major with 16-byte
+// chunk c of row r stored at chunk c ^ kswz(r): the 16 lanes that read one
+// operand chunk of 16 different rows then hit 16 different bank groups.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+
+// Per-wave state of one 32-key block: K copied HBM -> LDS by buffer_load
+// ... lds (each instruction reads whole rows, so the loads are coalesced),
+// V loaded into registers.
 template <int D>
 struct KvRegs {
   static constexpr int NSTEP = D / 16;  // score k-steps
   static constexpr int CPL = D / 32;    // V columns per lane (= O^T tiles)
-  u32x4 kf[NSTEP];                      // K operand, one per k-step
+  static constexpr int KBYTES = KB * 2 * D;   // one K slot
+  static constexpr int NI = KBYTES / 1024;    // copy instructions per block
+  static constexpr int RPK = 1024 / (2 * D);  // K rows per instruction
   // V: [k-step s][row e] -> CPL bf16 values (CPL/2 dwords)
   uint32_t vr[2][8][CPL / 2];
 
-  __device__ __forceinline__ void load(const uint16_t* kh, const uint16_t* vh,
-                                       int kb, int Nk, int h, int col) {
-    // K row for operand row `col`: key 16(a/8)... realised by the bit swap
-    const int kr = kb + ((col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1));
-    const bool kok = kr < Nk;
-    const uint16_t* kp = kh + (int64_t)(kok ? kr : 0) * D + (D / 2) * h;
+  // source offset of this lane within copy instruction i: row RPK i +
+  // lane / CPR of the block, the chunk that the swizzle puts at lane % CPR
+  static __device__ __forceinline__ uint32_t k_lane_off(int i) {
+    constexpr int CPR = 2 * D / 16;
+    const int lane = threadIdx.x & 63;
+    const int r = lane / CPR, p = lane % CPR;
+    return (uint32_t)(r * 2 * D + 16 * (p ^ kswz<D>(RPK * i + r)));
+  }
+
+  // Loads block rows kb .. kb + 31: K into the LDS slot, V into registers.
+  // Every load is issued unconditionally through buffer resources that end
+  // at row `end` (the chunk's last key + 1), so rows past it arrive as
+  // zeros without touching memory, and the number of loads in flight is
+  // the same on every path (which lets the compiler wait for just the
+  // block it needs).
+  __device__ __forceinline__ void load(char* kslot, const uint32_t* koff,
+                                       const uint16_t* kh,
+                                       __amdgpu_buffer_rsrc_t vrs, int kb,
+                                       int end, int h, int col) {
 #pragma unroll
-    for (int t = 0; t < NSTEP; ++t)
-      kf[t] = kok ? ldg16(kp + 8 * t) : u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = kb + RPK * i;
+      const uint32_t rem = r0 < end ? (uint32_t)(end - r0) * (2 * D) : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          buffer_rsrc(kh + (int64_t)r0 * D, rem),
+          (lds_void*)(kslot + 1024 * i), 16, koff[i % (16 / RPK)], 0, 0,
+          kStreamAux);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int vrow = kb + 16 * s + 8 * h + e;
-        const bool vok = vrow < Nk;
-        const uint16_t* vp = vh + (int64_t)(vok ? vrow : 0) * D + CPL * col;
+        const int off = vrow * (2 * D) + 2 * CPL * col;
         if (CPL == 4) {
-          u32x2 x = vok ? *reinterpret_cast<const u32x2*>(vp) : u32x2{0u, 0u};
+          const u32x2 x = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
           vr[s][e][0] = x[0];
           vr[s][e][CPL / 2 - 1] = x[1];
         } else {
-          vr[s][e][0] = vok ? *reinterpret_cast<const uint32_t*>(vp) : 0u;
+          vr[s][e][0] =
+              __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, kStreamAux);
         }
       }
     }
+  }
+
+  // K operand of k-step t for lane (col, h): row kr of the block (the
+  // A-operand row order realised by the bit swap), head-dimension chunk
+  // (D/16) h + t (each lane half covers one contiguous half row)
+  static __device__ __forceinline__ bf16x8 kop(const char* kslot, int kr,
+                                               int h, int t) {
+    const int c = (D / 16) * h + t;
+    return *reinterpret_cast<const bf16x8*>(kslot + kr * (2 * D) +
+                                            16 * (c ^ kswz<D>(kr)));
   }
 
   // A operand (V^T) of output tile tt for k-step s: 8 keys of column
@@ -137,6 +191,7 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
 #pragma unroll
   for (int i = 0; i < CPL; ++i) acc[i] = f32x16{};
   float m = -INFINITY, l = 0.f, lb = 0.f;
+  const int krow = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
 
   // K/V blocks stream through a ring of PF register buffers: the loads of
   // the next PF - 1 blocks are in flight while a block is computed (the
@@ -144,17 +199,26 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   // flight to cover the memory latency).  The loop is unrolled by PF so
   // that every buffer index is a compile-time constant.
   constexpr int PF = 4;
-  KvRegs<D> buf[PF];
+  using KV = KvRegs<D>;
+  __shared__ __attribute__((aligned(1024))) char kring[NT / 64][PF][KV::KBYTES];
+  char (*slots)[KV::KBYTES] = kring[threadIdx.x >> 6];
+  uint32_t koff[16 / KV::RPK];
+#pragma unroll
+  for (int i = 0; i < 16 / KV::RPK; ++i) koff[i] = KV::k_lane_off(i);
+  // rows this chunk reads: up to its last block (or the causal limit)
+  const int end = min(Nk, max(blk1, blk0) * KB);
+  const __amdgpu_buffer_rsrc_t vrs =
+      buffer_rsrc(vh, (uint32_t)max(end, 0) * (2 * D));
+  KV buf[PF];
 #pragma unroll
   for (int u = 0; u < PF - 1; ++u)
-    if (blk0 + u < blk1) buf[u].load(kh, vh, (blk0 + u) * KB, Nk, h, col);
-
-  auto compute = [&](const KvRegs<D>& cur, int blk) {
+    buf[u].load(slots[u], koff, kh, vrs, (blk0 + u) * KB, end, h, col);
+  auto compute = [&](const KV& cur, const char* kslot, int blk) {
     const int kb = blk * KB;
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t)
-      s = mfma32x32x16(__builtin_bit_cast(bf16x8, cur.kf[t]), qf[t], s);
+      s = mfma32x32x16(KV::kop(kslot, krow, h, t), qf[t], s);
 
     const bool need_mask = kb + KB - 1 > lim_first;
     uint32_t vis = 0xffffu;
@@ -209,15 +273,15 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   for (int blk = blk0; blk < blk1; blk += PF) {
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
-      if (blk + u < blk1) {
-        // refill the buffer the previous step consumed
-        if (blk + u + PF - 1 < blk1)
-          buf[(u + PF - 1) % PF].load(kh, vh, (blk + u + PF - 1) * KB, Nk, h,
-                                      col);
-        compute(buf[u], blk + u);
-      }
+      // refill the buffer the previous step consumed (past the chunk's end
+      // the loads read zeros and are never used)
+      buf[(u + PF - 1) % PF].load(slots[(u + PF - 1) % PF], koff, kh, vrs,
+                                  (blk + u + PF - 1) * KB, end, h, col);
+      if (blk + u < blk1) compute(buf[u], slots[u], blk + u);
     }
   }
+  // no copy into LDS may still be in flight when the wave ends
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   // ---- partial result of this chunk (unnormalised O, max m, sum l)
   const float lt = pair_sum(l);

@@ -84,9 +84,10 @@ enum { FA_OUT_BF16 = 0, FA_OUT_F32 = 1 };
  * Attention forward.  Picks the execution form by shape: the tiled prefill
  * kernel (a workgroup per block of 256 query rows of one head) when there
  * are enough query rows to fill the GPU, otherwise the KV-split form with
- * fa_default_num_splits() chunks.  The prefill form addresses one K or V
- * head with 32-bit byte offsets, so Nk * d * 2 must stay below 2^31
- * (FA_ERR_UNSUPPORTED otherwise; Nk < 8388608 at d = 128).  The KV-split form needs a temporary fp32
+ * fa_default_num_splits() chunks.  Both forms address one K or V head
+ * with 32-bit byte offsets, so Nk * d * 2 must stay below 2^31
+ * (FA_ERR_UNSUPPORTED otherwise; Nk < 8388608 at d = 128).  The KV-split
+ * form needs a temporary fp32
  * workspace (fa_splitkv_workspace_bytes), which this call takes with
  * hipMallocAsync on `stream` and returns with hipFreeAsync on the same
  * stream.  `stream` may be NULL (the null stream).
@@ -105,7 +106,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * nothing.  `workspace` is a device buffer of at least
  * fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) bytes, 16-byte
  * aligned; its contents on entry do not matter and on return are scratch.
- * num_splits must be in [1, 4096].
+ * num_splits must be in [1, 4096].  Nk * d * 2 must stay below 2^31, as
+ * for fa_fwd (FA_ERR_UNSUPPORTED otherwise).
  */
 size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d,
                                   int num_splits);

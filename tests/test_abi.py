@@ -104,6 +104,15 @@ def test_splitkv_invalid_arguments(lib, kw):
     assert _split(lib, **kw) == _lib.FA_ERR_INVALID_ARG
 
 
+def test_splitkv_kv_head_range(lib):
+    # one K/V head must span < 2^31 bytes in the KV-split form too
+    assert _split(lib, Hq=1, Hkv=1, Nq=1, Nk=1 << 23, d=128, S=1,
+                  wsb=1 << 20) == _lib.FA_ERR_UNSUPPORTED
+    assert _fwd(lib, Hq=1, Hkv=1, Nq=1, Nk=1 << 23, d=128) == \
+        _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+
+
 def test_splitkv_workspace_size(lib):
     # rows * splits * (d fp32 partial outputs + (m, l, lb, unused) fp32)
     assert lib.fa_splitkv_workspace_bytes(16, 32, 1, 128, 16) == \

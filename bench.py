@@ -61,13 +61,13 @@ MEASURED_TRAFFIC = {
         "fetch_kib": 71224.3, "write_kib": 66560.1},
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "b7f66908ccadcd721fedbd707a472bd6009b5aa149773822b4b614e31865197f",
-        "fetch_kib": 1049002.2, "write_kib": 2112.0},
+        "sha256": "3025497eb28833847f3d1d28ac24891368e33999e6a3aaf8173c5b74c56a3917",
+        "fetch_kib": 1048897.2, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "119116b2d718856d937ba34058a877868267ec6ac6256c961bbe44f022ce1fc0",
-        "fetch_kib": 548263.1, "write_kib": 123563.3},
+        "sha256": "b7f748803f3cfa55fcf1309956fc96e6f29d7a8f9cac52701547fd73d8fdeca0",
+        "fetch_kib": 612021.6, "write_kib": 100352.2},
 }
 
 

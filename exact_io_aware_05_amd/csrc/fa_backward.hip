@@ -262,7 +262,9 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
                                                       4 * XFLOATS * 4];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index, uniform (so buffer resources and LDS bases of copies stay
+  // in scalar registers instead of going through per-lane loops)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, col = lane & 31;
   const bool pw = wave < 4;  // P wave (K, dV) or dS wave (V, dK)
   const int kw = wave & 3;   // key group
@@ -478,7 +480,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(1024))) char smem[2 * STAGE];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // wave index, uniform (so buffer resources and LDS bases of copies stay
+  // in scalar registers instead of going through per-lane loops)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 5, col = lane & 31;
 
   // work item: (b, kv head, Q block of 128, head in group); causal: late

@@ -61,6 +61,7 @@ struct KvRegs {
   static constexpr int KBYTES = KB * 2 * D;   // one K slot
   static constexpr int NI = KBYTES / 1024;    // copy instructions per block
   static constexpr int RPK = 1024 / (2 * D);  // K rows per instruction
+  static constexpr int OPS = NI + 16;         // loads per block
   // V: [k-step s][row e] -> CPL bf16 values (CPL/2 dwords)
   uint32_t vr[2][8][CPL / 2];
 
@@ -73,7 +74,9 @@ struct KvRegs {
     return (uint32_t)(r * 2 * D + 16 * (p ^ kswz<D>(RPK * i + r)));
   }
 
-  // Loads block rows kb .. kb + 31: K into the LDS slot, V into registers.
+  // Loads block rows kb .. kb + 31: V into registers, then K into the LDS
+  // slot (the K copies are the last OPS_K loads of a block, which the
+  // explicit wait before the K reads counts on).
   // Every load is issued unconditionally through buffer resources that end
   // at row `end` (the chunk's last key + 1), so rows past it arrive as
   // zeros without touching memory, and the number of loads in flight is
@@ -83,15 +86,6 @@ struct KvRegs {
                                        const uint16_t* kh,
                                        __amdgpu_buffer_rsrc_t vrs, int kb,
                                        int end, int h, int col) {
-#pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int r0 = kb + RPK * i;
-      const uint32_t rem = r0 < end ? (uint32_t)(end - r0) * (2 * D) : 0u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          buffer_rsrc(kh + (int64_t)r0 * D, rem),
-          (lds_void*)(kslot + 1024 * i), 16, koff[i % (16 / RPK)], 0, 0,
-          kStreamAux);
-    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -108,6 +102,15 @@ struct KvRegs {
               __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, kStreamAux);
         }
       }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int r0 = kb + RPK * i;
+      const uint32_t rem = r0 < end ? (uint32_t)(end - r0) * (2 * D) : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          buffer_rsrc(kh + (int64_t)r0 * D, rem),
+          (lds_void*)(kslot + 1024 * i), 16, koff[i % (16 / RPK)], 0, 0,
+          kStreamAux);
     }
   }
 
@@ -143,7 +146,10 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   constexpr int NSTEP = D / 16;
   constexpr int CPL = D / 32;
   const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
+  // wave index, uniform (so buffer resources and LDS bases of copies stay
+  // in scalar registers instead of going through per-lane loops)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int item = blockIdx.x * (NT / 64) + wave;
   if (item >= n_items) return;  // whole wave leaves; no barrier below
   const int h = lane >> 5, col = lane & 31;
 
@@ -201,7 +207,7 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   constexpr int PF = 4;
   using KV = KvRegs<D>;
   __shared__ __attribute__((aligned(1024))) char kring[NT / 64][PF][KV::KBYTES];
-  char (*slots)[KV::KBYTES] = kring[threadIdx.x >> 6];
+  char (*slots)[KV::KBYTES] = kring[wave];
   uint32_t koff[16 / KV::RPK];
 #pragma unroll
   for (int i = 0; i < 16 / KV::RPK; ++i) koff[i] = KV::k_lane_off(i);
@@ -215,6 +221,16 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     buf[u].load(slots[u], koff, kh, vrs, (blk0 + u) * KB, end, h, col);
   auto compute = [&](const KV& cur, const char* kslot, int blk) {
     const int kb = blk * KB;
+    // The compiler does not order these LDS reads after the copies that
+    // filled the slot PF - 1 blocks ago, so wait for them here: the loads of
+    // the PF - 1 later blocks are issued after this block's K copies (more
+    // than the counter holds means those copies have completed).
+    constexpr int kAfter = (PF - 1) * KV::OPS;
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((kAfter > 62 ? 62 : kAfter) & 15 |
+                               (((kAfter > 62 ? 62 : kAfter) >> 4) << 14) |
+                               0x0F70);
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t)

@@ -18,6 +18,9 @@ kernel + merge kernel).  ``--workload gqa_prefill_bwd`` times the backward
 pass of the GQA prefill: one ``fa_bwd`` call (row preprocessing, dK/dV
 kernel, dQ kernel) per step, from the O and lse of one untimed forward,
 priced at 2.5 times the forward FLOPs; its roofline covers the whole call.
+``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
+causal prompts (seeded log-uniform lengths in [256, 8192], 32768 tokens,
+the GQA heads above), priced at the causal FLOPs of each sequence.
 
 The CPU baseline is the float64 oracle (test infrastructure) timed on the
 host on a bounded sample of the same workload: whole heads of the prefill,
@@ -37,14 +40,15 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from fa_inputs import make_dout, make_inputs, workload  # noqa: E402
+from fa_inputs import (VARLEN_PREFILL, make_dout, make_inputs,  # noqa: E402
+                       make_varlen, varlen_lengths, workload)
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
     PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_bwd_flops,
     attention_fwd_bytes, attention_fwd_flops)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
-             "tiny": 0, "gqa_prefill_bwd": 3}
+             "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None}
 # HBM bytes per launch of each workload's dominant kernel, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch; summaries under profiles/).  Each counter is scaled by what it
@@ -57,8 +61,12 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "b2d0b27edc9ab6dc8c0d04ec40045f448aac4dd87911d2ce700dc0169683b4b3",
-        "fetch_kib": 71224.3, "write_kib": 66560.1},
+        "sha256": "194f8c44a4c50a2fcb8accd97157ba0f0dfc19087963db25debf459eacffa4d4",
+        "fetch_kib": 71270.1, "write_kib": 66560.1},
+    "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
+        "source": "fa_prefill.hip",
+        "sha256": "194f8c44a4c50a2fcb8accd97157ba0f0dfc19087963db25debf459eacffa4d4",
+        "fetch_kib": 514048.7, "write_kib": 266357.8},
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
         "sha256": "3025497eb28833847f3d1d28ac24891368e33999e6a3aaf8173c5b74c56a3917",
@@ -91,18 +99,23 @@ def _dev_tensor(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
 
 
+def _blas_threads():
+    """Threads of the BLAS behind numpy (the oracle's matmuls)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()
+                    if i.get("internal_api") in ("openblas", "mkl", "blis")),
+                   default=os.cpu_count())
+    except Exception:
+        return os.cpu_count()
+
+
 def cpu_baseline(w, q, k, v, budget_s=10.0, do=None):
     """Oracle TFLOP/s on whole heads of batch 0, one head at a time (the
     gradient oracle when ``do`` is given)."""
     from fa_inputs import bf16_bits_to_f64
     from oracle import reference_attention, reference_attention_backward
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()
-                       if i.get("internal_api") in ("openblas", "mkl", "blis")),
-                      default=os.cpu_count())
-    except Exception:
-        threads = os.cpu_count()
+    threads = _blas_threads()
     G = w.Hq // w.Hkv
     scale = float(np.float32(w.scale))
     done, t_total = 0, 0.0
@@ -156,6 +169,107 @@ def calibrate_copy(mib, steps, warmup):
     return 0
 
 
+def _time_steps(step, steps, warmup, stream):
+    """W untimed steps, then K steps between device synchronisations with
+    one HIP event pair on the launch stream: (wall ms, device ms) per step."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, start.elapsed_time(end) / steps
+
+
+def cpu_baseline_varlen(spec, lens, q, k, v, cu, budget_s=10.0):
+    """Oracle TFLOP/s on whole (sequence, head) pairs of the packed batch,
+    in order (sequence 0 head 0, head 1, ...), until about 10 s of work."""
+    from fa_inputs import bf16_bits_to_f64
+    from oracle import reference_attention
+    G = spec["Hq"] // spec["Hkv"]
+    scale = float(np.float32(spec["scale"]))
+    flops, t_total, done = 0.0, 0.0, 0
+    pairs = [(b, h) for b in range(len(lens)) for h in range(spec["Hq"])]
+    for b, h in pairs:
+        if t_total >= budget_s:
+            break
+        r = slice(int(cu[b]), int(cu[b + 1]))
+        qh = bf16_bits_to_f64(q[r, h])[None, None]
+        kh = bf16_bits_to_f64(k[r, h // G])[None, None]
+        vh = bf16_bits_to_f64(v[r, h // G])[None, None]
+        t0 = time.perf_counter()
+        reference_attention(qh, kh, vh, causal=spec["causal"], scale=scale)
+        t_total += time.perf_counter() - t0
+        flops += attention_fwd_flops(1, 1, lens[b], lens[b], spec["d"],
+                                     spec["causal"])
+        done += 1
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
+            "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{done} of {len(pairs)} (sequence, head) pairs, in "
+                      f"order from sequence 0 head 0, float64 numpy; "
+                      f"{t_total:.1f} s"}
+
+
+def bench_varlen(args):
+    """One fa_fwd_varlen call over a packed batch of causal prompts."""
+    import torch
+    from exact_io_aware_05_amd import ops
+    spec = VARLEN_PREFILL
+    lens = varlen_lengths(spec["total"], spec["lo"], spec["hi"], seed=0)
+    q, k, v, cu_q, cu_k = make_varlen(lens, lens, spec["Hq"], spec["Hkv"],
+                                      spec["d"], seed=0)
+    Q, K, V = _dev_tensor(q), _dev_tensor(k), _dev_tensor(v)
+    CQ = torch.from_numpy(cu_q).cuda()
+    CK = torch.from_numpy(cu_k).cuda()
+    total, Hq, d = Q.shape
+    o = torch.empty((total, Hq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((Hq, total), dtype=torch.float32, device="cuda")
+    mx = max(lens)
+
+    def step():
+        ops.fa_fwd_varlen(Q, K, V, CQ, CK, mx, mx, causal=spec["causal"],
+                          scale=spec["scale"], o=o, lse=lse)
+
+    ms, kern_ms = _time_steps(step, args.steps, args.warmup,
+                              torch.cuda.current_stream())
+    flops = sum(attention_fwd_flops(1, Hq, n, n, d, spec["causal"])
+                for n in lens)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    out = {
+        "metric": f"attn fwd TFLOP/s ({spec['name']})",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) fp32 rounded to bf16; seeded "
+                "log-uniform lengths)",
+        "config": {"workload": spec["name"], "B": len(lens), "Hq": Hq,
+                   "Hkv": spec["Hkv"], "d": d, "causal": spec["causal"],
+                   "scale": spec["scale"], "total_tokens": total,
+                   "seqlens": lens, "out_dtype": "bf16",
+                   "kernel_ms": round(kern_ms, 4),
+                   "pct_bf16_mfma_peak": round(
+                       100 * achieved / PEAK_BF16_MFMA_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+                     "traffic": measured_traffic(spec["name"])},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_varlen(spec, lens, q, k, v, cu_q)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -183,6 +297,8 @@ def main(argv=None):
     if args.calibrate_copy:
         return calibrate_copy(args.calibrate_copy, args.steps, args.warmup)
 
+    if args.workload == "varlen_prefill":
+        return bench_varlen(args)
     w = workload(WORKLOADS[args.workload])
     backward = args.workload.endswith("_bwd")
     q, k, v = make_inputs(w, seed=0)
@@ -223,22 +339,9 @@ def main(argv=None):
         def step():
             ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
     # one HIP event pair on the launch stream around the K timed steps: the
     # average device time of a step, back to back as a real loop runs them
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = start.elapsed_time(end) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    ms_per_step, kern_ms = _time_steps(step, args.steps, args.warmup, stream)
 
     count = attention_bwd_flops if backward else attention_fwd_flops
     flops = count(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)

@@ -8,7 +8,8 @@ import importlib
 from ._lib import FAError, load  # noqa: F401
 
 _LAZY = ("fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
-         "default_num_splits", "fa_bwd", "bwd_workspace_bytes")
+         "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
+         "fa_fwd_varlen")
 
 
 def __getattr__(name):

@@ -150,7 +150,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
   const bool f32 = out_dtype == FA_OUT_F32;
   if (splits == 0)
-    return hip_status(fa::launch_prefill(q, k, v, o, lse, s, f32, stream));
+    return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
+                                         fa::dense_layout(s), f32, stream));
   const size_t bytes =
       fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, splits);
   void* ws = nullptr;
@@ -160,6 +161,47 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   hipError_t e2 = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(e2);
+}
+
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int Hq, int Hkv, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                  float scale, int out_dtype, hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, max_seqlen_q,
+                        max_seqlen_k, d, scale, out_dtype);
+  if (st != FA_OK) return st;
+  if (!cu_seqlens_q || !cu_seqlens_k ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_k) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (total_q < 1 || total_k < 1) return FA_ERR_INVALID_ARG;
+  // one sequence's K/V rows of one head are addressed with 32-bit byte
+  // offsets; the grid covers every (sequence, head, 256-row block)
+  if (((long long)max_seqlen_k - 1) * Hkv * d * 2 + 2LL * d > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  const long long qblk =
+      ((long long)max_seqlen_q + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  // (the grid is rounded up to whole rounds of 8 units of Hq / Hkv heads)
+  if (((long long)B * Hkv * qblk + 7) / 8 * 8 * (Hq / Hkv) > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, max_seqlen_q, max_seqlen_k, d, causal, scale};
+  fa::SeqLayout lay{};
+  lay.q_h = d;
+  lay.q_r = (long long)Hq * d;
+  lay.k_h = d;
+  lay.k_r = (long long)Hkv * d;
+  lay.l_h = total_q;
+  lay.l_r = 1;
+  lay.cu_q = cu_seqlens_q;
+  lay.cu_k = cu_seqlens_k;
+  lay.total_q = total_q;
+  lay.total_k = total_k;
+  lay.n_seq = B;
+  return hip_status(fa::launch_prefill(q, k, v, o, lse, s, lay,
+                                       out_dtype == FA_OUT_F32, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int Hq, int Nq) {

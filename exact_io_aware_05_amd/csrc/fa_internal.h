@@ -13,6 +13,37 @@ struct Shape {
   float scale;
 };
 
+// Where the rows of one (sequence, head) live, in elements: batch, head and
+// row strides of Q and O (same shape), of K and V, and of lse.  Fixed-length
+// batches have cu_q = cu_k = nullptr.  Packed variable-length batches take
+// sequence b's rows from cu_q[b] .. cu_q[b + 1] (and cu_k for K/V), the
+// batch stride unused; Nq / Nk of the Shape are then the maximum lengths and
+// total_q / total_k the row counts of the packed tensors.
+struct SeqLayout {
+  long long q_b, q_h, q_r;
+  long long k_b, k_h, k_r;
+  long long l_b, l_h, l_r;
+  const int* cu_q;
+  const int* cu_k;
+  int total_q, total_k;
+  int n_seq;  // sequences of a packed batch (cu_q, cu_k: n_seq + 1 entries)
+};
+
+// [B, H, N, d] contiguous tensors, lse [B, Hq, Nq].
+inline SeqLayout dense_layout(const Shape& s) {
+  SeqLayout l{};
+  l.q_r = s.d;
+  l.q_h = (long long)s.Nq * s.d;
+  l.q_b = l.q_h * s.Hq;
+  l.k_r = s.d;
+  l.k_h = (long long)s.Nk * s.d;
+  l.k_b = l.k_h * s.Hkv;
+  l.l_r = 1;
+  l.l_h = s.Nq;
+  l.l_b = (long long)s.Hq * s.Nq;
+  return l;
+}
+
 // Rows of queries per prefill workgroup and keys per streamed K/V block.
 constexpr int kPrefillRows = 256;
 constexpr int kPrefillKeys = 64;
@@ -22,7 +53,8 @@ constexpr int kSplitRows = 32;
 constexpr int kMaxSplits = 4096;
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v,
-                          void* o, float* lse, const Shape& s, bool out_f32,
+                          void* o, float* lse, const Shape& s,
+                          const SeqLayout& lay, bool out_f32,
                           hipStream_t stream);
 
 hipError_t launch_splitkv(const void* q, const void* k, const void* v,

@@ -102,25 +102,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base,
 }
 
 // Starts the HBM -> LDS copy of block `blk` (64 rows) of one K or V head
-// (`head`: its row 0) into the LDS buffer at `dst`, shared by the NW waves:
-// wave w issues 1 KiB buffer_load ... lds instructions i = w, w + NW, ...;
-// instruction i reads from lane offset `lane_off` plus `step * i` bytes.  Rows at or past Nk read as zeros (buffer range check
-// on the per-instruction resource); a block wholly past Nk is a copy of
-// zeros, which keeps the number of copies per loop iteration fixed.
+// (`head`: its row 0; rows `rsb` bytes apart) into the LDS buffer at `dst`,
+// shared by the NW waves: wave w issues 1 KiB buffer_load ... lds
+// instructions i = w, w + NW, ...; instruction i reads from lane offset
+// `lane_off` plus `step * i` bytes.  Rows at or past Nk read as zeros
+// (buffer range check on the per-instruction resource, which ends at the
+// end of row Nk - 1); a block wholly past Nk is a copy of zeros, which
+// keeps the number of copies per loop iteration fixed.
 template <int D>
 __device__ __forceinline__ void copy_block(char* dst, const char* head,
                                            int Nk, int blk, int wave,
-                                           uint32_t lane_off, int step) {
-  // (Nk here: number of rows that may be read; later rows read as zeros)
+                                           uint32_t lane_off, int step,
+                                           int rsb) {
+  // (Nk here: number of rows that may be read; later rows read as zeros.
+  // A head spans less than 2^31 bytes, so 32-bit offsets suffice.)
   using L = Layout<D>;
   const int kb = min(blk * BC, Nk);
-  const char* base = head + (int64_t)kb * L::ROWB;
-  const int rem = (Nk - kb) * L::ROWB;
+  const char* base = head + (int64_t)kb * rsb;
+  const int rem = kb < Nk ? (Nk - kb - 1) * rsb + L::ROWB : 0;
 #pragma unroll
   for (int n = 0; n < L::NINS / NW; ++n) {
     const int i = wave + NW * n;
+    const int left = rem - step * i;
     const __amdgpu_buffer_rsrc_t r =
-        rsrc(base + step * i, (uint32_t)max(rem - step * i, 0));
+        rsrc(base + step * i, (uint32_t)(left > 0 ? left : 0));
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         r, (lds_void*)(dst + 1024 * i), 16, lane_off, 0, 0, 0);
   }
@@ -318,8 +323,8 @@ template <int D, bool CAUSAL, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, void* __restrict__ o,
-    float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk, float c2,
-    int n_qblk, int n_items) {
+    float* __restrict__ lse, int Hq, int Hkv, int Nq_max, int Nk_max,
+    float c2, int n_qblk, int n_items, SeqLayout lay) {
   using L = Layout<D>;
   constexpr int NTILE = L::NTILE;
   constexpr int NSTEP = L::NSTEP;
@@ -332,21 +337,63 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   const int h = lane >> 5, col = lane & 31;
 
   // ---- work item: (b, kv head, Q block, head in group); heavy blocks first
-  const int item = xcd_contiguous(blockIdx.x, n_items);
   const int G = Hq / Hkv;
-  const int g = item % G;
-  const int t1 = item / G;
-  const int jq = t1 % n_qblk;
-  const int bh = t1 / n_qblk;  // b * Hkv + hkv
+  int g, jq, bh;  // bh = b * Hkv + hkv
+  if (lay.cu_q) {
+    // packed batch of unequal sequences: unit u = (Q block rank jq, bh),
+    // jq outermost, so the blocks of every sequence are ordered by their
+    // index from the top (the heaviest first under the causal mask).  Unit
+    // u runs on XCD u % 8 and its G query heads one after another there
+    // (they read the same K/V), so every XCD takes every 8th unit of the
+    // ordered list.  The grid is the unit count times G, rounded up to a
+    // multiple of 8 G; the surplus workgroups exit here.
+    const int s8 = blockIdx.x >> 3;
+    g = s8 % G;
+    const int u = 8 * (s8 / G) + (blockIdx.x & 7);
+    const int n_bh = lay.n_seq * Hkv;
+    if (u >= n_bh * n_qblk) return;
+    jq = u / n_bh;
+    bh = u % n_bh;
+  } else {
+    // equal sequences: each XCD takes one contiguous range of items
+    // (b, kv head, Q block, head in group), so a KV head's Q blocks share
+    // that XCD's L2
+    const int item = xcd_contiguous(blockIdx.x, n_items);
+    g = item % G;
+    const int t1 = item / G;
+    jq = t1 % n_qblk;
+    bh = t1 / n_qblk;
+  }
   const int qblk = CAUSAL ? (n_qblk - 1 - jq) : jq;
   const int b = bh / Hkv, hkv = bh % Hkv;
   const int hq = hkv * G + g;
   const int q0 = qblk * BR;
-  const int off = Nk - Nq;
 
-  const int64_t qhead = (int64_t)(b * Hq + hq) * Nq;
-  const char* kh = reinterpret_cast<const char*>(k + (int64_t)bh * Nk * D);
-  const char* vh = reinterpret_cast<const char*>(v + (int64_t)bh * Nk * D);
+  // this sequence's rows: element offsets of its row 0 in this head
+  int Nq = Nq_max, Nk = Nk_max;
+  int64_t qbase, kbase, lbase;
+  if (lay.cu_q) {
+    // packed variable-length batch; lengths clamped into the packed
+    // tensors whatever the offsets hold
+    const int qs = min(max(lay.cu_q[b], 0), lay.total_q);
+    const int ks = min(max(lay.cu_k[b], 0), lay.total_k);
+    Nq = min(min(max(lay.cu_q[b + 1] - qs, 0), lay.total_q - qs), Nq_max);
+    Nk = min(min(max(lay.cu_k[b + 1] - ks, 0), lay.total_k - ks), Nk_max);
+    qbase = qs * lay.q_r + hq * lay.q_h;
+    kbase = ks * lay.k_r + hkv * lay.k_h;
+    lbase = qs * lay.l_r + hq * lay.l_h;
+  } else {
+    qbase = b * lay.q_b + hq * lay.q_h;
+    kbase = b * lay.k_b + hkv * lay.k_h;
+    lbase = b * lay.l_b + hq * lay.l_h;
+  }
+  // a Q block past this sequence's rows has nothing to do (the test is
+  // uniform over the workgroup, so no wave is left at a barrier)
+  if (q0 >= Nq) return;
+  const int off = Nk - Nq;
+  const int rsb = (int)(2 * lay.k_r);  // bytes between K (V) rows
+  const char* kh = reinterpret_cast<const char*>(k + kbase);
+  const char* vh = reinterpret_cast<const char*>(v + kbase);
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, q0 + BR + off);
@@ -362,20 +409,21 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // chunk i of all 64 rows (lane = LDS row, holding key key_slot(lane)).
   // V: instruction i copies the rows of its KiB, lane -> (row, chunk) with
   // the 16-byte chunk index XOR-swizzled by the row.
-  const uint32_t k_off = key_slot(lane) * L::ROWB;
+  const uint32_t k_off = (uint32_t)(key_slot(lane) * rsb);
   uint32_t v_off;
   {
     const int row = lane / (L::ROWB / 16);   // row within the KiB
     const int p = lane % (L::ROWB / 16);     // physical 16-byte chunk
-    v_off = row * L::ROWB + ((p ^ (vswz<D>(row) >> 1)) * 16);
+    v_off = (uint32_t)(row * rsb) + ((p ^ (vswz<D>(row) >> 1)) * 16);
   }
+  const int v_step = (1024 / L::ROWB) * rsb;  // rows of one KiB
 
   // ---- Q^T operand fragments: lane holds q[row][16t + 8h .. +7]
   const int qrow = wrow0 + col;
   bf16x8 qf[NSTEP];
   {
     const bool ok = qrow < Nq;
-    const uint16_t* qp = q + (qhead + (ok ? qrow : 0)) * D + 8 * h;
+    const uint16_t* qp = q + qbase + (ok ? qrow : 0) * lay.q_r + 8 * h;
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t) {
       u32x4 x = ok ? ldg16(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
@@ -441,20 +489,21 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
   auto copies = [&](int j) {
     copy_block<D>(smem + ((j + 3) % L::NS) * L::KBYTES, kh, kv_rows, j + 3,
-                  wave, k_off, 16);
+                  wave, k_off, 16, rsb);
     copy_block<D>(smem + L::VBASE + ((j + 2) % L::NS) * L::VBYTES, vh,
-                  kv_rows, j + 2, wave, v_off, 1024);
+                  kv_rows, j + 2, wave, v_off, v_step, rsb);
   };
   // prologue: K_0, K_1, K_2, V_0, V_1 (all waves), fully waited.  V stage 3
   // is zeroed: block 0's matrix phase multiplies it by the all-zero
   // "previous" P, and 0 * (stale NaN/Inf bits) would not be 0.
 #pragma unroll
   for (int b0 = 0; b0 < 3; ++b0)
-    copy_block<D>(smem + b0 * L::KBYTES, kh, kv_rows, b0, wave, k_off, 16);
+    copy_block<D>(smem + b0 * L::KBYTES, kh, kv_rows, b0, wave, k_off, 16,
+                  rsb);
 #pragma unroll
   for (int b0 = 0; b0 < 2; ++b0)
     copy_block<D>(smem + L::VBASE + b0 * L::VBYTES, vh, kv_rows, b0, wave,
-                  v_off, 1024);
+                  v_off, v_step, rsb);
 #pragma unroll
   for (int i = tid; i < L::VBYTES / 16; i += NT)
     reinterpret_cast<u32x4*>(smem + L::VBASE + 3 * L::VBYTES)[i] =
@@ -498,7 +547,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   const float lse_v =
       lt > 0.f ? (st.m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   if (qrow < Nq) {
-    const int64_t orow = (qhead + qrow) * D;
+    const int64_t orow = qbase + qrow * lay.q_r;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
 #pragma unroll
@@ -517,15 +566,23 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
         }
       }
     }
-    if (h == 0) lse[qhead + qrow] = lse_v;
+    if (h == 0) lse[lbase + qrow * lay.l_r] = lse_v;
   }
 }
 
 template <int D, bool CAUSAL, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
-                  float* lse, const Shape& s, hipStream_t stream) {
+                  float* lse, const Shape& s, const SeqLayout& lay,
+                  hipStream_t stream) {
   const int n_qblk = (s.Nq + BR - 1) / BR;
-  const long long n_items = (long long)s.B * s.Hq * n_qblk;
+  long long n_items = (long long)s.B * s.Hq * n_qblk;
+  // packed batch: whole rounds of 8 units of G heads (the tail's surplus
+  // workgroups exit at once)
+  if (lay.cu_q) {
+    const long long per = 8LL * (s.Hq / s.Hkv);
+    const long long units = (long long)s.B * s.Hkv * n_qblk;
+    n_items = (units + 7) / 8 * per;
+  }
   // scale 0 is run as the smallest normal scale: every exponent is then
   // below 2^-24 in magnitude, so each weight is exactly 1, and -inf scores
   // stay -inf (no 0 * inf)
@@ -535,23 +592,26 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, lse, s.Hq, s.Hkv,
-                     s.Nq, s.Nk, c2, n_qblk, (int)n_items);
+                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v,
-                          void* o, float* lse, const Shape& s, bool out_f32,
+                          void* o, float* lse, const Shape& s,
+                          const SeqLayout& lay, bool out_f32,
                           hipStream_t stream) {
   const bool c = s.causal != 0;
-#define FA_DISPATCH(D_)                                                    \
-  if (s.d == D_) {                                                         \
-    if (c)                                                                 \
-      return out_f32 ? launch<D_, true, true>(q, k, v, o, lse, s, stream)  \
-                     : launch<D_, true, false>(q, k, v, o, lse, s, stream); \
-    return out_f32 ? launch<D_, false, true>(q, k, v, o, lse, s, stream)   \
-                   : launch<D_, false, false>(q, k, v, o, lse, s, stream); \
+#define FA_DISPATCH(D_)                                                      \
+  if (s.d == D_) {                                                           \
+    if (c)                                                                   \
+      return out_f32                                                         \
+                 ? launch<D_, true, true>(q, k, v, o, lse, s, lay, stream)   \
+                 : launch<D_, true, false>(q, k, v, o, lse, s, lay, stream); \
+    return out_f32                                                           \
+               ? launch<D_, false, true>(q, k, v, o, lse, s, lay, stream)    \
+               : launch<D_, false, false>(q, k, v, o, lse, s, lay, stream);  \
   }
   FA_DISPATCH(128)
   FA_DISPATCH(64)

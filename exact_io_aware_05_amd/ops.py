@@ -18,7 +18,8 @@ import torch
 from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
-           "default_num_splits", "fa_bwd", "bwd_workspace_bytes"]
+           "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
+           "fa_fwd_varlen"]
 
 
 def _dims(q, k, v):
@@ -70,6 +71,57 @@ def fa_fwd(q, k, v, causal=False, scale=None, out_dtype=torch.bfloat16,
                        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16,
                        _stream(q))
     check(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                  max_seqlen_k, causal=False, scale=None,
+                  out_dtype=torch.bfloat16, o=None, lse=None):
+    """Packed variable-length forward through ``fa_fwd_varlen``.
+
+    q [total_q, Hq, d], k and v [total_k, Hkv, d] (bf16, contiguous),
+    cu_seqlens_q / cu_seqlens_k int32 device tensors of B + 1 row offsets;
+    returns ``(o, lse)`` with o [total_q, Hq, d] and lse [Hq, total_q]."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if (not isinstance(t, torch.Tensor) or t.dim() != 3
+                or t.dtype != torch.bfloat16 or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor "
+                             "[total, H, d]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if (not isinstance(t, torch.Tensor) or t.dim() != 1
+                or t.dtype != torch.int32 or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 device "
+                             "tensor")
+    total_q, Hq, d = q.shape
+    total_k, Hkv, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or dk != d:
+        raise ValueError("shape mismatch between q, k and v")
+    B = cu_seqlens_q.numel() - 1
+    if B < 1 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k need B + 1 entries")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    if o is None:
+        o = torch.empty((total_q, Hq, d), dtype=out_dtype, device=q.device)
+    elif (o.dtype != out_dtype or tuple(o.shape) != (total_q, Hq, d)
+          or not o.is_contiguous()):
+        raise ValueError("o has the wrong dtype, shape or layout")
+    if lse is None:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (Hq, total_q)
+          or not lse.is_contiguous()):
+        raise ValueError("lse has the wrong dtype, shape or layout")
+    st = load().fa_fwd_varlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv,
+        total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), d,
+        int(bool(causal)), scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
+    check(st, "fa_fwd_varlen")
     return o, lse
 
 

@@ -29,6 +29,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv", "make_dout",
+    "make_varlen", "VARLEN_PREFILL", "varlen_lengths",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
 ]
 
@@ -144,6 +145,50 @@ def make_dout(B, Hq, Nq, d, *, seed=0):
     rng = np.random.default_rng([seed, 0x64])
     return f32_to_bf16_bits(rng.standard_normal((B, Hq, Nq, d),
                                                 dtype=np.float32))
+
+
+def make_varlen(seqlens_q, seqlens_k, Hq, Hkv, d, *, seed=0):
+    """A packed variable-length batch: sequence b has seqlens_q[b] query rows
+    and seqlens_k[b] key/value rows.  Returns (q, k, v, cu_q, cu_k) with q
+    [total_q, Hq, d], k and v [total_k, Hkv, d] as bf16 bit patterns
+    (token-major, the rows of all sequences back to back) and the int32
+    row offsets cu_q, cu_k (B + 1 entries, from 0).  The values are drawn
+    like ``make_qkv``: N(0, 1) fp32 from ``default_rng(seed)`` (Q, then K,
+    then V, each over the whole packed tensor), rounded to bf16."""
+    seqlens_q = np.asarray(seqlens_q, dtype=np.int64)
+    seqlens_k = np.asarray(seqlens_k, dtype=np.int64)
+    if seqlens_q.shape != seqlens_k.shape or seqlens_q.ndim != 1:
+        raise ValueError("one query and one key length per sequence")
+    cu_q = np.concatenate([[0], np.cumsum(seqlens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(seqlens_k)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((int(cu_q[-1]), Hq, d), dtype=np.float32)
+    k = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
+    v = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
+    return (f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v),
+            cu_q, cu_k)
+
+
+# A packed prefill batch of variable-length sequences, a serving mix: the
+# heads of the GQA prefill workload, causal, each sequence its own prompt
+# (query and key lengths equal); lengths drawn by ``varlen_lengths``.
+VARLEN_PREFILL = dict(name="varlen_prefill_t32768_hq32_hkv8_d128_causal",
+                      total=32768, lo=256, hi=8192, Hq=32, Hkv=8, d=128,
+                      causal=True, scale=1.0 / math.sqrt(128))
+
+
+def varlen_lengths(total, lo, hi, seed=0):
+    """Sequence lengths that add up to ``total``: each drawn log-uniform in
+    [lo, hi] (``exp(uniform(log lo, log hi))`` rounded to an integer, from
+    ``default_rng([seed, 0x76])``), the last one cut to what is left."""
+    rng = np.random.default_rng([seed, 0x76])
+    out, left = [], int(total)
+    while left > 0:
+        n = int(round(math.exp(rng.uniform(math.log(lo), math.log(hi)))))
+        n = min(n, left)
+        out.append(n)
+        left -= n
+    return out
 
 
 def make_inputs(w, seed=0):

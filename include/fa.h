@@ -126,6 +126,34 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /*
+ * Forward over a packed batch of variable-length sequences (prefill form).
+ * Sequence b has the query rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1
+ * and the key/value rows cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of the
+ * packed, token-major tensors
+ *     q   [total_q, Hq,  d]  bf16        k, v [total_k, Hkv, d]  bf16
+ *     o   [total_q, Hq,  d]  bf16 or fp32 (FA_OUT_*)
+ *     lse [Hq, total_q]      fp32, natural log
+ * and is attended to on its own: the result for it is fa_fwd on its rows
+ * (GQA mapping, causal mask aligned at its own last key, scale as for
+ * fa_fwd).  cu_seqlens_q and cu_seqlens_k are DEVICE arrays of B + 1 int32
+ * offsets, non-decreasing from 0 to total_q (total_k); max_seqlen_q and
+ * max_seqlen_k bound the per-sequence lengths.  Offsets are read on the
+ * device: a length is clamped to its max_seqlen and to the packed tensor,
+ * so bad offsets give wrong results but no access outside q, k, v, o, lse.
+ * Rows of o and lse that belong to no sequence are not written.  Every
+ * sequence runs on the tiled prefill kernel (workgroups of 256 query rows).
+ * Errors as for fa_fwd; FA_ERR_INVALID_ARG also for null or misaligned
+ * offset arrays and total_q or total_k < 1; FA_ERR_UNSUPPORTED also when
+ * (max_seqlen_k - 1) * Hkv * d * 2 + 2d >= 2^31 (one sequence's K/V rows
+ * of a head are addressed with 32-bit byte offsets).
+ */
+int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
+                  float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                  int B, int Hq, int Hkv, int total_q, int total_k,
+                  int max_seqlen_q, int max_seqlen_k, int d, int causal,
+                  float scale, int out_dtype, hipStream_t stream);
+
+/*
  * Attention backward pass by recomputation ("FlashAttention Analysis",
  * ryotta.opik.net, section 4 "Recomputation"; the per-row logsumexp kept
  * for it: cost guide, section on attention memory during training).  Given

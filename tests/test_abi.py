@@ -181,6 +181,34 @@ def test_bwd_workspace_size(lib):
     assert lib.fa_bwd_workspace_bytes(1, 1, 0) == 0
 
 
+def _varlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cq=P, ck=P, B=2, Hq=4, Hkv=2, tq=32,
+             tk=40, mq=16, mk=20, d=64, causal=0, scale=0.125, out=0)
+    a.update(kw)
+    return lib.fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                             a["cq"], a["ck"], a["B"], a["Hq"], a["Hkv"],
+                             a["tq"], a["tk"], a["mq"], a["mk"], a["d"],
+                             a["causal"], a["scale"], a["out"], None)
+
+
+@pytest.mark.parametrize(
+    "kw", [dict(q=None), dict(k=P + 8), dict(o=P + 1), dict(lse=P + 2),
+           dict(cq=None), dict(ck=None), dict(cq=P + 2), dict(ck=P + 1),
+           dict(B=0), dict(Hq=6, Hkv=4), dict(tq=0), dict(tk=0), dict(mq=0),
+           dict(mk=0), dict(scale=math.nan), dict(out=3)],
+    ids=lambda k: str(k))
+def test_varlen_invalid_arguments(lib, kw):
+    assert _varlen(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_varlen_unsupported(lib):
+    assert _varlen(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    # one sequence's K/V rows of one head span (mk - 1) * Hkv * d * 2 + 2d
+    assert _varlen(lib, Hkv=8, Hq=8, mk=(1 << 20) + 2, d=128) == \
+        _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+
+
 def test_no_hip_error_recorded_by_validation(lib):
     _fwd(lib, q=None)
     _split(lib, S=0)

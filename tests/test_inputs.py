@@ -89,3 +89,22 @@ def test_workload_table():
     d = workload(4)
     assert (d.Nq, d.Nk, d.B) == (1, 32768, 16)
     assert workload(2).outliers and not workload(1).outliers
+
+
+def test_varlen_lengths_recipe():
+    from fa_inputs import VARLEN_PREFILL as S, varlen_lengths
+    lens = varlen_lengths(S["total"], S["lo"], S["hi"], seed=0)
+    assert sum(lens) == S["total"]
+    assert all(S["lo"] <= n <= S["hi"] for n in lens[:-1])
+    assert 1 <= lens[-1] <= S["hi"]
+    assert lens == varlen_lengths(S["total"], S["lo"], S["hi"], seed=0)
+    assert lens != varlen_lengths(S["total"], S["lo"], S["hi"], seed=1)
+
+
+def test_make_varlen_layout():
+    from fa_inputs import make_varlen
+    q, k, v, cu_q, cu_k = make_varlen([3, 0, 5], [4, 2, 0], 4, 2, 64, seed=3)
+    assert q.shape == (8, 4, 64) and k.shape == (6, 2, 64) == v.shape
+    assert q.dtype == np.uint16
+    assert cu_q.tolist() == [0, 3, 3, 8] and cu_k.tolist() == [0, 4, 6, 6]
+    assert cu_q.dtype == np.int32 and cu_k.dtype == np.int32

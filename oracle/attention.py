@@ -39,6 +39,14 @@ Readings where the pages are silent (each is a documented choice):
 * lse is the natural-log logsumexp of the scaled, masked scores.
 * A query row with no visible key (only causal with Nq > Nk) has O = 0 and
   lse = -inf.
+* Sliding window (the training-cost guide's FAQ names sliding windows among
+  the mask features of the fused kernels; the pages give no formula):
+  ``window = (left, right)`` keeps key ``j`` visible to query ``i`` only if
+  ``c - left <= j <= c + right`` with ``c = i + (Nk - Nq)`` the query's own
+  position on the key axis (the same bottom-right alignment as causal); a
+  negative bound is no bound on that side.  ``(-1, 0)`` is the causal mask,
+  ``(-1, -1)`` no mask; the window combines with ``causal`` by intersection.
+  Rows whose window holds no key get O = 0 and lse = -inf.
 """
 from __future__ import annotations
 
@@ -58,13 +66,23 @@ def kv_head_of(hq: int, Hq: int, Hkv: int) -> int:
     return hq // (Hq // Hkv)
 
 
-def visible_mask(rows, cols, Nq: int, Nk: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), len(cols)]: may query ``i`` attend to key ``j``."""
+def visible_mask(rows, cols, Nq: int, Nk: int, causal: bool,
+                 window=None) -> np.ndarray:
+    """Boolean [len(rows), len(cols)]: may query ``i`` attend to key ``j``.
+    ``window``: None or (left, right), a negative bound meaning none."""
     rows = np.asarray(rows, dtype=np.int64)
     cols = np.asarray(cols, dtype=np.int64)
-    if not causal:
-        return np.ones((rows.size, cols.size), dtype=bool)
-    return cols[None, :] <= rows[:, None] + (Nk - Nq)
+    vis = np.ones((rows.size, cols.size), dtype=bool)
+    if causal:
+        vis &= cols[None, :] <= rows[:, None] + (Nk - Nq)
+    if window is not None:
+        left, right = window
+        pos = rows[:, None] + (Nk - Nq)   # the query's place on the key axis
+        if left >= 0:
+            vis &= cols[None, :] >= pos - left
+        if right >= 0:
+            vis &= cols[None, :] <= pos + right
+    return vis
 
 
 def _check(q, k, v):
@@ -78,19 +96,20 @@ def _check(q, k, v):
 
 
 def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
-                        return_sp: bool = False):
+                        return_sp: bool = False, window=None):
     """The definition, with S and P materialised per head in float64.
 
     S[i, j] = scale * sum_c q[i, c] k[j, c], set to -inf where key j is not
     visible to query i; P = row softmax of S; O = P V; lse[i] = logsumexp of
     row i of S.  ``rows`` restricts the computation to some query rows (the
     result then has ``len(rows)`` rows); ``return_sp`` also returns the
-    per-head S and P arrays (shape [B, Hq, rows, Nk]).
+    per-head S and P arrays (shape [B, Hq, rows, Nk]).  ``window`` adds the
+    sliding-window bounds (left, right) of ``visible_mask``.
     """
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
     R = rows.size
-    vis = visible_mask(rows, np.arange(Nk), Nq, Nk, causal)
+    vis = visible_mask(rows, np.arange(Nk), Nq, Nk, causal, window)
     O = np.zeros((B, Hq, R, d))
     lse = np.empty((B, Hq, R))
     if return_sp:

@@ -18,7 +18,9 @@ kernel + merge kernel).  ``--workload gqa_prefill_bwd`` times the backward
 pass of the GQA prefill: one ``fa_bwd`` call (row preprocessing, dK/dV
 kernel, dQ kernel) per step, from the O and lse of one untimed forward,
 priced at 2.5 times the forward FLOPs; its roofline covers the whole call.
-``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
+``--workload gqa_prefill_window`` runs ``fa_fwd_window`` on the GQA prefill
+with a 4096-key sliding window (causal), priced at 4 d FLOPs per visible
+pair, counted exactly.  ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
 causal prompts (seeded log-uniform lengths in [256, 8192], 32768 tokens,
 the GQA heads above), priced at the causal FLOPs of each sequence.
 
@@ -44,11 +46,14 @@ from fa_inputs import (VARLEN_PREFILL, make_dout, make_inputs,  # noqa: E402
                        make_varlen, varlen_lengths, workload)
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
     PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_bwd_flops,
-    attention_fwd_bytes, attention_fwd_flops)
+    attention_fwd_bytes, attention_fwd_flops, attention_window_flops)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
-             "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None}
+             "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None,
+             "gqa_prefill_window": 3}
+# sliding-window workloads: (left, right) bounds, run through fa_fwd_window
+WINDOWS = {"gqa_prefill_window": (4096, -1)}
 # HBM bytes per launch of each workload's dominant kernel, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch; summaries under profiles/).  Each counter is scaled by what it
@@ -110,7 +115,7 @@ def _blas_threads():
         return os.cpu_count()
 
 
-def cpu_baseline(w, q, k, v, budget_s=10.0, do=None):
+def cpu_baseline(w, q, k, v, budget_s=10.0, do=None, window=None):
     """Oracle TFLOP/s on whole heads of batch 0, one head at a time (the
     gradient oracle when ``do`` is given)."""
     from fa_inputs import bf16_bits_to_f64
@@ -126,7 +131,8 @@ def cpu_baseline(w, q, k, v, budget_s=10.0, do=None):
         vh = bf16_bits_to_f64(v[:1, h // G:h // G + 1])
         t0 = time.perf_counter()
         if do is None:
-            reference_attention(qh, kh, vh, causal=w.causal, scale=scale)
+            reference_attention(qh, kh, vh, causal=w.causal, scale=scale,
+                                window=window)
         else:
             reference_attention_backward(
                 qh, kh, vh, bf16_bits_to_f64(do[:1, h:h + 1]),
@@ -135,6 +141,9 @@ def cpu_baseline(w, q, k, v, budget_s=10.0, do=None):
         done += 1
     count = attention_fwd_flops if do is None else attention_bwd_flops
     flops = count(1, done, w.Nq, w.Nk, w.d, w.causal)
+    if window is not None:
+        flops = attention_window_flops(1, done, w.Nq, w.Nk, w.d, w.causal,
+                                       window)
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
@@ -301,6 +310,7 @@ def main(argv=None):
         return bench_varlen(args)
     w = workload(WORKLOADS[args.workload])
     backward = args.workload.endswith("_bwd")
+    window = WINDOWS.get(args.workload)
     q, k, v = make_inputs(w, seed=0)
     Q, K, V = _dev_tensor(q), _dev_tensor(k), _dev_tensor(v)
     o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
@@ -333,6 +343,12 @@ def main(argv=None):
         def step():
             ops.fa_bwd(Q, K, V, o, lse, DO, causal=w.causal, scale=w.scale,
                        dq=dq, dk=dk, dv=dv, workspace=ws)
+    elif window is not None:
+        splits = 0
+
+        def step():
+            ops.fa_fwd_window(Q, K, V, window, causal=w.causal, scale=w.scale,
+                              o=o, lse=lse)
     else:
         splits = 0
 
@@ -345,8 +361,12 @@ def main(argv=None):
 
     count = attention_bwd_flops if backward else attention_fwd_flops
     flops = count(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    if window is not None:
+        flops = attention_window_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal,
+                                       window)
     nbytes = attention_fwd_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
-    traffic = measured_traffic(args.workload if backward else w.name)
+    traffic = measured_traffic(args.workload if (backward or window)
+                               else w.name)
     if w.Nq == 1:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit, metric = "GB/s", f"attn decode HBM GB/s ({w.name})"
@@ -358,6 +378,9 @@ def main(argv=None):
         value = flops / (ms_per_step * 1e-3) / 1e12
         if backward:
             metric = f"attn bwd TFLOP/s ({w.name})"
+        elif window is not None:
+            metric = (f"attn fwd TFLOP/s ({w.name}, window {window[0]},"
+                      f"{window[1]})")
         elif w.name == workload(3).name:
             metric = METRIC
         else:
@@ -382,12 +405,14 @@ def main(argv=None):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) fp32 rounded to bf16)",
-        "config": {"workload": w.name + ("_backward" if backward else ""),
+        "config": {"workload": w.name + ("_backward" if backward else "") +
+                   (f"_window{window[0]}" if window is not None else ""),
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
                    "scale": w.scale,
                    ("grad_dtype" if backward else "out_dtype"): "bf16",
                    "kv_splits": splits,
+                   "window": list(window) if window is not None else None,
                    "kernel_ms": round(kern_ms, 4),
                    "pct_bf16_mfma_peak": round(100 * flops / (kern_ms * 1e-3)
                                                / 1e12 / PEAK_BF16_MFMA_TFLOPS, 2)},
@@ -396,7 +421,8 @@ def main(argv=None):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v,
-                                           do=do if backward else None)
+                                           do=do if backward else None,
+                                           window=window)
         if w.Nq == 1:
             cb = out["cpu_baseline"]
             cb["note"] = "oracle TFLOP/s (decode bytes are not a CPU metric)"

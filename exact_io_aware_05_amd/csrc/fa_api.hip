@@ -163,6 +163,39 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   return hip_status(e2);
 }
 
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                  int causal, int window_left, int window_right, float scale,
+                  int out_dtype, hipStream_t stream) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  // A bound that no query reaches past hides nothing: left >= Nk - 1 or
+  // right >= Nq - 1 (every key then lies on the visible side of every
+  // row's bound).  Without a left bound the mask is causal (right bound 0
+  // or the causal flag) or none, which fa_fwd runs (KV split included).
+  const bool left_free = window_left < 0 || window_left >= Nk - 1;
+  const bool right_free = window_right < 0 || window_right >= Nq - 1;
+  if (left_free && (causal || window_right == 0))
+    return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, 1, scale, out_dtype,
+                  stream);
+  if (left_free && right_free)
+    return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, 0, scale, out_dtype,
+                  stream);
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
+  return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
+                                       fa::dense_layout(s),
+                                       out_dtype == FA_OUT_F32, stream));
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k,

@@ -11,6 +11,9 @@ struct Shape {
   int B, Hq, Hkv, Nq, Nk, d;
   int causal;
   float scale;
+  // sliding window around each query's place c = i + Nk - Nq on the key
+  // axis: keys c - win_left .. c + win_right; -1 is no bound on that side
+  int win_left = -1, win_right = -1;
 };
 
 // Where the rows of one (sequence, head) live, in elements: batch, head and

@@ -225,7 +225,8 @@ __device__ __forceinline__ void matrix_phase(const char* kp,
 
 // Softmax phase of one wave for block j: optional mask (`lim`: last
 // visible key relative to this lane's first key of the block; register r of
-// half 0 holds relative key 16(r/8) + r%8, half 1 adds 32), weights
+// half 0 holds relative key 16(r/8) + r%8, half 1 adds 32; with a band,
+// also `lo`: the first visible key, same reference), weights
 // p = 2^(s c2 - m) against the reference max m, rounded to bf16 once into
 // pk, and the row sums.  When the weights would grow past 2^64 (or a row
 // has no reference yet) the block is redone with m moved to the row max;
@@ -234,18 +235,19 @@ __device__ __forceinline__ void matrix_phase(const char* kp,
 // The rounded weights feed P V and their own row sum lb, so O = acc / lb
 // is an exact convex combination of V rows up to fp32 summation; the fp32
 // sum l of the unrounded weights gives lse.
-template <bool MASK>
+template <bool MASK, bool LOWER = false>
 __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
                                               const f32x16& s1, int lim,
-                                              float c2, RowState& st,
+                                              int lo, float c2, RowState& st,
                                               float& alpha, u32x4* pk) {
   // The mask never overwrites the score registers (that would make the
   // masked and unmasked variants rejoin with copies): hidden keys are left
   // out of the max and get weight 0 after the exponential.
-  auto hide0 = [&](int r) { return MASK && 16 * (r >> 3) + (r & 7) > lim; };
-  auto hide1 = [&](int r) {
-    return MASK && 16 * (r >> 3) + (r & 7) + 32 > lim;
+  auto hidden = [&](int key) {
+    return MASK && (key > lim || (LOWER && key < lo));
   };
+  auto hide0 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7)); };
+  auto hide1 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7) + 32); };
   // weights p = 2^(s c2 - msub) (0 for hidden keys), rounded to bf16 once
   // into pk; partial sums of the fp32 and of the rounded weights
   auto weights = [&](float msub, float* rs, float* rb) {
@@ -319,12 +321,18 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
   return true;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+// Mask modes: kNone, kCausal (key j visible to row i iff j <= i + Nk - Nq),
+// kBand (iff i + Nk - Nq - wl <= j <= i + Nk - Nq + wr, wl and wr >= 0).
+constexpr int kNone = 0, kCausal = 1, kBand = 2;
+
+template <int D, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, void* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int Nq_max, int Nk_max,
-    float c2, int n_qblk, int n_items, SeqLayout lay) {
+    float c2, int n_qblk, int n_items, SeqLayout lay, int wl, int wr) {
+  constexpr bool CAUSAL = MODE == kCausal;
+  constexpr bool BAND = MODE == kBand;
   using L = Layout<D>;
   constexpr int NTILE = L::NTILE;
   constexpr int NSTEP = L::NSTEP;
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     jq = t1 % n_qblk;
     bh = t1 / n_qblk;
   }
-  const int qblk = CAUSAL ? (n_qblk - 1 - jq) : jq;
+  const int qblk = MODE != kNone ? (n_qblk - 1 - jq) : jq;
   const int b = bh / Hkv, hkv = bh % Hkv;
   const int hq = hkv * G + g;
   const int q0 = qblk * BR;
@@ -397,6 +405,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, q0 + BR + off);
+  // band: keys from the first row's lower bound to the last row's upper one
+  int j0 = 0;
+  if (BAND) {
+    kv_end = min(Nk, min(q0 + BR, Nq) + off + wr);
+    j0 = max(0, q0 + off - wl) / BC;
+  }
   const int nblk = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
 
   // this wave's rows: blocks from w_mask on may hide keys from one of them
@@ -404,6 +418,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   const int wrow0 = q0 + wave * 32;
   int w_mask = Nk / BC;
   if (CAUSAL) w_mask = min(w_mask, max(0, wrow0 + off + 1) / BC);
+  // band: also blocks before w_lo may hide keys (below the lower bound of
+  // the wave's last row)
+  int w_lo = 0;
+  if (BAND) {
+    w_mask = min(w_mask, max(0, wrow0 + off + wr + 1) / BC);
+    w_lo = (max(0, wrow0 + 31 + off - wl) + BC - 1) / BC;
+  }
 
   // ---- per-lane DMA source offsets.  K: instruction i copies 16-byte
   // chunk i of all 64 rows (lane = LDS row, holding key key_slot(lane)).
@@ -452,7 +473,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     }
   }
   // this lane's row limit relative to its first key of block 0
-  const int lim0 = (CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1) - 8 * h;
+  const int lim0 = (CAUSAL ? min(Nk - 1, qrow + off)
+                    : BAND ? min(Nk - 1, qrow + off + wr)
+                           : Nk - 1) - 8 * h;
+  const int lo0 = BAND ? qrow + off - wl - 8 * h : 0;
 
   f32x16 s0, s1;    // scores of the block in flight
   u32x4 pk[4];      // bf16 weights of the previous block
@@ -493,20 +517,22 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     copy_block<D>(smem + L::VBASE + ((j + 2) % L::NS) * L::VBYTES, vh,
                   kv_rows, j + 2, wave, v_off, v_step, rsb);
   };
-  // prologue: K_0, K_1, K_2, V_0, V_1 (all waves), fully waited.  V stage 3
-  // is zeroed: block 0's matrix phase multiplies it by the all-zero
+  // prologue: K_j0, K_j0+1, K_j0+2, V_j0, V_j0+1 (all waves), fully
+  // waited (j0 = 0 unless a band starts later).  The V stage before j0 is
+  // zeroed: block j0's matrix phase multiplies it by the all-zero
   // "previous" P, and 0 * (stale NaN/Inf bits) would not be 0.
 #pragma unroll
   for (int b0 = 0; b0 < 3; ++b0)
-    copy_block<D>(smem + b0 * L::KBYTES, kh, kv_rows, b0, wave, k_off, 16,
-                  rsb);
+    copy_block<D>(smem + ((j0 + b0) % L::NS) * L::KBYTES, kh, kv_rows,
+                  j0 + b0, wave, k_off, 16, rsb);
 #pragma unroll
   for (int b0 = 0; b0 < 2; ++b0)
-    copy_block<D>(smem + L::VBASE + b0 * L::VBYTES, vh, kv_rows, b0, wave,
-                  v_off, v_step, rsb);
+    copy_block<D>(smem + L::VBASE + ((j0 + b0) % L::NS) * L::VBYTES, vh,
+                  kv_rows, j0 + b0, wave, v_off, v_step, rsb);
 #pragma unroll
   for (int i = tid; i < L::VBYTES / 16; i += NT)
-    reinterpret_cast<u32x4*>(smem + L::VBASE + 3 * L::VBYTES)[i] =
+    reinterpret_cast<u32x4*>(smem + L::VBASE +
+                             ((j0 + L::NS - 1) % L::NS) * L::VBYTES)[i] =
         u32x4{0u, 0u, 0u, 0u};
   wait_vmcnt<0>();
   __syncthreads();
@@ -522,21 +548,23 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
   if (!group_a) __syncthreads();
-  for (int j = 0; j < nblk; ++j) {
+  for (int j = j0; j < nblk; ++j) {
     mphase(j, std::true_type{});
     __syncthreads();
     copies(j);
-    if (j >= w_mask)
-      rescale = softmax_phase<true>(s0, s1, lim0 - j * BC, c2, st, alpha, pk);
+    if (j >= w_mask || (BAND && j < w_lo))
+      rescale = softmax_phase<true, BAND>(s0, s1, lim0 - j * BC,
+                                          lo0 - j * BC, c2, st, alpha, pk);
     else
-      rescale = softmax_phase<false>(s0, s1, lim0 - j * BC, c2, st, alpha, pk);
+      rescale = softmax_phase<false>(s0, s1, lim0 - j * BC, 0, c2, st,
+                                     alpha, pk);
     if (group_a)
       wait_vmcnt<2 * OPS>();  // own copies of iteration j-2 have landed
     else
       wait_vmcnt<OPS>();      // own copies of iteration j-1 have landed
     __syncthreads();
   }
-  if (nblk > 0) mphase(nblk, std::false_type{});  // P V of the last block
+  if (nblk > j0) mphase(nblk, std::false_type{});  // P V of the last block
   __syncthreads();
   if (group_a) __syncthreads();
 
@@ -570,10 +598,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
-                  float* lse, const Shape& s, const SeqLayout& lay,
-                  hipStream_t stream) {
+                  float* lse, const Shape& s, const SeqLayout& lay, int wl,
+                  int wr, hipStream_t stream) {
   const int n_qblk = (s.Nq + BR - 1) / BR;
   long long n_items = (long long)s.B * s.Hq * n_qblk;
   // packed batch: whole rounds of 8 units of G heads (the tail's surplus
@@ -587,13 +615,47 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   // below 2^-24 in magnitude, so each weight is exactly 1, and -inf scores
   // stay -inf (no 0 * inf)
   const float c2 = fmaxf(s.scale * kLog2e, 1.17549435e-38f);
-  hipLaunchKernelGGL((prefill_kernel<D, CAUSAL, OUT_F32>),
+  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32>),
                      dim3((unsigned)n_items), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, lse, s.Hq, s.Hkv,
-                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay);
+                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr);
   return hipGetLastError();
+}
+
+template <int D, int MODE>
+hipError_t launch_mode(const void* q, const void* k, const void* v, void* o,
+                       float* lse, const Shape& s, const SeqLayout& lay,
+                       int wl, int wr, bool out_f32, hipStream_t stream) {
+  return out_f32 ? launch<D, MODE, true>(q, k, v, o, lse, s, lay, wl, wr,
+                                         stream)
+                 : launch<D, MODE, false>(q, k, v, o, lse, s, lay, wl, wr,
+                                          stream);
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
+                    float* lse, const Shape& s, const SeqLayout& lay,
+                    bool out_f32, hipStream_t stream) {
+  // The window bounds as the kernel takes them: a bound that no query
+  // reaches past (left >= Nk - 1, right >= Nq - 1: every key is then on
+  // that side of every row's bound) is no bound; the causal flag caps the
+  // right bound at 0.  Without a bound left the mask is causal or none.
+  const int big = s.Nq + s.Nk;
+  int wl = s.win_left < 0 ? big : (s.win_left < big ? s.win_left : big);
+  int wr = s.win_right < 0 ? big : (s.win_right < big ? s.win_right : big);
+  if (s.causal) wr = 0;
+  const bool left_free = wl >= s.Nk - 1;
+  const bool right_free = wr >= s.Nq - 1;
+  if (left_free && right_free)
+    return launch_mode<D, kNone>(q, k, v, o, lse, s, lay, 0, 0, out_f32,
+                                 stream);
+  if (left_free && wr == 0)
+    return launch_mode<D, kCausal>(q, k, v, o, lse, s, lay, 0, 0, out_f32,
+                                   stream);
+  return launch_mode<D, kBand>(q, k, v, o, lse, s, lay, wl, wr, out_f32,
+                               stream);
 }
 
 }  // namespace
@@ -602,20 +664,9 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s,
                           const SeqLayout& lay, bool out_f32,
                           hipStream_t stream) {
-  const bool c = s.causal != 0;
-#define FA_DISPATCH(D_)                                                      \
-  if (s.d == D_) {                                                           \
-    if (c)                                                                   \
-      return out_f32                                                         \
-                 ? launch<D_, true, true>(q, k, v, o, lse, s, lay, stream)   \
-                 : launch<D_, true, false>(q, k, v, o, lse, s, lay, stream); \
-    return out_f32                                                           \
-               ? launch<D_, false, true>(q, k, v, o, lse, s, lay, stream)    \
-               : launch<D_, false, false>(q, k, v, o, lse, s, lay, stream);  \
-  }
-  FA_DISPATCH(128)
-  FA_DISPATCH(64)
-#undef FA_DISPATCH
+  if (s.d == 128)
+    return launch_d<128>(q, k, v, o, lse, s, lay, out_f32, stream);
+  if (s.d == 64) return launch_d<64>(q, k, v, o, lse, s, lay, out_f32, stream);
   return hipErrorInvalidValue;
 }
 

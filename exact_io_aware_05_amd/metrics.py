@@ -20,6 +20,27 @@ def attention_fwd_flops(B, Hq, Nq, Nk, d, causal) -> float:
     return f / 2.0 if causal else f
 
 
+def visible_pairs(Nq, Nk, causal, window=None) -> int:
+    """Exact number of visible (query row, key) pairs of one head: row i,
+    placed at c = i + Nk - Nq, sees keys max(0, c - left) .. min(Nk - 1,
+    c + right) (right capped at 0 when causal; -1 is no bound)."""
+    import numpy as np
+    left, right = (-1, -1) if window is None else window
+    c = np.arange(Nq, dtype=np.int64) + (Nk - Nq)
+    lo = np.zeros(Nq, dtype=np.int64) if left < 0 else np.maximum(0, c - left)
+    hi = np.full(Nq, Nk - 1, dtype=np.int64) if right < 0 else \
+        np.minimum(Nk - 1, c + right)
+    if causal:
+        hi = np.minimum(hi, c)
+    return int(np.maximum(hi - lo + 1, 0).sum())
+
+
+def attention_window_flops(B, Hq, Nq, Nk, d, causal, window) -> float:
+    """Forward FLOPs of a windowed mask: 4 d per visible pair (the two
+    products), counted exactly."""
+    return 4.0 * B * Hq * d * visible_pairs(Nq, Nk, causal, window)
+
+
 def attention_bwd_flops(B, Hq, Nq, Nk, d, causal) -> float:
     """Backward FLOPs: the five N x N x d products of the recomputation
     form (scores, dP = dO V^T, dV = P^T dO, dQ = dS K, dK = dS^T Q), i.e.

@@ -19,7 +19,7 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
-           "fa_fwd_varlen"]
+           "fa_fwd_varlen", "fa_fwd_window"]
 
 
 def _dims(q, k, v):
@@ -71,6 +71,23 @@ def fa_fwd(q, k, v, causal=False, scale=None, out_dtype=torch.bfloat16,
                        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16,
                        _stream(q))
     check(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_window(q, k, v, window, causal=False, scale=None,
+                  out_dtype=torch.bfloat16, o=None, lse=None):
+    """Sliding-window forward through ``fa_fwd_window``; ``window`` is
+    ``(left, right)`` keys around each query's place on the key axis, -1
+    for no bound on a side.  Returns ``(o, lse)``."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    left, right = (int(x) for x in window)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    st = load().fa_fwd_window(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), left, right, scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
+    check(st, "fa_fwd_window")
     return o, lse
 
 

@@ -126,6 +126,27 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /*
+ * Forward with a sliding-window mask (the training-cost guide,
+ * tool.smithlab.co.kr, FAQ: sliding windows are among the mask features of
+ * the fused kernels).  Query i, placed at c = i + Nk - Nq on the key axis
+ * (the bottom-right alignment of the causal mask), sees key j only if
+ *     c - window_left <= j <= c + window_right,
+ * and, with `causal` set, j <= c as well.  A bound of -1 is no bound on
+ * that side: (-1, -1) is fa_fwd without a mask, (-1, 0) or the causal flag
+ * alone is fa_fwd causal, and those cases (and windows that hide nothing,
+ * left >= Nk - 1 and right >= Nq - 1) are run by fa_fwd itself, KV split
+ * included.  Otherwise the tiled prefill kernel runs with the band: K/V
+ * blocks outside every row's window of a 256-row block are never read.
+ * Rows whose window holds no key get O = 0 and lse = -inf.  Layouts,
+ * types, alignment, asynchrony and status codes as for fa_fwd;
+ * FA_ERR_INVALID_ARG also for a bound below -1.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
+                  float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                  int causal, int window_left, int window_right, float scale,
+                  int out_dtype, hipStream_t stream);
+
+/*
  * Forward over a packed batch of variable-length sequences (prefill form).
  * Sequence b has the query rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1
  * and the key/value rows cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of the

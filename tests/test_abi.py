@@ -214,3 +214,27 @@ def test_no_hip_error_recorded_by_validation(lib):
     _split(lib, S=0)
     _bwd(lib, ws=None)
     assert lib.fa_last_hip_error() == 0
+
+
+def _win(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=64,
+             causal=0, wl=4, wr=0, scale=0.125, out=0)
+    a.update(kw)
+    return lib.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"],
+                             a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                             a["causal"], a["wl"], a["wr"], a["scale"],
+                             a["out"], None)
+
+
+@pytest.mark.parametrize("kw", INVALID + [dict(wl=-2), dict(wr=-2),
+                                          dict(wl=-5, wr=3)],
+                         ids=lambda k: str(k))
+def test_window_invalid_arguments(lib, kw):
+    assert _win(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_window_unsupported(lib):
+    assert _win(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _win(lib, d=96, wl=-1, wr=-1) == _lib.FA_ERR_UNSUPPORTED
+    assert _win(lib, Nk=(1 << 23) + 1, d=128) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0

@@ -1,0 +1,105 @@
+"""Sliding-window forward (fa_fwd_window) against the float64 oracle with
+the same window: ragged shapes element by element, the windowed GQA
+prefill at full size on sampled rows, and windows that hide nothing
+against fa_fwd bit for bit."""
+import numpy as np
+import pytest
+
+from fa_inputs import make_inputs, make_qkv, workload
+from oracle import reference_attention
+from tests.gpu_util import compare, dev, f64, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _ops():
+    from exact_io_aware_05_amd import ops
+    return ops
+
+
+def _both(Q, K, V, window, causal, scale):
+    """fp32 and bf16 outputs of one window call; the bf16 one must be the
+    round-to-nearest-even of the fp32 one, with the same lse."""
+    o32, l32 = _ops().fa_fwd_window(Q, K, V, window, causal=causal,
+                                    scale=scale, out_dtype=torch.float32)
+    o16, l16 = _ops().fa_fwd_window(Q, K, V, window, causal=causal,
+                                    scale=scale, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o32.to(torch.bfloat16), o16), "bf16 O != RNE(fp32 O)"
+    assert torch.equal(l32, l16)
+    return o32, l32
+
+
+# B, Hq, Hkv, Nq, Nk, d, causal, (left, right)
+CASES = [
+    (1, 4, 2, 700, 700, 128, False, (100, 0)),     # sliding causal window
+    (1, 4, 4, 600, 600, 64, True, (257, -1)),      # causal flag + left bound
+    (2, 2, 1, 300, 900, 128, False, (50, 20)),     # two-sided, Nq < Nk
+    (1, 2, 2, 900, 300, 128, True, (64, -1)),      # Nq > Nk: empty rows
+    (1, 2, 1, 513, 513, 64, False, (0, 0)),        # one key per row
+    (1, 2, 2, 1000, 1000, 128, False, (-1, 70)),   # right bound only
+    (1, 2, 2, 1000, 1000, 128, False, (63, 64)),   # block-sized bounds
+    (2, 8, 2, 1, 5000, 128, False, (1000, -1)),    # decode row, last 1001
+    (1, 2, 1, 77, 4000, 64, True, (3000, 5)),      # chunk of a long cache
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "x".join(
+    map(str, c[:6])) + f"-{'causal' if c[6] else 'full'}-w{c[7][0]},{c[7][1]}")
+def test_window_matches_oracle(case):
+    B, Hq, Hkv, Nq, Nk, d, causal, window = case
+    q, k, v = make_qkv(B, Hq, Hkv, Nq, Nk, d, seed=31)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    o, lse = _both(dev(q), dev(k), dev(v), window, causal, scale)
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=causal,
+                                       scale=scale, window=window)
+    compare(host(o), host(lse), O_ref, L_ref, what=f"window {window}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_windows_that_hide_nothing_match_fa_fwd(causal):
+    """(-1, -1), bounds past every key and (-1, 0) run fa_fwd itself."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 333, 128
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, d, seed=32)
+    Q, K, V = dev(q), dev(k), dev(v)
+    ops = _ops()
+    ref_o, ref_l = ops.fa_fwd(Q, K, V, causal=causal, out_dtype=torch.float32)
+    for w in ((-1, -1), (N, N), (N - 1, N - 1)):
+        o, l = ops.fa_fwd_window(Q, K, V, w, causal=causal,
+                                 out_dtype=torch.float32)
+        assert torch.equal(o, ref_o) and torch.equal(l, ref_l), w
+    c_o, c_l = ops.fa_fwd(Q, K, V, causal=True, out_dtype=torch.float32)
+    o, l = ops.fa_fwd_window(Q, K, V, (-1, 0), causal=False,
+                             out_dtype=torch.float32)
+    assert torch.equal(o, c_o) and torch.equal(l, c_l)
+
+
+def test_window_gqa_prefill_full_size_sampled_rows():
+    """The GQA prefill workload (B1 Hq32 Hkv8 N8192 d128, causal) with a
+    4096-key window, in the benchmark's launch configuration, checked on
+    sampled rows of every head that the oracle computes one by one."""
+    w = workload(3)
+    q, k, v = make_inputs(w, seed=0)
+    o, lse = _both(dev(q), dev(k), dev(v), (4096, -1), True, w.scale)
+    O, L = host(o), host(lse)
+    del o, lse
+    rng = np.random.default_rng(33)
+    rows = np.unique(np.concatenate([
+        [0, 1, 255, 256, 4095, 4096, 4097, 4159, 4160, 8190, 8191],
+        rng.choice(w.Nq, size=40, replace=False)]))
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=True,
+                                       scale=float(np.float32(w.scale)),
+                                       rows=rows, window=(4096, -1))
+    compare(O[:, :, rows], L[:, :, rows], O_ref, L_ref,
+            what="gqa prefill, window 4096")
+
+
+def test_window_deterministic():
+    q, k, v = make_qkv(1, 4, 2, 777, 777, 128, seed=34)
+    Q, K, V = dev(q), dev(k), dev(v)
+    a = _ops().fa_fwd_window(Q, K, V, (200, 10), out_dtype=torch.float32)
+    b = _ops().fa_fwd_window(Q, K, V, (200, 10), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -64,3 +64,27 @@ def test_algorithmic_bytes_gqa_prefill():
     # Q 64 MiB + K, V 16 MiB each + O 64 MiB + lse 1 MiB
     b = attention_fwd_bytes(1, 32, 8, 8192, 8192, 128)
     assert b == (64 + 16 + 16 + 64 + 1) * 2 ** 20
+
+
+def test_visible_pairs_counts():
+    from exact_io_aware_05_amd.metrics import visible_pairs
+    import numpy as np
+    assert visible_pairs(5, 5, False) == 25
+    assert visible_pairs(5, 5, True) == 15
+    assert visible_pairs(3, 5, True) == 3 + 4 + 5
+    assert visible_pairs(5, 3, True) == 0 + 0 + 1 + 2 + 3
+    assert visible_pairs(8192, 8192, True, (4096, -1)) == \
+        4096 * 4097 // 2 + 4096 * 4097
+    # brute force against explicit sets
+    for Nq, Nk in ((4, 7), (7, 4), (6, 6)):
+        for w in ((-1, -1), (0, 0), (2, 1), (-1, 2), (3, -1)):
+            for causal in (False, True):
+                n = 0
+                for i in range(Nq):
+                    c = i + Nk - Nq
+                    for j in range(Nk):
+                        ok = (w[0] < 0 or j >= c - w[0]) and \
+                            (w[1] < 0 or j <= c + w[1]) and \
+                            (not causal or j <= c)
+                        n += ok
+                assert visible_pairs(Nq, Nk, causal, w) == n, (Nq, Nk, w)

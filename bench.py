@@ -20,7 +20,9 @@ kernel, dQ kernel) per step, from the O and lse of one untimed forward,
 priced at 2.5 times the forward FLOPs; its roofline covers the whole call.
 ``--workload gqa_prefill_window`` runs ``fa_fwd_window`` on the GQA prefill
 with a 4096-key sliding window (causal), priced at 4 d FLOPs per visible
-pair, counted exactly.  ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
+pair, counted exactly.  ``--workload decode_window`` runs the decode workload through
+``fa_fwd_window`` with a 4096-key window (KV split over the window's keys),
+priced at the bytes of the keys it must read.  ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
 causal prompts (seeded log-uniform lengths in [256, 8192], 32768 tokens,
 the GQA heads above), priced at the causal FLOPs of each sequence.
 
@@ -46,14 +48,15 @@ from fa_inputs import (VARLEN_PREFILL, make_dout, make_inputs,  # noqa: E402
                        make_varlen, varlen_lengths, workload)
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
     PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_bwd_flops,
-    attention_fwd_bytes, attention_fwd_flops, attention_window_flops)
+    attention_fwd_bytes, attention_fwd_flops, attention_window_flops,
+    visible_keys)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None,
-             "gqa_prefill_window": 3}
+             "gqa_prefill_window": 3, "decode_window": 4}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
-WINDOWS = {"gqa_prefill_window": (4096, -1)}
+WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1)}
 # HBM bytes per launch of each workload's dominant kernel, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch; summaries under profiles/).  Each counter is scaled by what it
@@ -317,7 +320,15 @@ def main(argv=None):
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    if w.Nq == 1:
+    if window is not None:
+        # fa_fwd_window picks the form itself (KV split for a single query,
+        # its workspace from the stream-ordered pool)
+        splits = 0
+
+        def step():
+            ops.fa_fwd_window(Q, K, V, window, causal=w.causal, scale=w.scale,
+                              o=o, lse=lse)
+    elif w.Nq == 1:
         # single-query decode: the KV-split path with a workspace allocated
         # once, as a serving loop would hold it
         splits = args.splits or ops.default_num_splits(w.B, w.Hq, w.Hkv, w.Nq,
@@ -343,12 +354,6 @@ def main(argv=None):
         def step():
             ops.fa_bwd(Q, K, V, o, lse, DO, causal=w.causal, scale=w.scale,
                        dq=dq, dk=dk, dv=dv, workspace=ws)
-    elif window is not None:
-        splits = 0
-
-        def step():
-            ops.fa_fwd_window(Q, K, V, window, causal=w.causal, scale=w.scale,
-                              o=o, lse=lse)
     else:
         splits = 0
 
@@ -365,11 +370,18 @@ def main(argv=None):
         flops = attention_window_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal,
                                        window)
     nbytes = attention_fwd_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
+    if window is not None:   # only the keys some row sees must be read
+        nbytes = attention_fwd_bytes(
+            w.B, w.Hq, w.Hkv, w.Nq,
+            visible_keys(w.Nq, w.Nk, w.causal, window), w.d)
     traffic = measured_traffic(args.workload if (backward or window)
                                else w.name)
     if w.Nq == 1:
         value = nbytes / (ms_per_step * 1e-3) / 1e9
         unit, metric = "GB/s", f"attn decode HBM GB/s ({w.name})"
+        if window is not None:
+            metric = (f"attn decode HBM GB/s ({w.name}, window {window[0]},"
+                      f"{window[1]})")
         achieved = nbytes / (kern_ms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -411,7 +423,7 @@ def main(argv=None):
                    "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
                    "scale": w.scale,
                    ("grad_dtype" if backward else "out_dtype"): "bf16",
-                   "kv_splits": splits,
+                   "kv_splits": splits if window is None else None,
                    "window": list(window) if window is not None else None,
                    "kernel_ms": round(kern_ms, 4),
                    "pct_bf16_mfma_peak": round(100 * flops / (kern_ms * 1e-3)

@@ -79,6 +79,25 @@ int default_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   return (int)s;
 }
 
+// The prefill kernel (splits == 0) or the KV-split form with a workspace
+// taken from the stream-ordered pool for this call.
+int run_forward(const void* q, const void* k, const void* v, void* o,
+                float* lse, const fa::Shape& s, int splits, bool f32,
+                hipStream_t stream) {
+  if (splits == 0)
+    return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
+                                         fa::dense_layout(s), f32, stream));
+  const size_t bytes =
+      fa::splitkv_workspace_bytes((long long)s.B * s.Hq * s.Nq, s.d, splits);
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
+  hipError_t e2 = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(e2);
+}
+
 }  // namespace
 
 extern "C" {
@@ -148,19 +167,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   st = check_device();
   if (st != FA_OK) return st;
   const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
-  const bool f32 = out_dtype == FA_OUT_F32;
-  if (splits == 0)
-    return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
-                                         fa::dense_layout(s), f32, stream));
-  const size_t bytes =
-      fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, splits);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, stream);
-  if (e != hipSuccess) return hip_status(e);
-  e = fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
-  hipError_t e2 = hipFreeAsync(ws, stream);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(e2);
+  return run_forward(q, k, v, o, lse, s, splits, out_dtype == FA_OUT_F32,
+                     stream);
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
@@ -171,29 +179,29 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
                         out_dtype);
   if (st != FA_OK) return st;
-  // A bound that no query reaches past hides nothing: left >= Nk - 1 or
-  // right >= Nq - 1 (every key then lies on the visible side of every
-  // row's bound).  Without a left bound the mask is causal (right bound 0
-  // or the causal flag) or none, which fa_fwd runs (KV split included).
-  const bool left_free = window_left < 0 || window_left >= Nk - 1;
-  const bool right_free = window_right < 0 || window_right >= Nq - 1;
-  if (left_free && (causal || window_right == 0))
-    return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, 1, scale, out_dtype,
-                  stream);
-  if (left_free && right_free)
-    return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, 0, scale, out_dtype,
-                  stream);
-  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
-  if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
-  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
-  st = check_device();
-  if (st != FA_OK) return st;
   fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
   s.win_left = window_left;
   s.win_right = window_right;
-  return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
-                                       fa::dense_layout(s),
-                                       out_dtype == FA_OUT_F32, stream));
+  // A bound that no query reaches past hides nothing (left >= Nk - 1,
+  // right >= Nq - 1); what is left is no mask, the causal mask or a band.
+  const fa::MaskBounds mb = fa::mask_bounds(s);
+  if (mb.kind != 2)
+    return fa_fwd(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, mb.kind, scale,
+                  out_dtype, stream);
+  // the KV-split form when few query rows share a KV head, its chunks cut
+  // from the keys a row tile's band can span
+  const long long span =
+      (long long)fa::band_tile_blocks(s, mb, fa::kSplitKeys) * fa::kSplitKeys;
+  const int splits =
+      default_splits(B, Hq, Hkv, Nq, (int)(span < Nk ? span : Nk));
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  return run_forward(q, k, v, o, lse, s, splits, out_dtype == FA_OUT_F32,
+                     stream);
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,

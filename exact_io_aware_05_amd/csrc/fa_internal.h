@@ -16,6 +16,42 @@ struct Shape {
   int win_left = -1, win_right = -1;
 };
 
+// The mask of a Shape as the kernels take it: kind 0 none, 1 causal, 2 a
+// band of keys c - wl .. c + wr around each row's place c = i + Nk - Nq.
+// A bound that no row reaches past (wl >= Nk - 1, wr >= Nq - 1: every key
+// lies on its visible side for every row) is no bound; the causal flag
+// caps wr at 0; without a left bound the mask is causal (wr 0) or none.
+// A band's bounds are returned capped at those values (Nk - 1, Nq - 1),
+// which hides the same keys and keeps the key span of a row tile tight.
+struct MaskBounds {
+  int kind, wl, wr;
+};
+inline MaskBounds mask_bounds(const Shape& s) {
+  const int big = s.Nq + s.Nk;
+  int wl = s.win_left < 0 ? big : (s.win_left < big ? s.win_left : big);
+  int wr = s.win_right < 0 ? big : (s.win_right < big ? s.win_right : big);
+  if (s.causal) wr = 0;
+  const bool left_free = wl >= s.Nk - 1;
+  const bool right_free = wr >= s.Nq - 1;
+  if (left_free && right_free) return {0, 0, 0};
+  if (left_free && wr == 0) return {1, 0, 0};
+  return {2, left_free ? s.Nk - 1 : wl, right_free ? s.Nq - 1 : wr};
+}
+
+// Blocks of `kb` keys that the band of one 32-row tile of the KV-split
+// form can span, for sizing its chunks.  The tile's packed rows (G query
+// heads per query) cover queries a / G .. (a + 31) / G, at most 31 / G + 2
+// of them, so it sees at most 31 / G + 1 + wl + wr + 1 consecutive keys,
+// which span at most span / kb + 2 blocks.
+inline int band_tile_blocks(const Shape& s, const MaskBounds& m, int kb) {
+  const int G = s.Hq / s.Hkv;
+  const int nblk = (s.Nk + kb - 1) / kb;
+  if (m.kind != 2) return nblk;
+  const long long span = 31 / G + 2 + (long long)m.wl + m.wr;
+  const long long blocks = (span < s.Nk ? span : s.Nk) / kb + 2;
+  return blocks < nblk ? (int)blocks : nblk;
+}
+
 // Where the rows of one (sequence, head) live, in elements: batch, head and
 // row strides of Q and O (same shape), of K and V, and of lse.  Fixed-length
 // batches have cu_q = cu_k = nullptr.  Packed variable-length batches take

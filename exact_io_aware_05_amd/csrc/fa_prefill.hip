@@ -638,23 +638,14 @@ template <int D>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
                     float* lse, const Shape& s, const SeqLayout& lay,
                     bool out_f32, hipStream_t stream) {
-  // The window bounds as the kernel takes them: a bound that no query
-  // reaches past (left >= Nk - 1, right >= Nq - 1: every key is then on
-  // that side of every row's bound) is no bound; the causal flag caps the
-  // right bound at 0.  Without a bound left the mask is causal or none.
-  const int big = s.Nq + s.Nk;
-  int wl = s.win_left < 0 ? big : (s.win_left < big ? s.win_left : big);
-  int wr = s.win_right < 0 ? big : (s.win_right < big ? s.win_right : big);
-  if (s.causal) wr = 0;
-  const bool left_free = wl >= s.Nk - 1;
-  const bool right_free = wr >= s.Nq - 1;
-  if (left_free && right_free)
+  const MaskBounds m = mask_bounds(s);
+  if (m.kind == 0)
     return launch_mode<D, kNone>(q, k, v, o, lse, s, lay, 0, 0, out_f32,
                                  stream);
-  if (left_free && wr == 0)
+  if (m.kind == 1)
     return launch_mode<D, kCausal>(q, k, v, o, lse, s, lay, 0, 0, out_f32,
                                    stream);
-  return launch_mode<D, kBand>(q, k, v, o, lse, s, lay, wl, wr, out_f32,
+  return launch_mode<D, kBand>(q, k, v, o, lse, s, lay, m.wl, m.wr, out_f32,
                                stream);
 }
 

@@ -137,12 +137,21 @@ struct KvRegs {
   }
 };
 
-template <int D, bool CAUSAL>
+// Mask kinds: none, causal (key j visible to query i iff j <= i + Nk - Nq),
+// band (iff i + Nk - Nq - wl <= j <= i + Nk - Nq + wr).  With a band the
+// chunks of a row tile cut the blocks from its first row's lower bound on,
+// not from key 0.
+constexpr int kNone = 0, kCausal = 1, kBand = 2;
+
+template <int D, int MODE>
 __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_o,
     f32x4* __restrict__ ws_ml, int Hq, int Hkv, int Nq, int Nk, float c2,
-    int n_rowtiles, int num_splits, int blocks_per_split, int n_items) {
+    int n_rowtiles, int num_splits, int blocks_per_split, int n_items, int wl,
+    int wr) {
+  constexpr bool CAUSAL = MODE == kCausal;
+  constexpr bool BAND = MODE == kBand;
   constexpr int NSTEP = D / 16;
   constexpr int CPL = D / 32;
   const int lane = threadIdx.x & 63;
@@ -181,17 +190,28 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   const uint16_t* kh = k + (int64_t)bh * Nk * D;
   const uint16_t* vh = v + (int64_t)bh * Nk * D;
   const int nblk_all = (Nk + KB - 1) / KB;
-  const int blk0 = sp * blocks_per_split;
+  // queries of the first and last packed rows of this tile
+  const int first_q = (rt * 32) / G;
+  const int last_q = min(R - 1, rt * 32 + 31) / G;
+  const int blk_base = BAND ? max(0, first_q + off - wl) / KB : 0;
+  const int blk0 = blk_base + sp * blocks_per_split;
   int blk1 = min(blk0 + blocks_per_split, nblk_all);
-  if (CAUSAL) {
+  if (CAUSAL || BAND) {
     // last key visible to the last packed row of this tile
-    const int last_q = min(R - 1, rt * 32 + 31) / G;
-    const int kv_end = min(Nk, last_q + off + 1);
+    const int kv_end = min(Nk, last_q + off + (BAND ? wr : 0) + 1);
     blk1 = min(blk1, kv_end > 0 ? (kv_end + KB - 1) / KB : 0);
   }
-  const int lim = CAUSAL ? min(Nk - 1, iq + off) : Nk - 1;
+  const int lim = CAUSAL ? min(Nk - 1, iq + off)
+                  : BAND ? min(Nk - 1, iq + off + wr)
+                         : Nk - 1;
   // smallest per-row limit in this row tile (its first packed row)
-  const int lim_first = CAUSAL ? min(Nk - 1, (rt * 32) / G + off) : Nk - 1;
+  const int lim_first = CAUSAL ? min(Nk - 1, first_q + off)
+                        : BAND ? min(Nk - 1, first_q + off + wr)
+                               : Nk - 1;
+  // band: this row's first visible key, and the largest such bound in the
+  // tile (its last packed row)
+  const int lo = BAND ? iq + off - wl : 0;
+  const int lo_last = BAND ? last_q + off - wl : 0;
 
   f32x16 acc[CPL];
 #pragma unroll
@@ -236,14 +256,14 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     for (int t = 0; t < NSTEP; ++t)
       s = mfma32x32x16(KV::kop(kslot, krow, h, t), qf[t], s);
 
-    const bool need_mask = kb + KB - 1 > lim_first;
+    const bool need_mask = kb + KB - 1 > lim_first || (BAND && kb < lo_last);
     uint32_t vis = 0xffffu;
     if (need_mask) {
       vis = 0;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = kb + 16 * (r >> 3) + 8 * h + (r & 7);
-        if (key <= lim) vis |= 1u << r;
+        if (key <= lim && (!BAND || key >= lo)) vis |= 1u << r;
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -368,34 +388,52 @@ __global__ __launch_bounds__(NT) void splitkv_merge_kernel(
     lse[row] = L > 0.f ? (Mu + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
                   float* lse, const Shape& s, int num_splits, void* ws,
-                  hipStream_t stream) {
+                  const MaskBounds& mb, hipStream_t stream) {
   const int G = s.Hq / s.Hkv;
   const long long R = (long long)s.Nq * G;
   const int n_rowtiles = (int)((R + kSplitRows - 1) / kSplitRows);
-  const int nblk_all = (s.Nk + KB - 1) / KB;
-  const int bps = (nblk_all + num_splits - 1) / num_splits;
+  // blocks a tile's chunks cover: all of the keys, or the blocks the band
+  // of a tile can span
+  const int nblk = band_tile_blocks(s, mb, KB);
+  const int bps = (nblk + num_splits - 1) / num_splits;
   const long long n_items = (long long)s.B * s.Hkv * n_rowtiles * num_splits;
   const long long n_rows = (long long)s.B * s.Hq * s.Nq;
   float* ws_o = static_cast<float*>(ws);
   f32x4* ws_ml = reinterpret_cast<f32x4*>(ws_o + n_rows * num_splits * D);
   const float c2 = s.scale * kLog2e;
   const unsigned wpb = NT / 64;
-  hipLaunchKernelGGL((splitkv_partial_kernel<D, CAUSAL>),
+  hipLaunchKernelGGL((splitkv_partial_kernel<D, MODE>),
                      dim3((unsigned)((n_items + wpb - 1) / wpb)), dim3(NT), 0,
                      stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), ws_o, ws_ml, s.Hq, s.Hkv,
                      s.Nq, s.Nk, c2, n_rowtiles, num_splits, bps,
-                     (int)n_items);
+                     (int)n_items, mb.wl, mb.wr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((splitkv_merge_kernel<D, OUT_F32>),
                      dim3((unsigned)((n_rows + wpb - 1) / wpb)), dim3(NT), 0,
                      stream, ws_o, ws_ml, o, lse, n_rows, num_splits);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
+                    float* lse, const Shape& s, bool out_f32, int num_splits,
+                    void* ws, hipStream_t stream) {
+  const MaskBounds mb = mask_bounds(s);
+#define FA_MODE(M_)                                                        \
+  return out_f32 ? launch<D, M_, true>(q, k, v, o, lse, s, num_splits, ws,  \
+                                       mb, stream)                         \
+                 : launch<D, M_, false>(q, k, v, o, lse, s, num_splits, ws, \
+                                        mb, stream);
+  if (mb.kind == 0) { FA_MODE(kNone) }
+  if (mb.kind == 1) { FA_MODE(kCausal) }
+  FA_MODE(kBand)
+#undef FA_MODE
 }
 
 }  // namespace
@@ -409,22 +447,12 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s, bool out_f32,
                           int num_splits, void* workspace,
                           hipStream_t stream) {
-  const bool c = s.causal != 0;
-#define FA_DISPATCH(D_)                                                     \
-  if (s.d == D_) {                                                          \
-    if (c)                                                                  \
-      return out_f32 ? launch<D_, true, true>(q, k, v, o, lse, s,           \
-                                              num_splits, workspace, stream) \
-                     : launch<D_, true, false>(q, k, v, o, lse, s,          \
-                                               num_splits, workspace, stream); \
-    return out_f32 ? launch<D_, false, true>(q, k, v, o, lse, s, num_splits, \
-                                             workspace, stream)             \
-                   : launch<D_, false, false>(q, k, v, o, lse, s, num_splits, \
-                                              workspace, stream);           \
-  }
-  FA_DISPATCH(128)
-  FA_DISPATCH(64)
-#undef FA_DISPATCH
+  if (s.d == 128)
+    return launch_d<128>(q, k, v, o, lse, s, out_f32, num_splits, workspace,
+                         stream);
+  if (s.d == 64)
+    return launch_d<64>(q, k, v, o, lse, s, out_f32, num_splits, workspace,
+                        stream);
   return hipErrorInvalidValue;
 }
 

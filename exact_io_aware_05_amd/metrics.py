@@ -35,6 +35,18 @@ def visible_pairs(Nq, Nk, causal, window=None) -> int:
     return int(np.maximum(hi - lo + 1, 0).sum())
 
 
+def visible_keys(Nq, Nk, causal, window=None) -> int:
+    """Keys that at least one query row sees (the K/V rows a windowed call
+    must read): the union of the rows' key ranges, which is one range."""
+    left, right = (-1, -1) if window is None else window
+    c0, c1 = Nk - Nq, Nk - 1           # places of the first and last rows
+    lo = 0 if left < 0 else max(0, c0 - left)
+    hi = Nk - 1 if right < 0 else min(Nk - 1, c1 + right)
+    if causal:
+        hi = min(hi, c1)
+    return max(hi - lo + 1, 0)
+
+
 def attention_window_flops(B, Hq, Nq, Nk, d, causal, window) -> float:
     """Forward FLOPs of a windowed mask: 4 d per visible pair (the two
     products), counted exactly."""

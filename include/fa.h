@@ -135,8 +135,12 @@ int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
  * that side: (-1, -1) is fa_fwd without a mask, (-1, 0) or the causal flag
  * alone is fa_fwd causal, and those cases (and windows that hide nothing,
  * left >= Nk - 1 and right >= Nq - 1) are run by fa_fwd itself, KV split
- * included.  Otherwise the tiled prefill kernel runs with the band: K/V
- * blocks outside every row's window of a 256-row block are never read.
+ * included.  Otherwise the kernel fa_fwd would choose for the shape runs
+ * with the band: the tiled prefill kernel, where K/V blocks outside every
+ * row's window of a 256-row block are never read, or, when few query rows
+ * share a KV head (decode), the KV-split form with its chunks cut from the
+ * keys a row tile's window can reach (the last window_left + 1 keys for a
+ * single query), its workspace taken from the stream-ordered pool.
  * Rows whose window holds no key get O = 0 and lse = -inf.  Layouts,
  * types, alignment, asynchrony and status codes as for fa_fwd;
  * FA_ERR_INVALID_ARG also for a bound below -1.

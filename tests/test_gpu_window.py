@@ -43,6 +43,12 @@ CASES = [
     (1, 2, 2, 1000, 1000, 128, False, (63, 64)),   # block-sized bounds
     (2, 8, 2, 1, 5000, 128, False, (1000, -1)),    # decode row, last 1001
     (1, 2, 1, 77, 4000, 64, True, (3000, 5)),      # chunk of a long cache
+    # KV-split form (few query rows per KV head): chunks cut from the band
+    (4, 16, 4, 4, 9000, 64, True, (2000, -1)),
+    (2, 8, 8, 1, 700, 128, False, (0, 0)),
+    (1, 32, 8, 2, 32768, 128, False, (4096, 3)),
+    (3, 6, 2, 20, 3000, 128, True, (100, -1)),
+    (2, 4, 1, 3, 100, 128, False, (40, 1)),
 ]
 
 
@@ -94,6 +100,23 @@ def test_window_gqa_prefill_full_size_sampled_rows():
                                        rows=rows, window=(4096, -1))
     compare(O[:, :, rows], L[:, :, rows], O_ref, L_ref,
             what="gqa prefill, window 4096")
+
+
+def test_window_decode_full_size():
+    """The decode workload (B16 Hq32 Hkv8, one query over 32768 cached
+    keys, d128) with a 4096-key window, every output row against the
+    oracle; the KV-split form then reads only the window's keys."""
+    from exact_io_aware_05_amd import ops
+    w = workload(4)
+    assert ops.default_num_splits(w.B, w.Hq, w.Hkv, w.Nq, 4128, w.d) > 0
+    q, k, v = make_inputs(w, seed=0)
+    o, lse = _both(dev(q), dev(k), dev(v), (4096, -1), False, w.scale)
+    O, L = host(o), host(lse)
+    del o, lse
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=False,
+                                       scale=float(np.float32(w.scale)),
+                                       window=(4096, -1))
+    compare(O, L, O_ref, L_ref, what="decode, window 4096")
 
 
 def test_window_deterministic():

@@ -88,3 +88,22 @@ def test_visible_pairs_counts():
                             (not causal or j <= c)
                         n += ok
                 assert visible_pairs(Nq, Nk, causal, w) == n, (Nq, Nk, w)
+
+
+def test_visible_keys_counts():
+    from exact_io_aware_05_amd.metrics import visible_keys
+    assert visible_keys(1, 32768, False, (4096, -1)) == 4097
+    assert visible_keys(1, 100, False) == 100
+    assert visible_keys(10, 100, True, (5, -1)) == 15
+    for Nq, Nk in ((4, 7), (7, 4), (6, 6)):
+        for w in ((-1, -1), (0, 0), (2, 1), (-1, 2), (3, -1)):
+            for causal in (False, True):
+                seen = set()
+                for i in range(Nq):
+                    c = i + Nk - Nq
+                    for j in range(Nk):
+                        if (w[0] < 0 or j >= c - w[0]) and \
+                                (w[1] < 0 or j <= c + w[1]) and \
+                                (not causal or j <= c):
+                            seen.add(j)
+                assert visible_keys(Nq, Nk, causal, w) == len(seen)

@@ -33,7 +33,8 @@ definition (S = scale Q K^T with the mask, P = row softmax of S, O = P V):
 and with grouped-query attention each KV head receives the sum of the
 gradients of all the query heads that read it.  Masked entries have P = 0
 and so no gradient.  A query row that sees no key (O = 0, lse = -inf) gives
-no gradient either.
+no gradient either.  ``window`` is the forward oracle's sliding window
+(left, right); it only changes which entries are masked.
 """
 from __future__ import annotations
 
@@ -44,14 +45,15 @@ from .attention import _check, kv_head_of, reference_attention, visible_mask
 __all__ = ["reference_attention_backward", "recompute_backward"]
 
 
-def reference_attention_backward(q, k, v, do, *, causal: bool, scale: float):
+def reference_attention_backward(q, k, v, do, *, causal: bool, scale: float,
+                                 window=None):
     """The gradients from the definition, with S, P, dP and dS materialised
     per head in float64.  Returns (dq, dk, dv)."""
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     if do.shape != q.shape:
         raise ValueError("do must have the shape of q")
     _, _, _, P = reference_attention(q, k, v, causal=causal, scale=scale,
-                                     return_sp=True)
+                                     return_sp=True, window=window)
     dq = np.zeros(q.shape)
     dk = np.zeros(k.shape)
     dv = np.zeros(v.shape)
@@ -69,7 +71,7 @@ def reference_attention_backward(q, k, v, do, *, causal: bool, scale: float):
 
 
 def recompute_backward(q, k, v, o, lse, do, *, causal: bool, scale: float,
-                       block_q: int, block_k: int):
+                       block_q: int, block_k: int, window=None):
     """The recomputation form, block by block, in float64.
 
     D_i = dO_i . O_i is formed once per row from the forward output.  Then
@@ -97,7 +99,7 @@ def recompute_backward(q, k, v, o, lse, do, *, causal: bool, scale: float,
                 for c0 in range(0, Nk, block_k):
                     cols = np.arange(c0, min(c0 + block_k, Nk))
                     S = scale * (q[b, h, rows] @ k[b, hk, cols].T)
-                    vis = visible_mask(rows, cols, Nq, Nk, causal)
+                    vis = visible_mask(rows, cols, Nq, Nk, causal, window)
                     vis &= has[:, None]
                     P = np.where(vis, np.exp(np.where(vis, S, 0.0) - Lr[:, None]),
                                  0.0)

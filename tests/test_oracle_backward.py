@@ -28,11 +28,12 @@ def _rand(B, Hq, Hkv, Nq, Nk, d, seed):
     return q, k, v, do
 
 
-def _numeric_grads(q, k, v, do, causal, scale, h=1e-5):
+def _numeric_grads(q, k, v, do, causal, scale, h=1e-5, window=None):
     """Central differences of L = sum(dO * O) with respect to every input
     element (the forward definition only)."""
     def loss(q_, k_, v_):
-        O, _ = reference_attention(q_, k_, v_, causal=causal, scale=scale)
+        O, _ = reference_attention(q_, k_, v_, causal=causal, scale=scale,
+                                   window=window)
         return float((do * O).sum())
     grads = []
     for which in range(3):
@@ -217,3 +218,107 @@ def test_checks_catch_planted_mistake(name):
         if caught:
             break
     assert caught, f"mutant {name} passed every check"
+
+
+# ------------------------------------------------------- sliding window
+# B, Hq, Hkv, Nq, Nk, d, causal, scale, window
+WINDOW_FD_CASES = [
+    (1, 2, 1, 4, 6, 2, False, 0.7, (1, 1)),
+    (1, 2, 2, 5, 5, 3, True, 0.5, (2, -1)),
+    (1, 1, 1, 6, 4, 2, False, 0.9, (0, 2)),    # Nq > Nk: empty rows
+    (1, 4, 2, 3, 7, 2, False, 0.6, (-1, 0)),
+]
+
+
+@pytest.mark.parametrize("case", WINDOW_FD_CASES, ids=str)
+def test_window_definition_matches_finite_differences(case):
+    B, Hq, Hkv, Nq, Nk, d, causal, scale, window = case
+    q, k, v, do = _rand(B, Hq, Hkv, Nq, Nk, d, seed=sum(case[:6]) + 50)
+    got = reference_attention_backward(q, k, v, do, causal=causal,
+                                       scale=scale, window=window)
+    want = _numeric_grads(q, k, v, do, causal, scale, window=window)
+    for g, w in zip(got, want):
+        assert np.max(np.abs(g - w)) <= 1e-7 * (1 + np.max(np.abs(w)))
+
+
+def test_window_matches_torch_autograd_float64():
+    torch = pytest.importorskip("torch")
+    B, Hq, Hkv, Nq, Nk, d, scale = 1, 4, 2, 12, 15, 8, 0.3
+    for window in ((3, 0), (2, 5), (-1, 1), (4, -1)):
+        q, k, v, do = _rand(B, Hq, Hkv, Nq, Nk, d, seed=60 + window[0])
+        Q = torch.tensor(q, requires_grad=True)
+        K = torch.tensor(k, requires_grad=True)
+        V = torch.tensor(v, requires_grad=True)
+        G = Hq // Hkv
+        Kr, Vr = K.repeat_interleave(G, dim=1), V.repeat_interleave(G, dim=1)
+        S = scale * (Q @ Kr.transpose(-1, -2))
+        c = torch.arange(Nq)[:, None] + (Nk - Nq)
+        j = torch.arange(Nk)[None, :]
+        hide = torch.zeros(Nq, Nk, dtype=torch.bool)
+        if window[0] >= 0:
+            hide |= j < c - window[0]
+        if window[1] >= 0:
+            hide |= j > c + window[1]
+        O = torch.softmax(S.masked_fill(hide, float("-inf")), dim=-1) @ Vr
+        O.backward(torch.tensor(do))
+        got = reference_attention_backward(q, k, v, do, causal=False,
+                                           scale=scale, window=window)
+        for g, w in zip(got, (Q.grad, K.grad, V.grad)):
+            assert np.max(np.abs(g - w.numpy())) <= 1e-12
+
+
+def test_window_of_one_key_gradients():
+    """window (0, 0): row i sees only key c = i + Nk - Nq with weight 1, so
+    O_i = v_c does not depend on q or k (dQ = dK = 0) and dV_c = dO_i."""
+    q, k, v, do = _rand(1, 2, 1, 5, 7, 3, seed=70)
+    dq, dk, dv = reference_attention_backward(q, k, v, do, causal=False,
+                                              scale=0.8, window=(0, 0))
+    assert np.max(np.abs(dq)) <= 1e-12 and np.max(np.abs(dk)) <= 1e-12
+    want = np.zeros_like(dv)
+    for h in range(2):
+        for i in range(5):
+            want[0, 0, i + 2] += do[0, h, i]
+    assert np.max(np.abs(dv - want)) <= 1e-12
+
+
+@pytest.mark.parametrize("window", [(2, 1), (0, -1), (5, 0)])
+@pytest.mark.parametrize("bq,bk", [(1, 1), (3, 4), (64, 64)])
+def test_window_recompute_equals_definition(window, bq, bk):
+    q, k, v, do = _rand(1, 4, 2, 11, 17, 6, seed=bq + bk + window[0])
+    scale = 0.4
+    O, lse = reference_attention(q, k, v, causal=False, scale=scale,
+                                 window=window)
+    want = reference_attention_backward(q, k, v, do, causal=False,
+                                        scale=scale, window=window)
+    got = recompute_backward(q, k, v, O, lse, do, causal=False, scale=scale,
+                             block_q=bq, block_k=bk, window=window)
+    for g, w in zip(got, want):
+        assert np.max(np.abs(g - w)) <= 1e-12
+
+
+WINDOW_MUTANTS = {
+    "window_dropped_in_definition": (
+        "return_sp=True, window=window)", "return_sp=True)"),
+    "window_dropped_in_recompute": (
+        "visible_mask(rows, cols, Nq, Nk, causal, window)",
+        "visible_mask(rows, cols, Nq, Nk, causal)"),
+}
+
+
+@pytest.mark.parametrize("name", list(WINDOW_MUTANTS))
+def test_window_checks_catch_planted_mistake(name):
+    mod = _load_mutant(*WINDOW_MUTANTS[name])
+    B, Hq, Hkv, Nq, Nk, d, causal, scale, window = WINDOW_FD_CASES[0]
+    q, k, v, do = _rand(B, Hq, Hkv, Nq, Nk, d, seed=sum(WINDOW_FD_CASES[0][:6]) + 50)
+    if name.endswith("recompute"):
+        O, lse = reference_attention(q, k, v, causal=causal, scale=scale,
+                                     window=window)
+        got = mod.recompute_backward(q, k, v, O, lse, do, causal=causal,
+                                     scale=scale, block_q=2, block_k=2,
+                                     window=window)
+    else:
+        got = mod.reference_attention_backward(q, k, v, do, causal=causal,
+                                               scale=scale, window=window)
+    want = _numeric_grads(q, k, v, do, causal, scale, window=window)
+    assert any(np.max(np.abs(g - w)) > 1e-7 * (1 + np.max(np.abs(w)))
+               for g, w in zip(got, want)), name

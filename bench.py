@@ -54,9 +54,12 @@ from exact_io_aware_05_amd.metrics import (  # noqa: E402
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None,
-             "gqa_prefill_window": 3, "decode_window": 4}
+             "gqa_prefill_window": 3, "decode_window": 4,
+             "gqa_prefill_window_bwd": 3}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
-WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1)}
+# (and fa_bwd_window)
+WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
+           "gqa_prefill_window_bwd": (4096, -1)}
 # HBM bytes per launch of each workload's dominant kernel, from two
 # rocprofv3 --pmc runs of this script (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch; summaries under profiles/).  Each counter is scaled by what it
@@ -139,14 +142,14 @@ def cpu_baseline(w, q, k, v, budget_s=10.0, do=None, window=None):
         else:
             reference_attention_backward(
                 qh, kh, vh, bf16_bits_to_f64(do[:1, h:h + 1]),
-                causal=w.causal, scale=scale)
+                causal=w.causal, scale=scale, window=window)
         t_total += time.perf_counter() - t0
         done += 1
     count = attention_fwd_flops if do is None else attention_bwd_flops
     flops = count(1, done, w.Nq, w.Nk, w.d, w.causal)
     if window is not None:
         flops = attention_window_flops(1, done, w.Nq, w.Nk, w.d, w.causal,
-                                       window)
+                                       window) * (1.0 if do is None else 2.5)
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
@@ -320,7 +323,7 @@ def main(argv=None):
     lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
 
-    if window is not None:
+    if window is not None and not backward:
         # fa_fwd_window picks the form itself (KV split for a single query,
         # its workspace from the stream-ordered pool)
         splits = 0
@@ -344,7 +347,11 @@ def main(argv=None):
         splits = 0
         do = make_dout(w.B, w.Hq, w.Nq, w.d, seed=0)
         DO = _dev_tensor(do)
-        ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
+        if window is None:
+            ops.fa_fwd(Q, K, V, causal=w.causal, scale=w.scale, o=o, lse=lse)
+        else:
+            ops.fa_fwd_window(Q, K, V, window, causal=w.causal, scale=w.scale,
+                              o=o, lse=lse)
         dq = torch.empty_like(Q)
         dk = torch.empty_like(K)
         dv = torch.empty_like(V)
@@ -353,7 +360,7 @@ def main(argv=None):
 
         def step():
             ops.fa_bwd(Q, K, V, o, lse, DO, causal=w.causal, scale=w.scale,
-                       dq=dq, dk=dk, dv=dv, workspace=ws)
+                       dq=dq, dk=dk, dv=dv, workspace=ws, window=window)
     else:
         splits = 0
 
@@ -368,7 +375,7 @@ def main(argv=None):
     flops = count(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
     if window is not None:
         flops = attention_window_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal,
-                                       window)
+                                       window) * (2.5 if backward else 1.0)
     nbytes = attention_fwd_bytes(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d)
     if window is not None:   # only the keys some row sees must be read
         nbytes = attention_fwd_bytes(
@@ -390,6 +397,9 @@ def main(argv=None):
         value = flops / (ms_per_step * 1e-3) / 1e12
         if backward:
             metric = f"attn bwd TFLOP/s ({w.name})"
+            if window is not None:
+                metric = (f"attn bwd TFLOP/s ({w.name}, window {window[0]},"
+                          f"{window[1]})")
         elif window is not None:
             metric = (f"attn fwd TFLOP/s ({w.name}, window {window[0]},"
                       f"{window[1]})")

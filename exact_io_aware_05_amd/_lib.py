@@ -36,6 +36,8 @@ SIGNATURES = {
     "fa_bwd_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),
     "fa_bwd": (_c_int, [_vp] * 9 + [_c_int] * 7 + [_c_float, _c_int, _vp,
                                                    _c_size, _vp]),
+    "fa_bwd_window": (_c_int, [_vp] * 9 + [_c_int] * 9 + [_c_float, _c_int,
+                                                           _vp, _c_size, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
     "fa_last_hip_error": (_c_int, []),
 }

@@ -255,6 +255,18 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
            float scale, int grad_dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream) {
+  return fa_bwd_window(q, k, v, o, lse, dout, dq, dk, dv, B, Hq, Hkv, Nq, Nk,
+                       d, causal, -1, -1, scale, grad_dtype, workspace,
+                       workspace_bytes, stream);
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk,
+                  void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                  int causal, int window_left, int window_right, float scale,
+                  int grad_dtype, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
                         grad_dtype);
   if (st != FA_OK) return st;
@@ -278,7 +290,9 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
     return FA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != FA_OK) return st;
-  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
   return hip_status(fa::launch_backward(q, k, v, o, lse, dout, dq, dk, dv, s,
                                         grad_dtype == FA_OUT_F32, workspace,
                                         stream));

@@ -242,13 +242,19 @@ __device__ __forceinline__ void row_stats(const float* v, int h, float* out) {
 // matrix products.
 constexpr int NT2 = 512;
 
-template <int D, bool CAUSAL, bool OUT_F32>
+// Mask kinds: none, causal (key j visible to query i iff j <= i + Nk - Nq),
+// band (iff i + Nk - Nq - wl <= j <= i + Nk - Nq + wr).
+constexpr int kNone = 0, kCausal = 1, kBand = 2;
+
+template <int D, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ dvec, const float* __restrict__ lse2,
     void* __restrict__ dk, void* __restrict__ dv, int Hq, int Hkv, int Nq,
-    int Nk, float c2, float scale, int n_kblk) {
+    int Nk, float c2, float scale, int n_kblk, int wl, int wr) {
+  constexpr bool CAUSAL = MODE == kCausal;
+  constexpr bool BAND = MODE == kBand;
   using T = Tiles<D>;
   constexpr int NSTEP = T::NSTEP, NTILE = T::NTILE;
   constexpr int QR = 64;  // query rows per step
@@ -296,11 +302,15 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
   for (int i = 0; i < NTILE; ++i) acc[i] = f32x16{};
 
   // query rows that can see a key of this workgroup (causal: rows i with
-  // i + off >= its first key), in steps of QR rows, for each of the G query
-  // heads of the group
-  const int t_begin = CAUSAL ? max(0, kfirst - off) / QR : 0;
-  const int t_end = (Nq + QR - 1) / QR;
-  const int n_it = G * (t_end - t_begin);
+  // i + off >= its first key; band: also i + off - wl <= its last key), in
+  // steps of QR rows, for each of the G query heads of the group
+  const int t_begin = CAUSAL ? max(0, kfirst - off) / QR
+                      : BAND ? max(0, kfirst - off - wr) / QR
+                             : 0;
+  const int t_end =
+      BAND ? (max(0, min(Nq, kfirst + 128 - off + wl)) + QR - 1) / QR
+           : (Nq + QR - 1) / QR;
+  const int n_it = G * max(0, t_end - t_begin);
   const bool keys_in = kfirst + 128 <= Nk;
   const int arow = row_slot(col);  // tile row read for operand row col
 
@@ -370,7 +380,9 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
       // every score of the step visible: all rows in range, all keys in
       // range, and the first row sees the workgroup's last key
       const bool full = q0 + QR <= Nq && keys_in &&
-                        (!CAUSAL || kfirst + 127 <= q0 + off);
+                        (!CAUSAL || kfirst + 127 <= q0 + off) &&
+                        (!BAND || (kfirst + 127 <= q0 + off + wr &&
+                                   kfirst >= q0 + QR - 1 + off - wl));
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         float lsv[16];
@@ -386,6 +398,8 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
             const int row = q0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
             bool vis = row < Nq && key < Nk;
             if (CAUSAL) vis = vis && key <= row + off;
+            if (BAND)
+              vis = vis && key <= row + off + wr && key >= row + off - wl;
             // rows that see no key have lse = -inf; their P is 0
             const float e = exp2_fast(fmaf(sp[half][i], c2, -lsv[i]));
             p[i] = vis && lsv[i] != -INFINITY ? e : 0.f;
@@ -465,13 +479,15 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ dvec, const float* __restrict__ lse2,
     void* __restrict__ dq, int Hq, int Hkv, int Nq, int Nk, float c2,
-    float scale, int n_qblk) {
+    float scale, int n_qblk, int wl, int wr) {
+  constexpr bool CAUSAL = MODE == kCausal;
+  constexpr bool BAND = MODE == kBand;
   using T = Tiles<D>;
   constexpr int NSTEP = T::NSTEP, NTILE = T::NTILE;
   constexpr int KR = 64;  // keys per step
@@ -493,7 +509,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
   const int t1 = item / G;
   const int jq = t1 % n_qblk;
   const int bh = t1 / n_qblk;
-  const int qblk = CAUSAL ? (n_qblk - 1 - jq) : jq;
+  const int qblk = MODE != kNone ? (n_qblk - 1 - jq) : jq;
   const int b = bh / Hkv, hkv = bh % Hkv;
   const int hq = hkv * G + gq;
   const int off = Nk - Nq;
@@ -524,10 +540,19 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
   const int64_t kvbase = (int64_t)bh * Nk * D;
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, qfirst + 128 + off);
+  // band: keys from the first row's lower bound to the last row's upper one
+  int j0 = 0;
+  if (BAND) {
+    kv_end = min(Nk, min(qfirst + 128, Nq) + off + wr);
+    j0 = max(0, qfirst + off - wl) / KR;
+  }
   const int nblk = kv_end > 0 ? (kv_end + KR - 1) / KR : 0;
   const int arow = row_slot(col);
-  // this lane's last visible key
-  const int lim = CAUSAL ? min(Nk - 1, qrow + off) : Nk - 1;
+  // this lane's last (band: and first) visible key
+  const int lim = CAUSAL ? min(Nk - 1, qrow + off)
+                  : BAND ? min(Nk - 1, qrow + off + wr)
+                         : Nk - 1;
+  const int lo = BAND ? qrow + off - wl : 0;
   // rows all in range (then every row sees key 0 or more)
   const bool rows_in = qfirst + 128 <= Nq;
   const char* kh = reinterpret_cast<const char*>(k + kvbase);
@@ -547,7 +572,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
                  i % Dma::NI, loff);
     }
   };
-  if (nblk > 0) copy_step(smem, 0);
+  if (nblk > j0) copy_step(smem, j0 * KR);
   wait_vmcnt0();
   __syncthreads();
 
@@ -562,7 +587,9 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
     // every score of the step visible: keys in range, rows in range, and
     // the workgroup's first row sees the step's last key
     const bool full = k0 + KR <= Nk && rows_in &&
-                      (!CAUSAL || k0 + KR - 1 <= qfirst + off);
+                      (!CAUSAL || k0 + KR - 1 <= qfirst + off) &&
+                      (!BAND || (k0 + KR - 1 <= qfirst + off + wr &&
+                                 k0 >= qfirst + 127 + off - wl));
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       // S^T = K Q^T, dP^T = V dO^T for keys 32 half + row_slot(row):
@@ -587,7 +614,8 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = k0 + 32 * half + 16 * (i >> 3) + 8 * h + (i & 7);
-          const bool vis = row_ok && key <= lim && l2 != -INFINITY;
+          const bool vis = row_ok && key <= lim && (!BAND || key >= lo) &&
+                           l2 != -INFINITY;
           const float p = vis ? exp2_fast(fmaf(sp[0][i], c2, -l2)) : 0.f;
           ds[i] = p * (sp[1][i] - dval);
         }
@@ -607,7 +635,7 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
     wait_vmcnt0();  // this wave's copies for the next step have landed
     __syncthreads();
   };
-  int j = 0;
+  int j = j0;
   for (; j + 2 <= nblk; j += 2) {
     step(j, std::integral_constant<int, 0>{});
     step(j + 1, std::integral_constant<int, 1>{});
@@ -634,11 +662,12 @@ __global__ __launch_bounds__(NT, 2) void bwd_dq_kernel(
   }
 }
 
-template <int D, bool CAUSAL, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32>
 hipError_t launch_bwd(const void* q, const void* k, const void* v,
                       const void* o, const float* lse, const void* dout,
                       void* dq, void* dk, void* dv, const Shape& s,
-                      void* workspace, hipStream_t stream) {
+                      const MaskBounds& mb, void* workspace,
+                      hipStream_t stream) {
   const long long rows = (long long)s.B * s.Hq * s.Nq;
   float* dvec = static_cast<float*>(workspace);
   float* lse2 = dvec + rows;
@@ -656,26 +685,44 @@ hipError_t launch_bwd(const void* q, const void* k, const void* v,
   {
     const int n_kblk = (s.Nk + 127) / 128;
     const long long items = (long long)s.B * s.Hkv * n_kblk;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, OUT_F32>),
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, OUT_F32>),
                        dim3((unsigned)items), dim3(NT2), 0, stream,
                        static_cast<const uint16_t*>(q),
                        static_cast<const uint16_t*>(k),
                        static_cast<const uint16_t*>(v),
                        static_cast<const uint16_t*>(dout), dvec, lse2, dk, dv,
-                       s.Hq, s.Hkv, s.Nq, s.Nk, c2, s.scale, n_kblk);
+                       s.Hq, s.Hkv, s.Nq, s.Nk, c2, s.scale, n_kblk, mb.wl,
+                       mb.wr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   const int n_qblk = (s.Nq + 127) / 128;
   const long long items = (long long)s.B * s.Hq * n_qblk;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, OUT_F32>),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, OUT_F32>),
                      dim3((unsigned)items), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v),
                      static_cast<const uint16_t*>(dout), dvec, lse2, dq, s.Hq,
-                     s.Hkv, s.Nq, s.Nk, c2, s.scale, n_qblk);
+                     s.Hkv, s.Nq, s.Nk, c2, s.scale, n_qblk, mb.wl, mb.wr);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_bwd_d(const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv, const Shape& s,
+                        bool out_f32, void* ws, hipStream_t stream) {
+  const MaskBounds mb = mask_bounds(s);
+#define FA_MODE(M_)                                                          \
+  return out_f32 ? launch_bwd<D, M_, true>(q, k, v, o, lse, dout, dq, dk, dv, \
+                                           s, mb, ws, stream)                \
+                 : launch_bwd<D, M_, false>(q, k, v, o, lse, dout, dq, dk,   \
+                                            dv, s, mb, ws, stream);
+  if (mb.kind == 0) { FA_MODE(kNone) }
+  if (mb.kind == 1) { FA_MODE(kCausal) }
+  FA_MODE(kBand)
+#undef FA_MODE
 }
 
 }  // namespace
@@ -688,24 +735,12 @@ hipError_t launch_backward(const void* q, const void* k, const void* v,
                            const void* o, const float* lse, const void* dout,
                            void* dq, void* dk, void* dv, const Shape& s,
                            bool out_f32, void* workspace, hipStream_t stream) {
-  const bool c = s.causal != 0;
-#define FA_DISPATCH(D_)                                                       \
-  if (s.d == D_) {                                                            \
-    if (c)                                                                    \
-      return out_f32 ? launch_bwd<D_, true, true>(q, k, v, o, lse, dout, dq,  \
-                                                  dk, dv, s, workspace, stream) \
-                     : launch_bwd<D_, true, false>(q, k, v, o, lse, dout, dq, \
-                                                   dk, dv, s, workspace,      \
-                                                   stream);                   \
-    return out_f32 ? launch_bwd<D_, false, true>(q, k, v, o, lse, dout, dq,   \
-                                                 dk, dv, s, workspace, stream) \
-                   : launch_bwd<D_, false, false>(q, k, v, o, lse, dout, dq,  \
-                                                  dk, dv, s, workspace,       \
-                                                  stream);                    \
-  }
-  FA_DISPATCH(128)
-  FA_DISPATCH(64)
-#undef FA_DISPATCH
+  if (s.d == 128)
+    return launch_bwd_d<128>(q, k, v, o, lse, dout, dq, dk, dv, s, out_f32,
+                             workspace, stream);
+  if (s.d == 64)
+    return launch_bwd_d<64>(q, k, v, o, lse, dout, dq, dk, dv, s, out_f32,
+                            workspace, stream);
   return hipErrorInvalidValue;
 }
 

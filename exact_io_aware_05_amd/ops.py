@@ -183,10 +183,11 @@ def _grad(name, t, shape, dtype, like):
 
 def fa_bwd(q, k, v, o, lse, do, causal=False, scale=None,
            grad_dtype=torch.bfloat16, dq=None, dk=None, dv=None,
-           workspace=None):
+           workspace=None, window=None):
     """Attention backward through ``fa_bwd`` from the forward inputs, its
     bf16 output ``o`` and ``lse``, and the incoming gradient ``do``;
-    returns ``(dq, dk, dv)``."""
+    returns ``(dq, dk, dv)``.  With ``window = (left, right)`` it runs
+    ``fa_bwd_window`` (the mask of ``fa_fwd_window``)."""
     B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
     for name, t in (("o", o), ("do", do)):
         if (not isinstance(t, torch.Tensor) or t.dtype != torch.bfloat16
@@ -206,11 +207,20 @@ def fa_bwd(q, k, v, o, lse, do, causal=False, scale=None,
     need = bwd_workspace_bytes(B, Hq, Nq)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    st = load().fa_bwd(
-        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
-        do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
-        FA_OUT_F32 if grad_dtype == torch.float32 else FA_OUT_BF16,
-        workspace.data_ptr(), workspace.numel(), _stream(q))
-    check(st, "fa_bwd")
+    gd = FA_OUT_F32 if grad_dtype == torch.float32 else FA_OUT_BF16
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+            dv.data_ptr())
+    if window is None:
+        st = load().fa_bwd(*ptrs, B, Hq, Hkv, Nq, Nk, d, int(bool(causal)),
+                           scale, gd, workspace.data_ptr(), workspace.numel(),
+                           _stream(q))
+        check(st, "fa_bwd")
+    else:
+        left, right = (int(x) for x in window)
+        st = load().fa_bwd_window(*ptrs, B, Hq, Hkv, Nq, Nk, d,
+                                  int(bool(causal)), left, right, scale, gd,
+                                  workspace.data_ptr(), workspace.numel(),
+                                  _stream(q))
+        check(st, "fa_bwd_window")
     return dq, dk, dv

@@ -214,6 +214,23 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o,
            float scale, int grad_dtype, void* workspace,
            size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Backward pass of fa_fwd_window: fa_bwd with the sliding-window mask of
+ * fa_fwd_window (same window_left / window_right meaning; -1 is no bound
+ * on that side), given the o and lse of fa_fwd_window for the same
+ * arguments.  Entries outside a row's window have P = 0 and no gradient;
+ * K/V blocks (query row steps) that no row (key) of a block can reach are
+ * skipped.  Arguments, layouts, workspace and status codes as for fa_bwd;
+ * FA_ERR_INVALID_ARG also for a bound below -1.  fa_bwd is this call with
+ * both bounds -1.
+ */
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
+                  const float* lse, const void* dout, void* dq, void* dk,
+                  void* dv, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                  int causal, int window_left, int window_right, float scale,
+                  int grad_dtype, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* fa_status_string(int status);
 

@@ -238,3 +238,28 @@ def test_window_unsupported(lib):
     assert _win(lib, d=96, wl=-1, wr=-1) == _lib.FA_ERR_UNSUPPORTED
     assert _win(lib, Nk=(1 << 23) + 1, d=128) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
+
+
+def _bwdw(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=4,
+             Hkv=2, Nq=16, Nk=16, d=64, causal=0, wl=4, wr=0, scale=0.125,
+             out=0, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_bwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                             a["do"], a["dq"], a["dk"], a["dv"], a["B"],
+                             a["Hq"], a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                             a["causal"], a["wl"], a["wr"], a["scale"],
+                             a["out"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw", INVALID + [dict(wl=-2), dict(wr=-3),
+                                          dict(do=None), dict(dq=P + 4),
+                                          dict(ws=None), dict(wsb=8)],
+                         ids=lambda k: str(k))
+def test_bwd_window_invalid_arguments(lib, kw):
+    assert _bwdw(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_bwd_window_unsupported(lib):
+    assert _bwdw(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0

@@ -126,3 +126,68 @@ def test_window_deterministic():
     b = _ops().fa_fwd_window(Q, K, V, (200, 10), out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------- backward
+def _window_grads(q, k, v, do, window, causal, scale):
+    """fp32 and bf16 gradients of one windowed forward + two backward calls;
+    the bf16 ones must be the round-to-nearest-even of the fp32 ones."""
+    ops = _ops()
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    o, lse = ops.fa_fwd_window(Q, K, V, window, causal=causal, scale=scale)
+    g32 = ops.fa_bwd(Q, K, V, o, lse, DO, causal=causal, scale=scale,
+                     grad_dtype=torch.float32, window=window)
+    g16 = ops.fa_bwd(Q, K, V, o, lse, DO, causal=causal, scale=scale,
+                     grad_dtype=torch.bfloat16, window=window)
+    torch.cuda.synchronize()
+    for a, b, name in zip(g32, g16, ("dq", "dk", "dv")):
+        assert torch.equal(a.to(torch.bfloat16), b), f"bf16 {name} != RNE(fp32)"
+    return [host(t) for t in g32]
+
+
+BWD_CASES = [
+    (1, 4, 2, 700, 700, 128, False, (100, 0)),
+    (1, 4, 4, 600, 600, 64, True, (257, -1)),
+    (2, 2, 1, 300, 900, 128, False, (50, 20)),
+    (1, 2, 2, 900, 300, 128, True, (64, -1)),      # rows that see no key
+    (1, 2, 1, 513, 513, 64, False, (0, 0)),        # dq = dk = 0
+    (1, 2, 2, 1000, 1000, 128, False, (-1, 70)),
+    (1, 2, 2, 1000, 1000, 128, False, (127, 128)),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: "x".join(
+    map(str, c[:6])) + f"-{'causal' if c[6] else 'full'}-w{c[7][0]},{c[7][1]}")
+def test_window_backward_matches_oracle(case):
+    from fa_inputs import make_dout
+    from oracle import reference_attention_backward
+    from tests.gpu_util import compare_grad
+    B, Hq, Hkv, Nq, Nk, d, causal, window = case
+    q, k, v = make_qkv(B, Hq, Hkv, Nq, Nk, d, seed=35)
+    do = make_dout(B, Hq, Nq, d, seed=35)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    got = _window_grads(q, k, v, do, window, causal, scale)
+    ref = reference_attention_backward(f64(q), f64(k), f64(v), f64(do),
+                                       causal=causal, scale=scale,
+                                       window=window)
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        compare_grad(g, r, what=f"window {window} {name}")
+
+
+def test_window_backward_without_bounds_matches_fa_bwd():
+    """Bounds that hide nothing give fa_bwd's gradients bit for bit."""
+    from fa_inputs import make_dout
+    B, Hq, Hkv, N, d = 1, 4, 2, 333, 128
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, d, seed=36)
+    do = make_dout(B, Hq, N, d, seed=36)
+    ops = _ops()
+    Q, K, V, DO = dev(q), dev(k), dev(v), dev(do)
+    for causal in (False, True):
+        o, lse = ops.fa_fwd(Q, K, V, causal=causal)
+        ref = ops.fa_bwd(Q, K, V, o, lse, DO, causal=causal,
+                         grad_dtype=torch.float32)
+        for w in ((-1, -1), (N, N)):
+            got = ops.fa_bwd(Q, K, V, o, lse, DO, causal=causal,
+                             grad_dtype=torch.float32, window=w)
+            for a, b in zip(got, ref):
+                assert torch.equal(a, b), (causal, w)

@@ -72,21 +72,34 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "194f8c44a4c50a2fcb8accd97157ba0f0dfc19087963db25debf459eacffa4d4",
-        "fetch_kib": 71270.1, "write_kib": 66560.1},
+        "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
+        "fetch_kib": 71281.0, "write_kib": 66561.0},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "194f8c44a4c50a2fcb8accd97157ba0f0dfc19087963db25debf459eacffa4d4",
-        "fetch_kib": 514048.7, "write_kib": 266357.8},
+        "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
+        "fetch_kib": 514058.8, "write_kib": 266359.1},
+    "gqa_prefill_window": {
+        "source": "fa_prefill.hip",
+        "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
+        "fetch_kib": 67574.9, "write_kib": 66560.2},
+    # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "3025497eb28833847f3d1d28ac24891368e33999e6a3aaf8173c5b74c56a3917",
-        "fetch_kib": 1048897.2, "write_kib": 2112.0},
+        "sha256": "881b3a4e74d869e761c2e74a075bab2a8f2056a6ba18c7b25863a5b105387021",
+        "fetch_kib": 1048897.6, "write_kib": 2112.2},
+    "decode_window": {
+        "source": "fa_splitkv.hip",
+        "sha256": "881b3a4e74d869e761c2e74a075bab2a8f2056a6ba18c7b25863a5b105387021",
+        "fetch_kib": 132420.9, "write_kib": 2112.2},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "b7f748803f3cfa55fcf1309956fc96e6f29d7a8f9cac52701547fd73d8fdeca0",
-        "fetch_kib": 612021.6, "write_kib": 100352.2},
+        "sha256": "e8e76eb17411cfff27993283a50ad0121075c7027f6b089191acfe796ed920d0",
+        "fetch_kib": 576941.8, "write_kib": 100354.8},
+    "gqa_prefill_window_bwd": {
+        "source": "fa_backward.hip",
+        "sha256": "e8e76eb17411cfff27993283a50ad0121075c7027f6b089191acfe796ed920d0",
+        "fetch_kib": 298552.5, "write_kib": 100352.3},
 }
 
 

@@ -11,3 +11,4 @@ from .attention import (  # noqa: F401
 from .backward import (  # noqa: F401
     reference_attention_backward, recompute_backward,
 )
+from .paged import paged_rows, paged_attention  # noqa: F401

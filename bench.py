@@ -22,7 +22,9 @@ priced at 2.5 times the forward FLOPs; its roofline covers the whole call.
 with a 4096-key sliding window (causal), priced at 4 d FLOPs per visible
 pair, counted exactly.  ``--workload decode_window`` runs the decode workload through
 ``fa_fwd_window`` with a 4096-key window (KV split over the window's keys),
-priced at the bytes of the keys it must read.  ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
+priced at the bytes of the keys it must read.  ``--workload decode_paged`` runs ``fa_fwd_paged`` on the decode workload's
+shape stored in 256-key pages scattered over the pool, priced like the
+decode.  ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
 causal prompts (seeded log-uniform lengths in [256, 8192], 32768 tokens,
 the GQA heads above), priced at the causal FLOPs of each sequence.
 
@@ -45,7 +47,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from fa_inputs import (VARLEN_PREFILL, make_dout, make_inputs,  # noqa: E402
-                       make_varlen, varlen_lengths, workload)
+                       make_paged, make_varlen, varlen_lengths, workload)
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
     PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_bwd_flops,
     attention_fwd_bytes, attention_fwd_flops, attention_window_flops,
@@ -55,7 +57,7 @@ METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None,
              "gqa_prefill_window": 3, "decode_window": 4,
-             "gqa_prefill_window_bwd": 3}
+             "gqa_prefill_window_bwd": 3, "decode_paged": None}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
 # (and fa_bwd_window)
 WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
@@ -298,6 +300,64 @@ def bench_varlen(args):
     return 0
 
 
+# the decode workload's shape over a paged cache: 256-key pages, 128 per
+# sequence, scattered over the pool
+PAGED_DECODE = dict(name="decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256",
+                    B=16, Hq=32, Hkv=8, Nq=1, d=128, page_size=256,
+                    max_pages=128, scale=1.0 / math.sqrt(128))
+
+
+def bench_paged(args):
+    """One fa_fwd_paged call (partial + merge kernels, workspace allocated
+    once) over the decode workload's shape stored in scattered pages."""
+    import torch
+    from exact_io_aware_05_amd import ops
+    sp = PAGED_DECODE
+    B, Hq, Hkv, Nq, d = sp["B"], sp["Hq"], sp["Hkv"], sp["Nq"], sp["d"]
+    P, maxp = sp["page_size"], sp["max_pages"]
+    lens = [P * maxp] * B
+    q, kc, vc, table, sl = make_paged(B, Hq, Hkv, Nq, d, P, maxp, lens, seed=0)
+    Q, KC, VC = _dev_tensor(q), _dev_tensor(kc), _dev_tensor(vc)
+    del kc, vc
+    T = torch.from_numpy(table).cuda()
+    SL = torch.from_numpy(sl).cuda()
+    splits = ops.paged_num_splits(B, Hq, Hkv, Nq, d, P, maxp)
+    ws = torch.empty(ops.splitkv_workspace_bytes(B, Hq, Nq, d, splits),
+                     dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.fa_fwd_paged(Q, KC, VC, T, SL, scale=sp["scale"], o=o, lse=lse,
+                         num_splits=splits, workspace=ws)
+
+    ms, kern_ms = _time_steps(step, args.steps, args.warmup,
+                              torch.cuda.current_stream())
+    nbytes = attention_fwd_bytes(B, Hq, Hkv, Nq, P * maxp, d)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    out = {
+        "metric": f"attn decode HBM GB/s ({sp['name']})",
+        "value": round(nbytes / (ms * 1e-3) / 1e9, 3), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) fp32 rounded to bf16; seeded "
+                "page permutation)",
+        "config": {"workload": sp["name"], "B": B, "Hq": Hq, "Hkv": Hkv,
+                   "Nq": Nq, "Nk": P * maxp, "d": d, "page_size": P,
+                   "pages_per_seq": maxp, "causal": False,
+                   "scale": sp["scale"], "out_dtype": "bf16",
+                   "kv_splits": splits, "kernel_ms": round(kern_ms, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(sp["name"])},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -327,6 +387,8 @@ def main(argv=None):
 
     if args.workload == "varlen_prefill":
         return bench_varlen(args)
+    if args.workload == "decode_paged":
+        return bench_paged(args)
     w = workload(WORKLOADS[args.workload])
     backward = args.workload.endswith("_bwd")
     window = WINDOWS.get(args.workload)

@@ -31,6 +31,10 @@ SIGNATURES = {
     "fa_default_num_splits": (_c_int, [_c_int] * 6),
     "fa_fwd_window": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int,
                                                            _vp]),
+    "fa_paged_num_splits": (_c_int, [_c_int] * 7),
+    "fa_fwd_paged": (_c_int, [_vp] * 7 + [_c_int] * 11 + [_c_float, _c_int,
+                                                           _c_int, _vp,
+                                                           _c_size, _vp]),
     "fa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_c_float, _c_int,
                                                            _vp]),
     "fa_bwd_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),

@@ -204,6 +204,79 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
                      stream);
 }
 
+int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
+                        int max_pages_per_seq) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Hq % Hkv) return 0;
+  if (d != 64 && d != 128) return 0;
+  if (page_size < fa::kSplitKeys || (page_size & (page_size - 1)) ||
+      max_pages_per_seq < 1)
+    return 0;
+  const long long nk = (long long)page_size * max_pages_per_seq;
+  if (nk > (1LL << 30)) return 0;
+  // as fa_fwd would split a cache of the longest length (at least one
+  // chunk: the paged form is always the KV-split form), and enough chunks
+  // that none spans 64 pages
+  int s = default_splits(B, Hq, Hkv, Nq, (int)nk);
+  if (s < 1) s = 1;
+  const long long nblk = (nk + fa::kSplitKeys - 1) / fa::kSplitKeys;
+  const long long per = fa::paged_max_blocks_per_chunk(page_size);
+  const long long need = (nblk + per - 1) / per;
+  if (s < need) s = (int)need;
+  return s <= fa::kMaxSplits ? s : 0;
+}
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                 void* o, float* lse, const int* page_table,
+                 const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int d,
+                 int num_pages, int page_size, int max_pages_per_seq,
+                 int causal, int window_left, int window_right, float scale,
+                 int out_dtype, int num_splits, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  if (!page_table || !seqlens_k ||
+      (reinterpret_cast<uintptr_t>(page_table) & 3u) ||
+      (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (num_pages < 1 || max_pages_per_seq < 1 || page_size < fa::kSplitKeys ||
+      (page_size & (page_size - 1)))
+    return FA_ERR_INVALID_ARG;
+  const long long nk = (long long)page_size * max_pages_per_seq;
+  if (nk > (1LL << 30)) return FA_ERR_UNSUPPORTED;
+  int st = check_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, (int)nk,
+                        d, scale, out_dtype);
+  if (st != FA_OK) return st;
+  if ((long long)num_pages * page_size * Hkv * d > (1LL << 46))
+    return FA_ERR_UNSUPPORTED;
+  const int need = fa_paged_num_splits(B, Hq, Hkv, Nq, d, page_size,
+                                       max_pages_per_seq);
+  if (need == 0) return FA_ERR_UNSUPPORTED;
+  const int splits = num_splits == 0 ? need : num_splits;
+  const long long nblk = (nk + fa::kSplitKeys - 1) / fa::kSplitKeys;
+  if (splits < 1 || splits > fa::kMaxSplits ||
+      (nblk + splits - 1) / splits > fa::paged_max_blocks_per_chunk(page_size))
+    return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes <
+      fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, splits))
+    return FA_ERR_INVALID_ARG;
+  const long long rowtiles = ((long long)Nq * (Hq / Hkv) + fa::kSplitRows - 1) /
+                             fa::kSplitRows;
+  if ((long long)B * Hkv * rowtiles * splits > (1LL << 31) - 64)
+    return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::Shape s{B, Hq, Hkv, Nq, (int)nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const fa::PagedKv pg{page_table, seqlens_k, max_pages_per_seq, page_size,
+                       num_pages, shift};
+  return hip_status(fa::launch_splitkv_paged(q, k_cache, v_cache, o, lse, s,
+                                             pg, out_dtype == FA_OUT_F32,
+                                             splits, workspace, stream));
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k,

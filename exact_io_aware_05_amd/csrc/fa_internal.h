@@ -101,6 +101,34 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
                           int num_splits, void* workspace,
                           hipStream_t stream);
 
+// A paged KV cache: k and v are [num_pages, page_size, Hkv, d]; sequence b
+// owns pages table[b * max_pages + 0, 1, ...] in that order and its first
+// seqlen[b] rows (clamped to max_pages * page_size); page numbers are
+// clamped into [0, num_pages).  page_size is a power of two and a multiple
+// of the 32-key block (a block never straddles two pages), and a chunk of
+// the KV-split form spans fewer than 64 pages.  Shape::Nk is then
+// max_pages * page_size.
+struct PagedKv {
+  const int* table;
+  const int* seqlen;
+  int max_pages, page_size, num_pages;
+  int page_shift;  // log2(page_size)
+};
+
+// Most 32-key blocks per chunk for pages of `page_size` keys: a chunk of
+// that many blocks holds the keys of 62 pages and, starting anywhere inside
+// a page, touches at most 63 of them (the kernel keeps the chunk's page
+// numbers one per lane of a wave).
+inline int paged_max_blocks_per_chunk(int page_size) {
+  return 62 * (page_size / kSplitKeys);
+}
+
+hipError_t launch_splitkv_paged(const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse,
+                                const Shape& s, const PagedKv& pg,
+                                bool out_f32, int num_splits, void* workspace,
+                                hipStream_t stream);
+
 size_t splitkv_workspace_bytes(long long rows, int d, int num_splits);
 
 // Backward pass: D and lse * log2(e) per query row in `workspace`, then the

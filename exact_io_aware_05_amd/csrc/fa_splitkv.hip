@@ -114,6 +114,52 @@ struct KvRegs {
     }
   }
 
+  // The same loads for a block whose rows are `rs` bytes apart starting at
+  // `kbase` / `vbase` (a page of a paged cache), of which the first
+  // `rows` exist; `koff` holds the lane offsets for that row pitch.
+  __device__ __forceinline__ void load_rows(char* kslot, const uint32_t* koff,
+                                            const uint16_t* kbase,
+                                            const uint16_t* vbase, int rows,
+                                            int rs, int h, int col) {
+    const uint32_t vrange = rows > 0 ? (uint32_t)((rows - 1) * rs + 2 * D) : 0u;
+    const __amdgpu_buffer_rsrc_t vrs = buffer_rsrc(vbase, vrange);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int off = (16 * s + 8 * h + e) * rs + 2 * CPL * col;
+        if (CPL == 4) {
+          const u32x2 x = __builtin_bit_cast(
+              u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
+          vr[s][e][0] = x[0];
+          vr[s][e][CPL / 2 - 1] = x[1];
+        } else {
+          vr[s][e][0] =
+              __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, kStreamAux);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int left = rows - RPK * i;
+      const uint32_t rem = left > 0 ? (uint32_t)((left - 1) * rs + 2 * D) : 0u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          buffer_rsrc(reinterpret_cast<const char*>(kbase) +
+                          (int64_t)RPK * i * rs,
+                      rem),
+          (lds_void*)(kslot + 1024 * i), 16, koff[i % (16 / RPK)], 0, 0,
+          kStreamAux);
+    }
+  }
+
+  // lane offsets of load_rows for rows `rs` bytes apart
+  static __device__ __forceinline__ uint32_t k_lane_off_rows(int i, int rs) {
+    constexpr int CPR = 2 * D / 16;
+    const int lane = threadIdx.x & 63;
+    const int r = lane / CPR, p = lane % CPR;
+    return (uint32_t)(r * rs + 16 * (p ^ kswz<D>(RPK * i + r)));
+  }
+
   // K operand of k-step t for lane (col, h): row kr of the block (the
   // A-operand row order realised by the bit swap), head-dimension chunk
   // (D/16) h + t (each lane half covers one contiguous half row)
@@ -143,13 +189,13 @@ struct KvRegs {
 // not from key 0.
 constexpr int kNone = 0, kCausal = 1, kBand = 2;
 
-template <int D, int MODE>
+template <int D, int MODE, bool PAGED = false>
 __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, float* __restrict__ ws_o,
-    f32x4* __restrict__ ws_ml, int Hq, int Hkv, int Nq, int Nk, float c2,
+    f32x4* __restrict__ ws_ml, int Hq, int Hkv, int Nq, int Nk_arg, float c2,
     int n_rowtiles, int num_splits, int blocks_per_split, int n_items, int wl,
-    int wr) {
+    int wr, PagedKv pg) {
   constexpr bool CAUSAL = MODE == kCausal;
   constexpr bool BAND = MODE == kBand;
   constexpr int NSTEP = D / 16;
@@ -167,6 +213,9 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   const int rt = t1 % n_rowtiles;
   const int bh = t1 / n_rowtiles;  // b * Hkv + hkv
   const int b = bh / Hkv, hkv = bh % Hkv;
+  // keys of this sequence: all of them, or (paged) its own cache length
+  const int Nk =
+      PAGED ? min(max(pg.seqlen[b], 0), pg.max_pages * pg.page_size) : Nk_arg;
   const int G = Hq / Hkv;
   const int R = Nq * G;
   const int prow = rt * 32 + col;  // packed (query, head-in-group) row
@@ -189,6 +238,10 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
 
   const uint16_t* kh = k + (int64_t)bh * Nk * D;
   const uint16_t* vh = v + (int64_t)bh * Nk * D;
+  // paged: bytes between the rows of one page and head, the chunk's first
+  // page, and its page numbers, one per lane (clamped into the cache)
+  const int rs = PAGED ? Hkv * D * 2 : 2 * D;
+  int first_page = 0, page_of_lane = 0;
   const int nblk_all = (Nk + KB - 1) / KB;
   // queries of the first and last packed rows of this tile
   const int first_q = (rt * 32) / G;
@@ -196,6 +249,13 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   const int blk_base = BAND ? max(0, first_q + off - wl) / KB : 0;
   const int blk0 = blk_base + sp * blocks_per_split;
   int blk1 = min(blk0 + blocks_per_split, nblk_all);
+  if (PAGED) {
+    first_page = (blk0 * KB) >> pg.page_shift;
+    const int pi = first_page + lane;
+    const int pv = pi < pg.max_pages ? pg.table[(int64_t)b * pg.max_pages + pi]
+                                     : 0;
+    page_of_lane = min(max(pv, 0), pg.num_pages - 1);
+  }
   if (CAUSAL || BAND) {
     // last key visible to the last packed row of this tile
     const int kv_end = min(Nk, last_q + off + (BAND ? wr : 0) + 1);
@@ -230,15 +290,33 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   char (*slots)[KV::KBYTES] = kring[wave];
   uint32_t koff[16 / KV::RPK];
 #pragma unroll
-  for (int i = 0; i < 16 / KV::RPK; ++i) koff[i] = KV::k_lane_off(i);
+  for (int i = 0; i < 16 / KV::RPK; ++i)
+    koff[i] = PAGED ? KV::k_lane_off_rows(i, rs) : KV::k_lane_off(i);
   // rows this chunk reads: up to its last block (or the causal limit)
   const int end = min(Nk, max(blk1, blk0) * KB);
   const __amdgpu_buffer_rsrc_t vrs =
       buffer_rsrc(vh, (uint32_t)max(end, 0) * (2 * D));
+  // starts the loads of block `blk` into a ring buffer and its K slot
+  auto issue = [&](KV& bf, char* slot, int blk) {
+    if (PAGED) {
+      // the block's page (the chunk spans fewer than 64 pages), then its
+      // rows inside that page
+      const int kb = blk * KB;
+      const int pslot = min(max((kb >> pg.page_shift) - first_page, 0), 63);
+      const int page = __builtin_amdgcn_readlane(page_of_lane, pslot);
+      const int64_t row0 =
+          (((int64_t)page << pg.page_shift) + (kb & (pg.page_size - 1))) *
+              Hkv * D +
+          (int64_t)hkv * D;
+      bf.load_rows(slot, koff, k + row0, v + row0, min(end - kb, KB), rs, h,
+                   col);
+    } else {
+      bf.load(slot, koff, kh, vrs, blk * KB, end, h, col);
+    }
+  };
   KV buf[PF];
 #pragma unroll
-  for (int u = 0; u < PF - 1; ++u)
-    buf[u].load(slots[u], koff, kh, vrs, (blk0 + u) * KB, end, h, col);
+  for (int u = 0; u < PF - 1; ++u) issue(buf[u], slots[u], blk0 + u);
   auto compute = [&](const KV& cur, const char* kslot, int blk) {
     const int kb = blk * KB;
     // The compiler does not order these LDS reads after the copies that
@@ -311,8 +389,8 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
     for (int u = 0; u < PF; ++u) {
       // refill the buffer the previous step consumed (past the chunk's end
       // the loads read zeros and are never used)
-      buf[(u + PF - 1) % PF].load(slots[(u + PF - 1) % PF], koff, kh, vrs,
-                                  (blk + u + PF - 1) * KB, end, h, col);
+      issue(buf[(u + PF - 1) % PF], slots[(u + PF - 1) % PF],
+            blk + u + PF - 1);
       if (blk + u < blk1) compute(buf[u], slots[u], blk + u);
     }
   }
@@ -388,10 +466,11 @@ __global__ __launch_bounds__(NT) void splitkv_merge_kernel(
     lse[row] = L > 0.f ? (Mu + __builtin_amdgcn_logf(L)) * kLn2 : -INFINITY;
 }
 
-template <int D, int MODE, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32, bool PAGED>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
                   float* lse, const Shape& s, int num_splits, void* ws,
-                  const MaskBounds& mb, hipStream_t stream) {
+                  const MaskBounds& mb, const PagedKv& pg,
+                  hipStream_t stream) {
   const int G = s.Hq / s.Hkv;
   const long long R = (long long)s.Nq * G;
   const int n_rowtiles = (int)((R + kSplitRows - 1) / kSplitRows);
@@ -405,13 +484,13 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   f32x4* ws_ml = reinterpret_cast<f32x4*>(ws_o + n_rows * num_splits * D);
   const float c2 = s.scale * kLog2e;
   const unsigned wpb = NT / 64;
-  hipLaunchKernelGGL((splitkv_partial_kernel<D, MODE>),
+  hipLaunchKernelGGL((splitkv_partial_kernel<D, MODE, PAGED>),
                      dim3((unsigned)((n_items + wpb - 1) / wpb)), dim3(NT), 0,
                      stream, static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), ws_o, ws_ml, s.Hq, s.Hkv,
                      s.Nq, s.Nk, c2, n_rowtiles, num_splits, bps,
-                     (int)n_items, mb.wl, mb.wr);
+                     (int)n_items, mb.wl, mb.wr, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((splitkv_merge_kernel<D, OUT_F32>),
@@ -420,16 +499,16 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
                     float* lse, const Shape& s, bool out_f32, int num_splits,
-                    void* ws, hipStream_t stream) {
+                    void* ws, const PagedKv& pg, hipStream_t stream) {
   const MaskBounds mb = mask_bounds(s);
-#define FA_MODE(M_)                                                        \
-  return out_f32 ? launch<D, M_, true>(q, k, v, o, lse, s, num_splits, ws,  \
-                                       mb, stream)                         \
-                 : launch<D, M_, false>(q, k, v, o, lse, s, num_splits, ws, \
-                                        mb, stream);
+#define FA_MODE(M_)                                                          \
+  return out_f32 ? launch<D, M_, true, PAGED>(q, k, v, o, lse, s, num_splits, \
+                                              ws, mb, pg, stream)            \
+                 : launch<D, M_, false, PAGED>(q, k, v, o, lse, s,           \
+                                               num_splits, ws, mb, pg, stream);
   if (mb.kind == 0) { FA_MODE(kNone) }
   if (mb.kind == 1) { FA_MODE(kCausal) }
   FA_MODE(kBand)
@@ -447,12 +526,27 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s, bool out_f32,
                           int num_splits, void* workspace,
                           hipStream_t stream) {
+  const PagedKv none{};
   if (s.d == 128)
-    return launch_d<128>(q, k, v, o, lse, s, out_f32, num_splits, workspace,
-                         stream);
+    return launch_d<128, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                                workspace, none, stream);
   if (s.d == 64)
-    return launch_d<64>(q, k, v, o, lse, s, out_f32, num_splits, workspace,
-                        stream);
+    return launch_d<64, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                               workspace, none, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitkv_paged(const void* q, const void* k_cache,
+                                const void* v_cache, void* o, float* lse,
+                                const Shape& s, const PagedKv& pg,
+                                bool out_f32, int num_splits, void* workspace,
+                                hipStream_t stream) {
+  if (s.d == 128)
+    return launch_d<128, true>(q, k_cache, v_cache, o, lse, s, out_f32,
+                               num_splits, workspace, pg, stream);
+  if (s.d == 64)
+    return launch_d<64, true>(q, k_cache, v_cache, o, lse, s, out_f32,
+                              num_splits, workspace, pg, stream);
   return hipErrorInvalidValue;
 }
 

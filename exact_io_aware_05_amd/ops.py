@@ -19,7 +19,8 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
-           "fa_fwd_varlen", "fa_fwd_window"]
+           "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged",
+           "paged_num_splits"]
 
 
 def _dims(q, k, v):
@@ -224,3 +225,63 @@ def fa_bwd(q, k, v, o, lse, do, causal=False, scale=None,
                                   _stream(q))
         check(st, "fa_bwd_window")
     return dq, dk, dv
+
+
+def paged_num_splits(B, Hq, Hkv, Nq, d, page_size, max_pages_per_seq) -> int:
+    return int(load().fa_paged_num_splits(B, Hq, Hkv, Nq, d, page_size,
+                                          max_pages_per_seq))
+
+
+def fa_fwd_paged(q, k_cache, v_cache, page_table, seqlens_k, causal=False,
+                 scale=None, window=(-1, -1), out_dtype=torch.bfloat16,
+                 num_splits=0, o=None, lse=None, workspace=None):
+    """Forward over a paged KV cache through ``fa_fwd_paged``.
+
+    q [B, Hq, Nq, d] bf16; k_cache, v_cache [num_pages, page_size, Hkv, d]
+    bf16; page_table int32 [B, max_pages_per_seq] and seqlens_k int32 [B]
+    on the device.  Returns ``(o, lse)`` shaped like ``fa_fwd``'s."""
+    if (not isinstance(q, torch.Tensor) or q.dim() != 4
+            or q.dtype != torch.bfloat16 or not q.is_cuda
+            or not q.is_contiguous()):
+        raise ValueError("q must be a contiguous bf16 device tensor "
+                         "[B, Hq, Nq, d]")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if (not isinstance(t, torch.Tensor) or t.dim() != 4
+                or t.dtype != torch.bfloat16 or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor "
+                             "[num_pages, page_size, Hkv, d]")
+    if tuple(k_cache.shape) != tuple(v_cache.shape):
+        raise ValueError("k_cache and v_cache differ in shape")
+    B, Hq, Nq, d = q.shape
+    num_pages, page_size, Hkv, dk = k_cache.shape
+    if dk != d:
+        raise ValueError("head dimensions differ")
+    for name, t, shape in (("page_table", page_table, None),
+                           ("seqlens_k", seqlens_k, (B,))):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.int32
+                or not t.is_cuda or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous int32 device tensor")
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError("page_table must be [B, max_pages_per_seq]")
+    if tuple(seqlens_k.shape) != (B,):
+        raise ValueError("seqlens_k must be [B]")
+    max_pages = page_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    splits = int(num_splits) or paged_num_splits(B, Hq, Hkv, Nq, d, page_size,
+                                                 max_pages)
+    if workspace is None:
+        need = splitkv_workspace_bytes(B, Hq, Nq, d, max(splits, 1))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                device=q.device)
+    left, right = (int(x) for x in window)
+    st = load().fa_fwd_paged(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), page_table.data_ptr(), seqlens_k.data_ptr(), B, Hq,
+        Hkv, Nq, d, num_pages, page_size, max_pages, int(bool(causal)), left,
+        right, scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, splits,
+        workspace.data_ptr(), workspace.numel(), _stream(q))
+    check(st, "fa_fwd_paged")
+    return o, lse

@@ -29,7 +29,7 @@ import numpy as np
 
 __all__ = [
     "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv", "make_dout",
-    "make_varlen", "VARLEN_PREFILL", "varlen_lengths",
+    "make_varlen", "VARLEN_PREFILL", "varlen_lengths", "make_paged",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
 ]
 
@@ -167,6 +167,27 @@ def make_varlen(seqlens_q, seqlens_k, Hq, Hkv, d, *, seed=0):
     v = rng.standard_normal((int(cu_k[-1]), Hkv, d), dtype=np.float32)
     return (f32_to_bf16_bits(q), f32_to_bf16_bits(k), f32_to_bf16_bits(v),
             cu_q, cu_k)
+
+
+def make_paged(B, Hq, Hkv, Nq, d, page_size, max_pages, seqlens, *, seed=0,
+               extra_pages=3):
+    """A paged KV cache and queries: q [B, Hq, Nq, d] and the caches
+    [num_pages, page_size, Hkv, d] as bf16 bit patterns, the int32 page
+    table [B, max_pages] and the int32 lengths.  num_pages = B * max_pages
+    + extra_pages; each sequence's pages are a seeded random draw without
+    repeats from the pool, so pages are scattered and some pages belong to
+    no sequence.  Values: N(0, 1) fp32 from ``default_rng(seed)`` (q, then
+    the K cache, then the V cache), rounded to bf16; the page permutation
+    comes from ``default_rng([seed, 0x70])``."""
+    rng = np.random.default_rng(seed)
+    num_pages = B * max_pages + extra_pages
+    q = rng.standard_normal((B, Hq, Nq, d), dtype=np.float32)
+    kc = rng.standard_normal((num_pages, page_size, Hkv, d), dtype=np.float32)
+    vc = rng.standard_normal((num_pages, page_size, Hkv, d), dtype=np.float32)
+    perm = np.random.default_rng([seed, 0x70]).permutation(num_pages)
+    table = perm[:B * max_pages].reshape(B, max_pages).astype(np.int32)
+    return (f32_to_bf16_bits(q), f32_to_bf16_bits(kc), f32_to_bf16_bits(vc),
+            table, np.asarray(seqlens, dtype=np.int32))
 
 
 # A packed prefill batch of variable-length sequences, a serving mix: the

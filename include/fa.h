@@ -151,6 +151,48 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
                   int out_dtype, hipStream_t stream);
 
 /*
+ * Forward over a paged KV cache (decode and short chunks of queries).
+ * "FlashAttention Analysis" (ryotta.opik.net), in its closing section on
+ * where the method sits, notes that paged KV caches (PagedAttention, vLLM)
+ * run the fused kernels inside; the layout below is that of common serving
+ * engines.
+ *     q        [B, Hq, Nq, d] bf16            o [B, Hq, Nq, d] (FA_OUT_*)
+ *     k_cache, v_cache  [num_pages, page_size, Hkv, d] bf16
+ *     page_table  int32 [B, max_pages_per_seq]   (DEVICE)
+ *     seqlens_k   int32 [B]                      (DEVICE)
+ *     lse      [B, Hq, Nq] fp32
+ * Sequence b owns pages page_table[b][0], [1], ... in that order: its key
+ * (value) row r is row r % page_size of page page_table[b][r / page_size],
+ * and its keys are its first seqlens_k[b] rows.  Its Nq queries attend to
+ * them as fa_fwd_window would (causal alignment at its own last key:
+ * query i sits at c = i + seqlens_k[b] - Nq; window bounds -1 for none).
+ * page_size must be a power of two, at least 32.  Offsets and page numbers
+ * are read on the device; a length is clamped to [0, max_pages_per_seq *
+ * page_size] and a page number to [0, num_pages), so bad tables give wrong
+ * results but no access outside the caches.  A sequence with no keys gets
+ * O = 0 and lse = -inf.  The KV-split form always runs (partial + merge
+ * kernels); num_splits = 0 takes fa_paged_num_splits(...), otherwise it
+ * must be 1 .. 4096 with no chunk over 62 pages of 32-key blocks
+ * (ceil(max_pages_per_seq * page_size / 32 / num_splits) <= 62 *
+ * page_size / 32).  `workspace` (16-byte aligned, device) holds at least
+ * fa_splitkv_workspace_bytes(B, Hq, Nq, d, splits) bytes.  Errors as for
+ * fa_fwd; FA_ERR_INVALID_ARG also for null or misaligned tables, a bad
+ * page_size, num_pages or max_pages_per_seq < 1, a bound below -1, a bad
+ * split count or a small workspace; FA_ERR_UNSUPPORTED when
+ * max_pages_per_seq * page_size exceeds 2^30.
+ */
+int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
+                        int max_pages_per_seq);
+
+int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
+                 void* o, float* lse, const int* page_table,
+                 const int* seqlens_k, int B, int Hq, int Hkv, int Nq, int d,
+                 int num_pages, int page_size, int max_pages_per_seq,
+                 int causal, int window_left, int window_right, float scale,
+                 int out_dtype, int num_splits, void* workspace,
+                 size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Forward over a packed batch of variable-length sequences (prefill form).
  * Sequence b has the query rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1
  * and the key/value rows cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of the

@@ -263,3 +263,43 @@ def test_bwd_window_invalid_arguments(lib, kw):
 def test_bwd_window_unsupported(lib):
     assert _bwdw(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
+
+
+def _paged(lib, **kw):
+    a = dict(q=P, kc=P, vc=P, o=P, lse=P, pt=P, sl=P, B=2, Hq=4, Hkv=2, Nq=1,
+             d=64, np_=16, ps=32, mp=8, causal=0, wl=-1, wr=-1, scale=0.125,
+             out=0, S=0, ws=P, wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_fwd_paged(a["q"], a["kc"], a["vc"], a["o"], a["lse"],
+                            a["pt"], a["sl"], a["B"], a["Hq"], a["Hkv"],
+                            a["Nq"], a["d"], a["np_"], a["ps"], a["mp"],
+                            a["causal"], a["wl"], a["wr"], a["scale"],
+                            a["out"], a["S"], a["ws"], a["wsb"], None)
+
+
+PAGED_INVALID = [
+    dict(q=None), dict(kc=P + 2), dict(vc=None), dict(o=P + 4), dict(lse=None),
+    dict(pt=None), dict(sl=None), dict(pt=P + 2), dict(sl=P + 1),
+    dict(B=0), dict(Hq=3), dict(Nq=0), dict(np_=0), dict(mp=0),
+    dict(ps=16), dict(ps=48), dict(ps=0), dict(wl=-2), dict(wr=-7),
+    dict(scale=-1.0), dict(out=5), dict(S=-1), dict(S=4097),
+    dict(ws=None), dict(ws=P + 8), dict(wsb=0),
+    # a 32-page chunk limit: 32-key pages, 1000 pages per sequence need >= 17
+    dict(mp=1000, S=16),
+]
+
+
+@pytest.mark.parametrize("kw", PAGED_INVALID, ids=lambda k: str(k))
+def test_paged_invalid_arguments(lib, kw):
+    assert _paged(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_paged_unsupported_and_splits(lib):
+    assert _paged(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _paged(lib, ps=1 << 16, mp=1 << 15) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+    # default split count: at least one chunk, none over 62 pages
+    assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 32, 1000) >= 17
+    assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 32, 1) == 1
+    assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 48, 10) == 0
+    assert lib.fa_paged_num_splits(1, 4, 2, 1, 96, 32, 10) == 0

@@ -87,12 +87,16 @@ MEASURED_TRAFFIC = {
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "881b3a4e74d869e761c2e74a075bab2a8f2056a6ba18c7b25863a5b105387021",
-        "fetch_kib": 1048897.6, "write_kib": 2112.2},
+        "sha256": "1acaafd5e45ab88efc2ce090301abffd1bbd4df094e09d001aa107b2a9f0ed79",
+        "fetch_kib": 1048893.5, "write_kib": 2112.0},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "881b3a4e74d869e761c2e74a075bab2a8f2056a6ba18c7b25863a5b105387021",
-        "fetch_kib": 132420.9, "write_kib": 2112.2},
+        "sha256": "1acaafd5e45ab88efc2ce090301abffd1bbd4df094e09d001aa107b2a9f0ed79",
+        "fetch_kib": 132403.3, "write_kib": 2112.0},
+    "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
+        "source": "fa_splitkv.hip",
+        "sha256": "1acaafd5e45ab88efc2ce090301abffd1bbd4df094e09d001aa107b2a9f0ed79",
+        "fetch_kib": 1048918.7, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",

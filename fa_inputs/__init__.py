@@ -30,6 +30,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv", "make_dout",
     "make_varlen", "VARLEN_PREFILL", "varlen_lengths", "make_paged",
+    "f32_to_e4m3", "make_fp8",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
 ]
 
@@ -188,6 +189,51 @@ def make_paged(B, Hq, Hkv, Nq, d, page_size, max_pages, seqlens, *, seed=0,
     table = perm[:B * max_pages].reshape(B, max_pages).astype(np.int32)
     return (f32_to_bf16_bits(q), f32_to_bf16_bits(kc), f32_to_bf16_bits(vc),
             table, np.asarray(seqlens, dtype=np.int32))
+
+
+def f32_to_e4m3(x) -> np.ndarray:
+    """float32 -> OCP FP8 E4M3 codes (uint8), round to nearest, ties to the
+    even code; magnitudes that round above 448 are an error (the caller
+    scales first).  Built by search over the 127 finite magnitudes, not by
+    bit manipulation."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.any(~np.isfinite(x)):
+        raise ValueError("non-finite input")
+    codes = np.arange(127)                       # 0x00 .. 0x7E
+    e, m = codes >> 3, codes & 7
+    mags = np.where(e == 0, m / 512.0, (8 + m) * np.exp2(e - 10.0))
+    a = np.abs(x)
+    if np.any(a > 464.0) or np.any(a == 464.0):
+        raise ValueError("magnitude rounds past 448")
+    hi = np.clip(np.searchsorted(mags, a), 1, 126)
+    lo = hi - 1
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    c = np.where(a >= mags[126], 126, np.where(pick_hi, hi, lo))
+    c = np.where(a <= mags[0], 0, c)
+    return (c | np.where(np.signbit(x), 0x80, 0)).astype(np.uint8)
+
+
+def make_fp8(B, Hq, Hkv, Nq, Nk, d, *, seed=0):
+    """FP8 E4M3 inputs with one fp32 descale per (batch, head): the N(0, 1)
+    fp32 draws of ``make_qkv`` (same generator and order), each head scaled
+    by its own amax / 448 (rounded to fp32) and rounded to E4M3.  Returns
+    (q8 [B, Hq, Nq, d], k8 [B, Hkv, Nk, d], vt8 [B, Hkv, d, Nk] -- V
+    transposed --, q_descale [B, Hq], k_descale [B, Hkv], v_descale
+    [B, Hkv])."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, Hq, Nq, d), dtype=np.float32)
+    k = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+    v = rng.standard_normal((B, Hkv, Nk, d), dtype=np.float32)
+
+    def quant(x):
+        amax = np.abs(x).reshape(x.shape[0], x.shape[1], -1).max(axis=2)
+        ds = (np.maximum(amax, 1e-30) / 448.0).astype(np.float32)
+        return f32_to_e4m3(x / ds[:, :, None, None].astype(np.float64)), ds
+    q8, qd = quant(q)
+    k8, kd = quant(k)
+    v8, vd = quant(v)
+    return q8, k8, np.ascontiguousarray(v8.transpose(0, 1, 3, 2)), qd, kd, vd
 
 
 # A packed prefill batch of variable-length sequences, a serving mix: the

@@ -24,7 +24,9 @@ pair, counted exactly.  ``--workload decode_window`` runs the decode workload th
 ``fa_fwd_window`` with a 4096-key window (KV split over the window's keys),
 priced at the bytes of the keys it must read.  ``--workload decode_paged`` runs ``fa_fwd_paged`` on the decode workload's
 shape stored in 256-key pages scattered over the pool, priced like the
-decode.  ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
+decode.  ``--workload gqa_prefill_fp8`` runs ``fa_fwd_fp8`` on the GQA prefill's shape
+with E4M3 inputs and reports TFLOP/s against the FP8 matrix-core peak.
+``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
 causal prompts (seeded log-uniform lengths in [256, 8192], 32768 tokens,
 the GQA heads above), priced at the causal FLOPs of each sequence.
 
@@ -46,10 +48,12 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from fa_inputs import (VARLEN_PREFILL, make_dout, make_inputs,  # noqa: E402
-                       make_paged, make_varlen, varlen_lengths, workload)
+from fa_inputs import (VARLEN_PREFILL, make_dout, make_fp8,  # noqa: E402
+                       make_inputs, make_paged, make_varlen, varlen_lengths,
+                       workload)
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
-    PEAK_BF16_MFMA_TFLOPS, PEAK_HBM_GBS, attention_bwd_flops,
+    PEAK_BF16_MFMA_TFLOPS, PEAK_FP8_MFMA_TFLOPS, PEAK_HBM_GBS,
+    attention_bwd_flops,
     attention_fwd_bytes, attention_fwd_flops, attention_window_flops,
     visible_keys)
 
@@ -57,7 +61,8 @@ METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None,
              "gqa_prefill_window": 3, "decode_window": 4,
-             "gqa_prefill_window_bwd": 3, "decode_paged": None}
+             "gqa_prefill_window_bwd": 3, "decode_paged": None,
+             "gqa_prefill_fp8": None}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
 # (and fa_bwd_window)
 WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
@@ -362,6 +367,79 @@ def bench_paged(args):
     return 0
 
 
+def bench_fp8(args):
+    """One fa_fwd_fp8 call on the GQA prefill's shape with E4M3 inputs
+    (per-head descales, V transposed), priced like the bf16 forward and
+    held against the FP8 matrix-core peak."""
+    import torch
+    from exact_io_aware_05_amd import ops
+    w = workload(3)
+    q8, k8, vt8, qd, kd, vd = make_fp8(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d,
+                                       seed=0)
+    ldv = (w.Nk + 63) // 64 * 64
+    if ldv != w.Nk:
+        pad = np.zeros(vt8.shape[:3] + (ldv,), np.uint8)
+        pad[..., :w.Nk] = vt8
+        vt8 = pad
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    Q, K, VT, QD, KD, VD = t(q8), t(k8), t(vt8), t(qd), t(kd), t(vd)
+    o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.fa_fwd_fp8(Q, K, VT, QD, KD, VD, causal=w.causal, scale=w.scale,
+                       o=o, lse=lse)
+
+    ms, kern_ms = _time_steps(step, args.steps, args.warmup,
+                              torch.cuda.current_stream())
+    flops = attention_fwd_flops(w.B, w.Hq, w.Nq, w.Nk, w.d, w.causal)
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    name = w.name + "_fp8"
+    out = {
+        "metric": f"attn fwd TFLOP/s ({name})",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) fp32, per-head amax/448 descale, "
+                "rounded to E4M3)",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "out_dtype": "bf16", "v_layout":
+                   "transposed [B, Hkv, d, Nk]",
+                   "kernel_ms": round(kern_ms, 4),
+                   "pct_fp8_mfma_peak": round(100 * achieved /
+                                              PEAK_FP8_MFMA_TFLOPS, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_FP8_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_FP8_MFMA_TFLOPS, 4),
+                     "traffic": measured_traffic(name)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import reference_attention_fp8
+        G = w.Hq // w.Hkv
+        t_total, done = 0.0, 0
+        while done < w.Hq and t_total < 10.0:
+            h = done
+            t0 = time.perf_counter()
+            reference_attention_fp8(q8[:, h:h + 1], k8[:, h // G:h // G + 1],
+                                    vt8[:, h // G:h // G + 1, :, :w.Nk],
+                                    qd[:, h:h + 1], kd[:, h // G:h // G + 1],
+                                    vd[:, h // G:h // G + 1], causal=w.causal,
+                                    scale=float(np.float32(w.scale)))
+            t_total += time.perf_counter() - t0
+            done += 1
+        out["cpu_baseline"] = {
+            "value": round(attention_fwd_flops(1, done, w.Nq, w.Nk, w.d,
+                                               w.causal) / t_total / 1e12, 6),
+            "unit": "TFLOP/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
+                      f"float64 numpy on the decoded inputs; {t_total:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -393,6 +471,8 @@ def main(argv=None):
         return bench_varlen(args)
     if args.workload == "decode_paged":
         return bench_paged(args)
+    if args.workload == "gqa_prefill_fp8":
+        return bench_fp8(args)
     w = workload(WORKLOADS[args.workload])
     backward = args.workload.endswith("_bwd")
     window = WINDOWS.get(args.workload)

@@ -35,6 +35,8 @@ SIGNATURES = {
     "fa_fwd_paged": (_c_int, [_vp] * 7 + [_c_int] * 11 + [_c_float, _c_int,
                                                            _c_int, _vp,
                                                            _c_size, _vp]),
+    "fa_fwd_fp8": (_c_int, [_vp] * 8 + [_c_int] * 8 + [_c_float, _c_int,
+                                                       _vp]),
     "fa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_c_float, _c_int,
                                                            _vp]),
     "fa_bwd_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),

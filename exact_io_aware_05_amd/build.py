@@ -20,12 +20,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfa.so")
 BUILD_DIR = os.path.join(PKG, "_build")
-SOURCES = ("fa_api.hip", "fa_prefill.hip", "fa_splitkv.hip", "fa_backward.hip")
+SOURCES = ("fa_api.hip", "fa_prefill.hip", "fa_splitkv.hip", "fa_backward.hip",
+           "fa_prefill_fp8.hip")
 # Kernel sources never produce NaN from valid inputs; -fno-honor-nans lets
 # fmaxf map to v_max_f32 without canonicalising its operands.  The host
 # validation layer (fa_api.hip) must keep NaN semantics for its checks.
 EXTRA = {"fa_prefill.hip": ["-fno-honor-nans"], "fa_splitkv.hip": ["-fno-honor-nans"],
-         "fa_backward.hip": ["-fno-honor-nans"]}
+         "fa_backward.hip": ["-fno-honor-nans"],
+         "fa_prefill_fp8.hip": ["-fno-honor-nans"]}
 ARCH = "gfx950"
 
 

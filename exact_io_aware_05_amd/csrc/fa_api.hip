@@ -277,6 +277,35 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                                              splits, workspace, stream));
 }
 
+int fa_fwd_fp8(const void* q, const void* k, const void* vt,
+               const float* q_descale, const float* k_descale,
+               const float* v_descale, void* o, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nk, int ldv, int d, int causal,
+               float scale, int out_dtype, hipStream_t stream) {
+  int st = check_common(q, k, vt, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  if (!q_descale || !k_descale || !v_descale ||
+      (reinterpret_cast<uintptr_t>(q_descale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(k_descale) & 3u) ||
+      (reinterpret_cast<uintptr_t>(v_descale) & 3u))
+    return FA_ERR_INVALID_ARG;
+  if (ldv < Nk || ldv % 64 != 0) return FA_ERR_INVALID_ARG;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  // one head of K and of V^T is addressed with 32-bit byte offsets
+  if ((long long)Nk * d > (1LL << 31) - 1 ||
+      (long long)ldv * d > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  return hip_status(fa::launch_prefill_fp8(q, k, vt, q_descale, k_descale,
+                                           v_descale, o, lse, s, ldv,
+                                           out_dtype == FA_OUT_F32, stream));
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k,

@@ -96,6 +96,14 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           const SeqLayout& lay, bool out_f32,
                           hipStream_t stream);
 
+// FP8 (E4M3) prefill, d = 128: q [B, Hq, Nq, d], k [B, Hkv, Nk, d], vt
+// [B, Hkv, d, ldv] codes; descales per (batch, head) on the device.
+hipError_t launch_prefill_fp8(const void* q, const void* k, const void* vt,
+                              const float* q_descale, const float* k_descale,
+                              const float* v_descale, void* o, float* lse,
+                              const Shape& s, int ldv, bool out_f32,
+                              hipStream_t stream);
+
 hipError_t launch_splitkv(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s, bool out_f32,
                           int num_splits, void* workspace,

@@ -10,6 +10,7 @@ from __future__ import annotations
 
 # MI355X published peaks (dense, no structured sparsity).
 PEAK_BF16_MFMA_TFLOPS = 2500.0     # bf16 / fp16 dense matrix-core peak
+PEAK_FP8_MFMA_TFLOPS = 5000.0      # fp8 dense matrix-core peak
 PEAK_HBM_GBS = 8000.0              # HBM3E bandwidth
 PEAK_FP32_VECTOR_TFLOPS = 157.3
 

@@ -20,7 +20,7 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
            "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged",
-           "paged_num_splits"]
+           "paged_num_splits", "fa_fwd_fp8"]
 
 
 def _dims(q, k, v):
@@ -284,4 +284,42 @@ def fa_fwd_paged(q, k_cache, v_cache, page_table, seqlens_k, causal=False,
         FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, splits,
         workspace.data_ptr(), workspace.numel(), _stream(q))
     check(st, "fa_fwd_paged")
+    return o, lse
+
+
+def fa_fwd_fp8(q8, k8, vt8, q_descale, k_descale, v_descale, causal=False,
+               scale=None, out_dtype=torch.bfloat16, o=None, lse=None):
+    """FP8 (E4M3) forward through ``fa_fwd_fp8``.
+
+    q8 [B, Hq, Nq, d], k8 [B, Hkv, Nk, d] and vt8 [B, Hkv, d, ldv] (V
+    transposed, ldv >= Nk a multiple of 64) are uint8 device tensors of
+    E4M3 codes; the descales are fp32 device tensors [B, Hq], [B, Hkv],
+    [B, Hkv].  Returns ``(o, lse)`` shaped like ``fa_fwd``'s."""
+    for name, t in (("q8", q8), ("k8", k8), ("vt8", vt8)):
+        if (not isinstance(t, torch.Tensor) or t.dim() != 4
+                or t.dtype != torch.uint8 or not t.is_cuda
+                or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous uint8 device "
+                             "tensor of E4M3 codes")
+    B, Hq, Nq, d = q8.shape
+    Bk, Hkv, Nk, dk = k8.shape
+    if Bk != B or dk != d or tuple(vt8.shape[:3]) != (B, Hkv, d):
+        raise ValueError("shape mismatch between q8, k8 and vt8")
+    ldv = vt8.shape[3]
+    for name, t, shape in (("q_descale", q_descale, (B, Hq)),
+                           ("k_descale", k_descale, (B, Hkv)),
+                           ("v_descale", v_descale, (B, Hkv))):
+        if (not isinstance(t, torch.Tensor) or t.dtype != torch.float32
+                or not t.is_cuda or not t.is_contiguous()
+                or tuple(t.shape) != shape):
+            raise ValueError(f"{name} must be a contiguous fp32 device "
+                             f"tensor {shape}")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q8, B, Hq, Nq, d, out_dtype, o, lse)
+    st = load().fa_fwd_fp8(
+        q8.data_ptr(), k8.data_ptr(), vt8.data_ptr(), q_descale.data_ptr(),
+        k_descale.data_ptr(), v_descale.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), B, Hq, Hkv, Nq, Nk, ldv, d, int(bool(causal)), scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q8))
+    check(st, "fa_fwd_fp8")
     return o, lse

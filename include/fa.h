@@ -126,6 +126,34 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d);
 
 /*
+ * Forward on FP8 inputs ("FlashAttention-2 (KO)", systems-analysis.info,
+ * comparison with later versions: 8-bit floating point for extra speed;
+ * "FlashAttention Analysis", ryotta.opik.net, evolution by generation:
+ * FlashAttention-3's FP8 low-precision path).  Inputs are OCP FP8 E4M3
+ * codes (1 byte each) with one fp32 descale factor per (batch, head); the
+ * real inputs are code value * descale:
+ *     q  [B, Hq,  Nq, d]      q_descale [B, Hq]    (DEVICE, fp32, > 0)
+ *     k  [B, Hkv, Nk, d]      k_descale [B, Hkv]
+ *     vt [B, Hkv, d, ldv]     v_descale [B, Hkv]   (V TRANSPOSED)
+ *     o  [B, Hq,  Nq, d] bf16 or fp32, lse [B, Hq, Nq] fp32
+ * ldv >= Nk is a multiple of 64; keys Nk .. ldv - 1 of vt are padding and
+ * must hold finite codes (they get zero weight).  Mask, GQA mapping and
+ * scale as for fa_fwd; d must be 128.  Both products run on the 8-bit
+ * matrix cores: S = scale q k^T from the E4M3 codes, and P V with the
+ * weights rounded to E4M3 (normalised by the fp32 sum of the unrounded
+ * weights), so O carries the error of 8-bit weights (a relative 2^-4 per
+ * weight) on top of the inputs' own quantisation; lse is computed in fp32
+ * from the unrounded weights.  Errors as for fa_fwd; FA_ERR_INVALID_ARG
+ * also for null or misaligned descale arrays or a bad ldv;
+ * FA_ERR_UNSUPPORTED for d != 128.
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* vt,
+               const float* q_descale, const float* k_descale,
+               const float* v_descale, void* o, float* lse, int B, int Hq,
+               int Hkv, int Nq, int Nk, int ldv, int d, int causal,
+               float scale, int out_dtype, hipStream_t stream);
+
+/*
  * Forward with a sliding-window mask (the training-cost guide,
  * tool.smithlab.co.kr, FAQ: sliding windows are among the mask features of
  * the fused kernels).  Query i, placed at c = i + Nk - Nq on the key axis

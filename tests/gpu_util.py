@@ -74,3 +74,38 @@ def compare_grad(g, ref, tol=GRAD_TOL, atol=GRAD_ATOL, what=""):
             f"{what}: max |err| = {err:.3e} > {tol} * {scale:.3e} + {atol} at "
             f"{tuple(map(int, idx))}: got {g[idx]:.6f}, oracle {ref[idx]:.6f}")
     return err / scale if scale > 0 else err
+
+
+# FP8 forward: per-element tolerance derived from its arithmetic.  The
+# kernel rounds each weight W_j to E4M3 (round to nearest even: an error
+# uniform over one spacing of the E4M3 grid at W_j, 2^(floor(log2 W) - 3)
+# for W >= 2^-6 and 2^-9 below), in a frame where the row's largest weight
+# is at least 16, and normalises by the fp32 sum of the unrounded weights;
+# the scores carry the 8-bit matrix cores' accumulation error (measured
+# below 2^-13 of the sum of the magnitudes of the products; 2^-11 is
+# used).  The rounding errors are independent and zero-mean, so the error
+# of O_i,c is a sum of independent terms with standard deviation
+#     sigma = sqrt(sum_j (spacing_j^2 / 12 + (dS_j W_j)^2) v_j,c^2) / sum_j W_j
+# and the test allows 6 sigma (plus 1e-6 for fp32 sums).  lse is built from
+# the unrounded weights: its error is bounded by the largest score error.
+FP8_SIGMAS = 6.0
+FP8_MFMA_REL = 2.0 ** -11
+
+
+def e4m3_spacing(w):
+    w = np.asarray(w, dtype=np.float64)
+    e = np.floor(np.log2(np.maximum(w, 2.0 ** -6)))
+    return np.where(w >= 2.0 ** -6, 2.0 ** (e - 3), 2.0 ** -9)
+
+
+def fp8_tolerance(P, v, dS):
+    """P [R, Nk] row probabilities (oracle), v [Nk, d] real values, dS
+    [R, Nk] bound on each score's error (natural-log units).  Returns the
+    per-element tolerance [R, d] of O and the per-row bound [R] of lse."""
+    pmax = P.max(axis=1, keepdims=True)
+    W = np.where(pmax > 0, 16.0 * P / np.where(pmax > 0, pmax, 1.0), 0.0)
+    var = np.where(W > 0, e4m3_spacing(W) ** 2 / 12.0 + (dS * W) ** 2, 0.0)
+    sig = np.sqrt(var @ (v * v)) / np.maximum(W.sum(axis=1, keepdims=True),
+                                               1e-300)
+    lse_bound = np.where(P > 0, dS, 0.0).max(axis=1) + 1e-5
+    return FP8_SIGMAS * sig + 1e-6, lse_bound

@@ -303,3 +303,32 @@ def test_paged_unsupported_and_splits(lib):
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 32, 1) == 1
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 48, 10) == 0
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 96, 32, 10) == 0
+
+
+def _fp8(lib, **kw):
+    a = dict(q=P, k=P, vt=P, qd=P, kd=P, vd=P, o=P, lse=P, B=1, Hq=4, Hkv=2,
+             Nq=16, Nk=16, ldv=64, d=128, causal=0, scale=0.125, out=0)
+    a.update(kw)
+    return lib.fa_fwd_fp8(a["q"], a["k"], a["vt"], a["qd"], a["kd"], a["vd"],
+                          a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"],
+                          a["Nq"], a["Nk"], a["ldv"], a["d"], a["causal"],
+                          a["scale"], a["out"], None)
+
+
+FP8_INVALID = [
+    dict(q=None), dict(k=P + 8), dict(vt=None), dict(o=P + 2), dict(lse=None),
+    dict(qd=None), dict(kd=P + 2), dict(vd=None), dict(B=0), dict(Hq=3),
+    dict(Nq=0), dict(Nk=0), dict(ldv=8), dict(ldv=65), dict(Nk=65, ldv=64),
+    dict(scale=math.nan), dict(out=7),
+]
+
+
+@pytest.mark.parametrize("kw", FP8_INVALID, ids=lambda k: str(k))
+def test_fp8_invalid_arguments(lib, kw):
+    assert _fp8(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_fp8_unsupported(lib):
+    assert _fp8(lib, d=64) == _lib.FA_ERR_UNSUPPORTED
+    assert _fp8(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0

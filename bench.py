@@ -89,6 +89,10 @@ MEASURED_TRAFFIC = {
         "source": "fa_prefill.hip",
         "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
         "fetch_kib": 67574.9, "write_kib": 66560.2},
+    "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
+        "source": "fa_prefill_fp8.hip",
+        "sha256": "33d71c45690d58cf5b66d4391cc8ffa33d06f4507deed0898e04e71093e312ae",
+        "fetch_kib": 33947.1, "write_kib": 66561.8},
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",

@@ -306,6 +306,48 @@ int fa_fwd_fp8(const void* q, const void* k, const void* vt,
                                            out_dtype == FA_OUT_F32, stream));
 }
 
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   const long long* q_stride, const long long* k_stride,
+                   const long long* v_stride, const long long* o_stride,
+                   int causal, int window_left, int window_right, float scale,
+                   int out_dtype, hipStream_t stream) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  if (!q_stride || !k_stride || !v_stride || !o_stride)
+    return FA_ERR_INVALID_ARG;
+  // every row starts on a 16-byte boundary: strides are multiples of 8
+  // elements, and a row holds d elements
+  const long long* all[4] = {q_stride, k_stride, v_stride, o_stride};
+  for (const long long* t : all)
+    for (int i = 0; i < 3; ++i)
+      if (t[i] < 0 || t[i] % 8 != 0 || t[i] > (1LL << 40))
+        return FA_ERR_INVALID_ARG;
+  if (q_stride[2] < d || k_stride[2] < d || v_stride[2] < d ||
+      o_stride[2] < d)
+    return FA_ERR_INVALID_ARG;
+  // one head of K and of V is addressed with 32-bit byte offsets
+  if (((long long)Nk - 1) * k_stride[2] * 2 + 2LL * d > (1LL << 31) - 1 ||
+      ((long long)Nk - 1) * v_stride[2] * 2 + 2LL * d > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
+  fa::SeqLayout lay = fa::dense_layout(s);  // lse dense [B, Hq, Nq]
+  lay.q_b = q_stride[0]; lay.q_h = q_stride[1]; lay.q_r = q_stride[2];
+  lay.k_b = k_stride[0]; lay.k_h = k_stride[1]; lay.k_r = k_stride[2];
+  lay.v_b = v_stride[0]; lay.v_h = v_stride[1]; lay.v_r = v_stride[2];
+  lay.o_b = o_stride[0]; lay.o_h = o_stride[1]; lay.o_r = o_stride[2];
+  return hip_status(fa::launch_prefill(q, k, v, o, lse, s, lay,
+                                       out_dtype == FA_OUT_F32, stream));
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k,
@@ -343,6 +385,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
   lay.total_q = total_q;
   lay.total_k = total_k;
   lay.n_seq = B;
+  fa::same_vo(lay);
   return hip_status(fa::launch_prefill(q, k, v, o, lse, s, lay,
                                        out_dtype == FA_OUT_F32, stream));
 }

@@ -53,11 +53,11 @@ inline int band_tile_blocks(const Shape& s, const MaskBounds& m, int kb) {
 }
 
 // Where the rows of one (sequence, head) live, in elements: batch, head and
-// row strides of Q and O (same shape), of K and V, and of lse.  Fixed-length
-// batches have cu_q = cu_k = nullptr.  Packed variable-length batches take
-// sequence b's rows from cu_q[b] .. cu_q[b + 1] (and cu_k for K/V), the
-// batch stride unused; Nq / Nk of the Shape are then the maximum lengths and
-// total_q / total_k the row counts of the packed tensors.
+// row strides of Q, K, V, O and of lse.  Fixed-length batches have cu_q =
+// cu_k = nullptr.  Packed variable-length batches take sequence b's rows
+// from cu_q[b] .. cu_q[b + 1] (and cu_k for K/V), the batch strides unused;
+// Nq / Nk of the Shape are then the maximum lengths and total_q / total_k
+// the row counts of the packed tensors.
 struct SeqLayout {
   long long q_b, q_h, q_r;
   long long k_b, k_h, k_r;
@@ -66,7 +66,19 @@ struct SeqLayout {
   const int* cu_k;
   int total_q, total_k;
   int n_seq;  // sequences of a packed batch (cu_q, cu_k: n_seq + 1 entries)
+  long long v_b, v_h, v_r;  // V (same as K unless given apart)
+  long long o_b, o_h, o_r;  // O (same as Q unless given apart)
 };
+
+// V laid out like K and O like Q.
+inline void same_vo(SeqLayout& l) {
+  l.v_b = l.k_b;
+  l.v_h = l.k_h;
+  l.v_r = l.k_r;
+  l.o_b = l.q_b;
+  l.o_h = l.q_h;
+  l.o_r = l.q_r;
+}
 
 // [B, H, N, d] contiguous tensors, lse [B, Hq, Nq].
 inline SeqLayout dense_layout(const Shape& s) {
@@ -80,6 +92,7 @@ inline SeqLayout dense_layout(const Shape& s) {
   l.l_r = 1;
   l.l_h = s.Nq;
   l.l_b = (long long)s.Hq * s.Nq;
+  same_vo(l);
   return l;
 }
 

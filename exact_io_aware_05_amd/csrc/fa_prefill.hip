@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 
   // this sequence's rows: element offsets of its row 0 in this head
   int Nq = Nq_max, Nk = Nk_max;
-  int64_t qbase, kbase, lbase;
+  int64_t qbase, kbase, vbase, obase, lbase;
   if (lay.cu_q) {
     // packed variable-length batch; lengths clamped into the packed
     // tensors whatever the offsets hold
@@ -389,19 +389,24 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     Nk = min(min(max(lay.cu_k[b + 1] - ks, 0), lay.total_k - ks), Nk_max);
     qbase = qs * lay.q_r + hq * lay.q_h;
     kbase = ks * lay.k_r + hkv * lay.k_h;
+    vbase = ks * lay.v_r + hkv * lay.v_h;
+    obase = qs * lay.o_r + hq * lay.o_h;
     lbase = qs * lay.l_r + hq * lay.l_h;
   } else {
     qbase = b * lay.q_b + hq * lay.q_h;
     kbase = b * lay.k_b + hkv * lay.k_h;
+    vbase = b * lay.v_b + hkv * lay.v_h;
+    obase = b * lay.o_b + hq * lay.o_h;
     lbase = b * lay.l_b + hq * lay.l_h;
   }
   // a Q block past this sequence's rows has nothing to do (the test is
   // uniform over the workgroup, so no wave is left at a barrier)
   if (q0 >= Nq) return;
   const int off = Nk - Nq;
-  const int rsb = (int)(2 * lay.k_r);  // bytes between K (V) rows
+  const int rsb = (int)(2 * lay.k_r);   // bytes between K rows
+  const int rsbv = (int)(2 * lay.v_r);  // bytes between V rows
   const char* kh = reinterpret_cast<const char*>(k + kbase);
-  const char* vh = reinterpret_cast<const char*>(v + kbase);
+  const char* vh = reinterpret_cast<const char*>(v + vbase);
 
   int kv_end = Nk;
   if (CAUSAL) kv_end = min(Nk, q0 + BR + off);
@@ -435,9 +440,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   {
     const int row = lane / (L::ROWB / 16);   // row within the KiB
     const int p = lane % (L::ROWB / 16);     // physical 16-byte chunk
-    v_off = (uint32_t)(row * rsb) + ((p ^ (vswz<D>(row) >> 1)) * 16);
+    v_off = (uint32_t)(row * rsbv) + ((p ^ (vswz<D>(row) >> 1)) * 16);
   }
-  const int v_step = (1024 / L::ROWB) * rsb;  // rows of one KiB
+  const int v_step = (1024 / L::ROWB) * rsbv;  // rows of one KiB
 
   // ---- Q^T operand fragments: lane holds q[row][16t + 8h .. +7]
   const int qrow = wrow0 + col;
@@ -515,7 +520,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     copy_block<D>(smem + ((j + 3) % L::NS) * L::KBYTES, kh, kv_rows, j + 3,
                   wave, k_off, 16, rsb);
     copy_block<D>(smem + L::VBASE + ((j + 2) % L::NS) * L::VBYTES, vh,
-                  kv_rows, j + 2, wave, v_off, v_step, rsb);
+                  kv_rows, j + 2, wave, v_off, v_step, rsbv);
   };
   // prologue: K_j0, K_j0+1, K_j0+2, V_j0, V_j0+1 (all waves), fully
   // waited (j0 = 0 unless a band starts later).  The V stage before j0 is
@@ -528,7 +533,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 #pragma unroll
   for (int b0 = 0; b0 < 2; ++b0)
     copy_block<D>(smem + L::VBASE + ((j0 + b0) % L::NS) * L::VBYTES, vh,
-                  kv_rows, j0 + b0, wave, v_off, v_step, rsb);
+                  kv_rows, j0 + b0, wave, v_off, v_step, rsbv);
 #pragma unroll
   for (int i = tid; i < L::VBYTES / 16; i += NT)
     reinterpret_cast<u32x4*>(smem + L::VBASE +
@@ -575,7 +580,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   const float lse_v =
       lt > 0.f ? (st.m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
   if (qrow < Nq) {
-    const int64_t orow = qbase + qrow * lay.q_r;
+    const int64_t orow = obase + qrow * lay.o_r;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
 #pragma unroll

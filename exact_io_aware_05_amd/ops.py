@@ -20,7 +20,7 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
            "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged",
-           "paged_num_splits", "fa_fwd_fp8"]
+           "paged_num_splits", "fa_fwd_fp8", "fa_fwd_strided"]
 
 
 def _dims(q, k, v):
@@ -322,4 +322,48 @@ def fa_fwd_fp8(q8, k8, vt8, q_descale, k_descale, v_descale, causal=False,
         lse.data_ptr(), B, Hq, Hkv, Nq, Nk, ldv, d, int(bool(causal)), scale,
         FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q8))
     check(st, "fa_fwd_fp8")
+    return o, lse
+
+
+def fa_fwd_strided(q, k, v, causal=False, scale=None, window=(-1, -1),
+                   out_dtype=torch.bfloat16, o=None, lse=None):
+    """Forward through ``fa_fwd_strided`` on 4-D bf16 views indexed
+    [B, H, N, d] (any strides, head dimension contiguous, strides multiples
+    of 8); ``o`` may be a strided view too (default: a new contiguous
+    tensor).  Returns ``(o, lse)``."""
+    import ctypes
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if (not isinstance(t, torch.Tensor) or t.dim() != 4
+                or t.dtype != torch.bfloat16 or not t.is_cuda
+                or t.stride(3) != 1):
+            raise ValueError(f"{name} must be a bf16 device tensor viewed as "
+                             "[B, H, N, d] with the head dimension contiguous")
+    B, Hq, Nq, d = q.shape
+    Bk, Hkv, Nk, dk = k.shape
+    if tuple(v.shape) != tuple(k.shape) or Bk != B or dk != d:
+        raise ValueError("shape mismatch between q, k and v")
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("out_dtype must be torch.bfloat16 or torch.float32")
+    if o is None:
+        o = torch.empty((B, Hq, Nq, d), dtype=out_dtype, device=q.device)
+    elif (o.dtype != out_dtype or tuple(o.shape) != (B, Hq, Nq, d)
+          or o.stride(3) != 1):
+        raise ValueError("o has the wrong dtype, shape or layout")
+    if lse is None:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    elif (lse.dtype != torch.float32 or tuple(lse.shape) != (B, Hq, Nq)
+          or not lse.is_contiguous()):
+        raise ValueError("lse has the wrong dtype, shape or layout")
+    arr = lambda t: (ctypes.c_longlong * 3)(t.stride(0), t.stride(1),
+                                            t.stride(2))
+    qs, ks, vs, os_ = arr(q), arr(k), arr(v), arr(o)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    left, right = (int(x) for x in window)
+    st = load().fa_fwd_strided(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), B, Hq, Hkv, Nq, Nk, d, ctypes.addressof(qs),
+        ctypes.addressof(ks), ctypes.addressof(vs), ctypes.addressof(os_),
+        int(bool(causal)), left, right, scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
+    check(st, "fa_fwd_strided")
     return o, lse

@@ -179,6 +179,27 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
                   int out_dtype, hipStream_t stream);
 
 /*
+ * Forward on strided tensors (views such as slices of a fused QKV
+ * projection, [B, N, H, d] layouts, padded rows).  Each of q, k, v and o
+ * is described by its element strides {batch, head, row} (a host array of
+ * three), the head dimension contiguous: element (b, h, i, c) of q is
+ * q[b * q_stride[0] + h * q_stride[1] + i * q_stride[2] + c].  Strides are
+ * multiples of 8 (every row 16-byte aligned), row strides at least d; o's
+ * strides must give each (b, h, i) its own d elements.  lse is dense
+ * [B, Hq, Nq].  Semantics, masks (causal flag and window bounds as for
+ * fa_fwd_window) and status codes as for fa_fwd_window; the tiled prefill
+ * kernel always runs.  FA_ERR_INVALID_ARG also for a null stride array or
+ * a bad stride; FA_ERR_UNSUPPORTED when one head of K or V spans 2^31
+ * bytes or more ((Nk - 1) * row stride * 2 + 2d).
+ */
+int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   const long long* q_stride, const long long* k_stride,
+                   const long long* v_stride, const long long* o_stride,
+                   int causal, int window_left, int window_right, float scale,
+                   int out_dtype, hipStream_t stream);
+
+/*
  * Forward over a paged KV cache (decode and short chunks of queries).
  * "FlashAttention Analysis" (ryotta.opik.net), in its closing section on
  * where the method sits, notes that paged KV caches (PagedAttention, vLLM)

@@ -332,3 +332,41 @@ def test_fp8_unsupported(lib):
     assert _fp8(lib, d=64) == _lib.FA_ERR_UNSUPPORTED
     assert _fp8(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
+
+
+def _strided(lib, **kw):
+    import ctypes
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=4, Hkv=2, Nq=16, Nk=16, d=64,
+             qs=(4096, 1024, 64), ks=(2048, 1024, 64), vs=(2048, 1024, 64),
+             os_=(4096, 1024, 64), causal=0, wl=-1, wr=-1, scale=0.125, out=0)
+    a.update(kw)
+    arr = lambda t: None if t is None else ctypes.addressof((ctypes.c_longlong * 3)(*t))
+    keep = [(ctypes.c_longlong * 3)(*t) if t is not None else None
+            for t in (a["qs"], a["ks"], a["vs"], a["os_"])]
+    ptrs = [ctypes.addressof(x) if x is not None else None for x in keep]
+    return lib.fa_fwd_strided(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                              a["B"], a["Hq"], a["Hkv"], a["Nq"], a["Nk"],
+                              a["d"], *ptrs, a["causal"], a["wl"], a["wr"],
+                              a["scale"], a["out"], None)
+
+
+STRIDED_INVALID = INVALID + [
+    dict(qs=None), dict(os_=None), dict(ks=(2048, 1024, 60)),
+    dict(vs=(2048, 4, 64)), dict(qs=(-8, 1024, 64)), dict(os_=(4096, 1024, 32)),
+    dict(wl=-2),
+]
+
+
+@pytest.mark.parametrize("kw", STRIDED_INVALID, ids=lambda k: str(k))
+def test_strided_invalid_arguments(lib, kw):
+    assert _strided(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_strided_unsupported(lib):
+    assert _strided(lib, d=96, qs=(4096, 1024, 96), ks=(2048, 1024, 96),
+                    vs=(2048, 1024, 96), os_=(4096, 1024, 96)) == \
+        _lib.FA_ERR_UNSUPPORTED
+    # one K head spans (Nk - 1) * row stride * 2 + 2d bytes
+    assert _strided(lib, Nk=(1 << 16) + 2, ks=(0, 0, 1 << 14)) == \
+        _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0

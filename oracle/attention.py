@@ -47,13 +47,20 @@ Readings where the pages are silent (each is a documented choice):
   negative bound is no bound on that side.  ``(-1, 0)`` is the causal mask,
   ``(-1, -1)`` no mask; the window combines with ``causal`` by intersection.
   Rows whose window holds no key get O = 0 and lse = -inf.
+* Block-sparse attention ("FlashAttention Analysis", results of
+  FlashAttention-1: extended with a block-sparse pattern, only the non-zero
+  blocks of a mask are computed, an approximation faster than the exact
+  one; the pages give no block size or mask format): ``block_mask`` [B, Hq, nqb, nkb] (or
+  broadcastable) with blocks of ``block_size = (bq, bk)`` query rows and
+  keys; key j is visible to query i only if block (i // bq, j // bk) is
+  non-zero, intersected with the causal flag and any window.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "visible_mask", "kv_head_of", "reference_attention",
+    "visible_mask", "block_visible", "kv_head_of", "reference_attention",
     "tiled_online_attention", "splitkv_partials", "merge_partials",
     "splitkv_attention", "split_bounds",
 ]
@@ -85,6 +92,16 @@ def visible_mask(rows, cols, Nq: int, Nk: int, causal: bool,
     return vis
 
 
+def block_visible(rows, cols, block_mask_bh, block_size) -> np.ndarray:
+    """Boolean [len(rows), len(cols)] of one head's block mask: block
+    (i // bq, j // bk) non-zero."""
+    bq, bk = block_size
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    bm = np.asarray(block_mask_bh) != 0
+    return bm[(rows // bq)[:, None], (cols // bk)[None, :]]
+
+
 def _check(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B, H, N, d]")
@@ -96,7 +113,8 @@ def _check(q, k, v):
 
 
 def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
-                        return_sp: bool = False, window=None):
+                        return_sp: bool = False, window=None, block_mask=None,
+                        block_size=(256, 64)):
     """The definition, with S and P materialised per head in float64.
 
     S[i, j] = scale * sum_c q[i, c] k[j, c], set to -inf where key j is not
@@ -104,7 +122,9 @@ def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
     row i of S.  ``rows`` restricts the computation to some query rows (the
     result then has ``len(rows)`` rows); ``return_sp`` also returns the
     per-head S and P arrays (shape [B, Hq, rows, Nk]).  ``window`` adds the
-    sliding-window bounds (left, right) of ``visible_mask``.
+    sliding-window bounds (left, right) of ``visible_mask``; ``block_mask``
+    ([B, Hq, nqb, nkb], broadcastable) keeps only the keys of non-zero
+    blocks of ``block_size`` (query rows, keys).
     """
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -115,11 +135,18 @@ def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
     if return_sp:
         S_all = np.empty((B, Hq, R, Nk))
         P_all = np.empty((B, Hq, R, Nk))
+    if block_mask is not None:
+        block_mask = np.broadcast_to(np.asarray(block_mask),
+                                     (B, Hq) + np.shape(block_mask)[2:])
     for b in range(B):
         for h in range(Hq):
             hk = kv_head_of(h, Hq, Hkv)
             S = scale * (q[b, h, rows] @ k[b, hk].T)
-            S = np.where(vis, S, -np.inf)
+            vis_bh = vis
+            if block_mask is not None:
+                vis_bh = vis & block_visible(rows, np.arange(Nk),
+                                             block_mask[b, h], block_size)
+            S = np.where(vis_bh, S, -np.inf)
             m = S.max(axis=1)
             has = np.isfinite(m)
             m0 = np.where(has, m, 0.0)

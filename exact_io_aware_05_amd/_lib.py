@@ -39,6 +39,8 @@ SIGNATURES = {
                                                        _vp]),
     "fa_fwd_strided": (_c_int, [_vp] * 5 + [_c_int] * 6 + [_vp] * 4 +
                        [_c_int] * 3 + [_c_float, _c_int, _vp]),
+    "fa_fwd_block_sparse": (_c_int, [_vp] * 6 + [ctypes.c_longlong] * 2 +
+                            [_c_int] * 7 + [_c_float, _c_int, _vp]),
     "fa_fwd_varlen": (_c_int, [_vp] * 7 + [_c_int] * 9 + [_c_float, _c_int,
                                                            _vp]),
     "fa_bwd_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int]),

@@ -348,6 +348,31 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
                                        out_dtype == FA_OUT_F32, stream));
 }
 
+int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
+                        float* lse, const unsigned char* block_mask,
+                        long long mask_batch_stride, long long mask_head_stride,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        int causal, float scale, int out_dtype,
+                        hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  if (!block_mask || mask_batch_stride < 0 || mask_head_stride < 0)
+    return FA_ERR_INVALID_ARG;
+  const int nkb = (Nk + fa::kPrefillKeys - 1) / fa::kPrefillKeys;
+  if (nkb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  const fa::BlockMask bm{block_mask, mask_batch_stride, mask_head_stride, nkb};
+  return hip_status(fa::launch_prefill_sparse(q, k, v, o, lse, s, bm,
+                                              out_dtype == FA_OUT_F32,
+                                              stream));
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k,

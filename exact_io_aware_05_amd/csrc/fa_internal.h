@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa {
 
@@ -108,6 +109,23 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s,
                           const SeqLayout& lay, bool out_f32,
                           hipStream_t stream);
+
+// Block-sparse mask of the prefill kernel: one byte per (block of
+// kSparseRows query rows, block of kPrefillKeys keys), rows of nkb bytes;
+// head h of batch b starts at mask + b * mb + h * mh (strides may be 0 to
+// share a mask).  A zero byte skips the block.
+constexpr int kSparseRows = 128;
+constexpr int kSparseMaxKeyBlocks = 8191;  // the key-block list fills LDS
+struct BlockMask {
+  const uint8_t* mask;
+  long long mb, mh;
+  int nkb;
+};
+
+hipError_t launch_prefill_sparse(const void* q, const void* k, const void* v,
+                                 void* o, float* lse, const Shape& s,
+                                 const BlockMask& bm, bool out_f32,
+                                 hipStream_t stream);
 
 // FP8 (E4M3) prefill, d = 128: q [B, Hq, Nq, d], k [B, Hkv, Nk, d], vt
 // [B, Hkv, d, ldv] codes; descales per (batch, head) on the device.

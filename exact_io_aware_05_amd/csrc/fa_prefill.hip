@@ -325,15 +325,21 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
 // kBand (iff i + Nk - Nq - wl <= j <= i + Nk - Nq + wr, wl and wr >= 0).
 constexpr int kNone = 0, kCausal = 1, kBand = 2;
 
-template <int D, int MODE, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32, bool SPARSE = false>
 __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, void* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int Nq_max, int Nk_max,
-    float c2, int n_qblk, int n_items, SeqLayout lay, int wl, int wr) {
+    float c2, int n_qblk, int n_items, SeqLayout lay, int wl, int wr,
+    BlockMask bmask) {
   constexpr bool CAUSAL = MODE == kCausal;
   constexpr bool BAND = MODE == kBand;
+  static_assert(!(SPARSE && BAND), "block masks go with no mask or causal");
   using L = Layout<D>;
+  // block-sparse: the key blocks this workgroup computes, in order (bits
+  // 0..23 the block, bit 24 / 25 set when the rows of group A / B use it),
+  // then their count
+  __shared__ int blist[SPARSE ? kSparseMaxKeyBlocks + 1 : 1];
   constexpr int NTILE = L::NTILE;
   constexpr int NSTEP = L::NSTEP;
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
@@ -417,6 +423,38 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     j0 = max(0, q0 + off - wl) / BC;
   }
   const int nblk = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  // ---- block-sparse: wave 0 lists the key blocks below nblk that either
+  // 128-row half of this workgroup keeps (mask rows 2 qblk and 2 qblk + 1)
+  int n_act = nblk;
+  if (SPARSE) {
+    if (wave == 0) {
+      const uint8_t* ma = bmask.mask + b * bmask.mb + hq * bmask.mh +
+                          (int64_t)(2 * qblk) * bmask.nkb;
+      const bool has_b = q0 + BR / 2 < Nq;
+      int cnt = 0;
+      for (int base = 0; base < nblk; base += 64) {
+        const int i = base + lane;
+        const bool ua = i < nblk && ma[i] != 0;
+        const bool ub = i < nblk && has_b && ma[bmask.nkb + i] != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(ua || ub);
+        const int pos =
+            cnt + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        if (ua || ub) blist[pos] = i | (ua ? 1 << 24 : 0) | (ub ? 1 << 25 : 0);
+        cnt += (int)__builtin_popcountll(bal);
+      }
+      if (lane == 0) blist[kSparseMaxKeyBlocks] = cnt;
+    }
+    __syncthreads();
+    n_act = __builtin_amdgcn_readfirstlane(blist[kSparseMaxKeyBlocks]);
+  }
+  // key block at ring position p: p itself, or the p-th listed block (past
+  // the list: a block past Nk, whose copies are zeros)
+  auto blk_at = [&](int p) {
+    if (!SPARSE) return p;
+    return p < n_act ? __builtin_amdgcn_readfirstlane(blist[p] & 0xFFFFFF)
+                     : nblk + 1;
+  };
 
   // this wave's rows: blocks from w_mask on may hide keys from one of them
   // (past the causal limit of its first row, or past Nk)
@@ -517,10 +555,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   constexpr int OPS = 2 * (L::NINS / NW);  // copy instructions per wave
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
   auto copies = [&](int j) {
-    copy_block<D>(smem + ((j + 3) % L::NS) * L::KBYTES, kh, kv_rows, j + 3,
-                  wave, k_off, 16, rsb);
+    copy_block<D>(smem + ((j + 3) % L::NS) * L::KBYTES, kh, kv_rows,
+                  blk_at(j + 3), wave, k_off, 16, rsb);
     copy_block<D>(smem + L::VBASE + ((j + 2) % L::NS) * L::VBYTES, vh,
-                  kv_rows, j + 2, wave, v_off, v_step, rsbv);
+                  kv_rows, blk_at(j + 2), wave, v_off, v_step, rsbv);
   };
   // prologue: K_j0, K_j0+1, K_j0+2, V_j0, V_j0+1 (all waves), fully
   // waited (j0 = 0 unless a band starts later).  The V stage before j0 is
@@ -529,11 +567,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 #pragma unroll
   for (int b0 = 0; b0 < 3; ++b0)
     copy_block<D>(smem + ((j0 + b0) % L::NS) * L::KBYTES, kh, kv_rows,
-                  j0 + b0, wave, k_off, 16, rsb);
+                  blk_at(j0 + b0), wave, k_off, 16, rsb);
 #pragma unroll
   for (int b0 = 0; b0 < 2; ++b0)
     copy_block<D>(smem + L::VBASE + ((j0 + b0) % L::NS) * L::VBYTES, vh,
-                  kv_rows, j0 + b0, wave, v_off, v_step, rsbv);
+                  kv_rows, blk_at(j0 + b0), wave, v_off, v_step, rsbv);
 #pragma unroll
   for (int i = tid; i < L::VBYTES / 16; i += NT)
     reinterpret_cast<u32x4*>(smem + L::VBASE +
@@ -553,15 +591,26 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 #pragma unroll
   for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
   if (!group_a) __syncthreads();
-  for (int j = j0; j < nblk; ++j) {
+  // (ring position j holds key block jb: j itself, or the j-th listed
+  // block of a block-sparse mask; a listed block that this wave's half does
+  // not keep goes through the masked softmax with every key hidden)
+  for (int j = j0; j < n_act; ++j) {
     mphase(j, std::true_type{});
     __syncthreads();
     copies(j);
-    if (j >= w_mask || (BAND && j < w_lo))
-      rescale = softmax_phase<true, BAND>(s0, s1, lim0 - j * BC,
-                                          lo0 - j * BC, c2, st, alpha, pk);
+    int jb = j;
+    bool keep = true;
+    if (SPARSE) {
+      const int e = __builtin_amdgcn_readfirstlane(blist[j]);
+      jb = e & 0xFFFFFF;
+      keep = (e >> (group_a ? 24 : 25)) & 1;
+    }
+    if (jb >= w_mask || (BAND && jb < w_lo) || !keep)
+      rescale = softmax_phase<true, BAND>(
+          s0, s1, keep ? lim0 - jb * BC : -(1 << 30), lo0 - jb * BC, c2, st,
+          alpha, pk);
     else
-      rescale = softmax_phase<false>(s0, s1, lim0 - j * BC, 0, c2, st,
+      rescale = softmax_phase<false>(s0, s1, lim0 - jb * BC, 0, c2, st,
                                      alpha, pk);
     if (group_a)
       wait_vmcnt<2 * OPS>();  // own copies of iteration j-2 have landed
@@ -569,7 +618,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       wait_vmcnt<OPS>();      // own copies of iteration j-1 have landed
     __syncthreads();
   }
-  if (nblk > j0) mphase(nblk, std::false_type{});  // P V of the last block
+  if (n_act > j0) mphase(n_act, std::false_type{});  // P V of the last block
   __syncthreads();
   if (group_a) __syncthreads();
 
@@ -603,10 +652,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   }
 }
 
-template <int D, int MODE, bool OUT_F32>
+template <int D, int MODE, bool OUT_F32, bool SPARSE = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
                   float* lse, const Shape& s, const SeqLayout& lay, int wl,
-                  int wr, hipStream_t stream) {
+                  int wr, hipStream_t stream, const BlockMask& bm = {}) {
   const int n_qblk = (s.Nq + BR - 1) / BR;
   long long n_items = (long long)s.B * s.Hq * n_qblk;
   // packed batch: whole rounds of 8 units of G heads (the tail's surplus
@@ -620,12 +669,12 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   // below 2^-24 in magnitude, so each weight is exactly 1, and -inf scores
   // stay -inf (no 0 * inf)
   const float c2 = fmaxf(s.scale * kLog2e, 1.17549435e-38f);
-  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32>),
+  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32, SPARSE>),
                      dim3((unsigned)n_items), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, lse, s.Hq, s.Hkv,
-                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr);
+                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr, bm);
   return hipGetLastError();
 }
 
@@ -655,6 +704,34 @@ hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
 }
 
 }  // namespace
+
+template <int D>
+hipError_t launch_sparse_d(const void* q, const void* k, const void* v,
+                           void* o, float* lse, const Shape& s,
+                           const BlockMask& bm, bool out_f32,
+                           hipStream_t stream) {
+  const SeqLayout lay = dense_layout(s);
+  if (s.causal)
+    return out_f32 ? launch<D, kCausal, true, true>(q, k, v, o, lse, s, lay,
+                                                    0, 0, stream, bm)
+                   : launch<D, kCausal, false, true>(q, k, v, o, lse, s, lay,
+                                                     0, 0, stream, bm);
+  return out_f32 ? launch<D, kNone, true, true>(q, k, v, o, lse, s, lay, 0, 0,
+                                                stream, bm)
+                 : launch<D, kNone, false, true>(q, k, v, o, lse, s, lay, 0,
+                                                 0, stream, bm);
+}
+
+hipError_t launch_prefill_sparse(const void* q, const void* k, const void* v,
+                                 void* o, float* lse, const Shape& s,
+                                 const BlockMask& bm, bool out_f32,
+                                 hipStream_t stream) {
+  if (s.d == 128)
+    return launch_sparse_d<128>(q, k, v, o, lse, s, bm, out_f32, stream);
+  if (s.d == 64)
+    return launch_sparse_d<64>(q, k, v, o, lse, s, bm, out_f32, stream);
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s,

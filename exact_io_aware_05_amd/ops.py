@@ -20,7 +20,8 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
            "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged",
-           "paged_num_splits", "fa_fwd_fp8", "fa_fwd_strided"]
+           "paged_num_splits", "fa_fwd_fp8", "fa_fwd_strided",
+           "fa_fwd_block_sparse"]
 
 
 def _dims(q, k, v):
@@ -366,4 +367,36 @@ def fa_fwd_strided(q, k, v, causal=False, scale=None, window=(-1, -1),
         int(bool(causal)), left, right, scale,
         FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
     check(st, "fa_fwd_strided")
+    return o, lse
+
+
+SPARSE_BLOCK = (128, 64)  # query rows, keys per block of a block mask
+
+
+def fa_fwd_block_sparse(q, k, v, block_mask, causal=False, scale=None,
+                        out_dtype=torch.bfloat16, o=None, lse=None):
+    """Block-sparse forward through ``fa_fwd_block_sparse``.
+
+    block_mask: uint8 device tensor [Bm, Hm, ceil(Nq / 128), ceil(Nk / 64)]
+    with Bm in (1, B) and Hm in (1, Hq) (size-1 axes are shared), its last
+    two axes contiguous.  Returns ``(o, lse)`` like ``fa_fwd``."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    nqb = (Nq + SPARSE_BLOCK[0] - 1) // SPARSE_BLOCK[0]
+    nkb = (Nk + SPARSE_BLOCK[1] - 1) // SPARSE_BLOCK[1]
+    m = block_mask
+    if (not isinstance(m, torch.Tensor) or m.dtype != torch.uint8
+            or not m.is_cuda or m.dim() != 4 or tuple(m.shape[2:]) != (nqb, nkb)
+            or m.shape[0] not in (1, B) or m.shape[1] not in (1, Hq)
+            or m.stride(3) != 1 or m.stride(2) != nkb):
+        raise ValueError(f"block_mask must be a uint8 device tensor "
+                         f"[1 or B, 1 or Hq, {nqb}, {nkb}], rows contiguous")
+    mb = m.stride(0) if m.shape[0] == B and B > 1 else 0
+    mh = m.stride(1) if m.shape[1] == Hq and Hq > 1 else 0
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    st = load().fa_fwd_block_sparse(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        m.data_ptr(), mb, mh, B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
+    check(st, "fa_fwd_block_sparse")
     return o, lse

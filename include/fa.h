@@ -179,6 +179,28 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
                   int out_dtype, hipStream_t stream);
 
 /*
+ * Block-sparse forward ("FlashAttention Analysis", ryotta.opik.net,
+ * results of FlashAttention-1: extended with a block-sparse pattern, only
+ * the blocks of a mask are computed).  block_mask (DEVICE, one byte per
+ * block) marks blocks of 128 query rows x 64 keys: head hq of batch b uses
+ * the bytes block_mask[b * mask_batch_stride + hq * mask_head_stride +
+ * qb * nkb + kb] for query block qb = i / 128 and key block kb = j / 64,
+ * nkb = ceil(Nk / 64), rows qb = 0 .. ceil(Nq / 128) - 1 (strides in
+ * bytes, 0 to share a mask).  Key j is visible to query i only if that
+ * byte is non-zero (and, with `causal`, j <= i + Nk - Nq).  Rows whose
+ * blocks are all zero get O = 0, lse = -inf.  Layouts, types and status
+ * codes as for fa_fwd (dense [B, H, N, d]; the prefill kernel always
+ * runs, skipping zero blocks); FA_ERR_INVALID_ARG also for a null mask or
+ * negative strides; FA_ERR_UNSUPPORTED when nkb > 8191.
+ */
+int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
+                        float* lse, const unsigned char* block_mask,
+                        long long mask_batch_stride, long long mask_head_stride,
+                        int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                        int causal, float scale, int out_dtype,
+                        hipStream_t stream);
+
+/*
  * Forward on strided tensors (views such as slices of a fused QKV
  * projection, [B, N, H, d] layouts, padded rows).  Each of q, k, v and o
  * is described by its element strides {batch, head, row} (a host array of

@@ -370,3 +370,25 @@ def test_strided_unsupported(lib):
     assert _strided(lib, Nk=(1 << 16) + 2, ks=(0, 0, 1 << 14)) == \
         _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
+
+
+def _sparse(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, m=P, mb=0, mh=0, B=1, Hq=4, Hkv=2,
+             Nq=16, Nk=16, d=64, causal=0, scale=0.125, out=0)
+    a.update(kw)
+    return lib.fa_fwd_block_sparse(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                                   a["m"], a["mb"], a["mh"], a["B"], a["Hq"],
+                                   a["Hkv"], a["Nq"], a["Nk"], a["d"],
+                                   a["causal"], a["scale"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw", INVALID + [dict(m=None), dict(mb=-1),
+                                          dict(mh=-4)], ids=lambda k: str(k))
+def test_sparse_invalid_arguments(lib, kw):
+    assert _sparse(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_sparse_unsupported(lib):
+    assert _sparse(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _sparse(lib, Nk=8191 * 64 + 1) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0

@@ -528,7 +528,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // then the scores of block j when QK
   bool rescale = false;  // scale acc by alpha before the next P V
   float alpha = 1.f;
-  auto mphase = [&](int j, auto qk_tag) {
+  // (block-sparse: `pv` / `qk` false skip the products of a block this
+  // wave's half does not keep)
+  auto mphase = [&](int j, auto qk_tag, bool pv = true, bool qk = true) {
     if (rescale) {
 #pragma unroll
       for (int i = 0; i < NTILE; ++i) acc[i] *= alpha;
@@ -537,9 +539,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt)
       vp[tt] = smem + ((j + L::NS - 1) % L::NS) * L::VBYTES + v_rd[tt];
+    const char* kp = smem + (j % L::NS) * L::KBYTES + k_rd;
+    constexpr bool QK = decltype(qk_tag)::value;
     __builtin_amdgcn_s_setprio(1);
-    matrix_phase<D, true, decltype(qk_tag)::value>(
-        smem + (j % L::NS) * L::KBYTES + k_rd, vp, qf, pk, acc, s0, s1);
+    if (!SPARSE || (pv && qk)) {
+      matrix_phase<D, true, QK>(kp, vp, qf, pk, acc, s0, s1);
+    } else if (pv) {
+      matrix_phase<D, true, false>(kp, vp, qf, pk, acc, s0, s1);
+    } else if (QK && qk) {
+      matrix_phase<D, false, QK>(kp, vp, qf, pk, acc, s0, s1);
+    }
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -594,10 +603,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // (ring position j holds key block jb: j itself, or the j-th listed
   // block of a block-sparse mask; a listed block that this wave's half does
   // not keep goes through the masked softmax with every key hidden)
+  bool keep_prev = false;  // block-sparse: this half kept position j - 1
   for (int j = j0; j < n_act; ++j) {
-    mphase(j, std::true_type{});
-    __syncthreads();
-    copies(j);
     int jb = j;
     bool keep = true;
     if (SPARSE) {
@@ -605,20 +612,26 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       jb = e & 0xFFFFFF;
       keep = (e >> (group_a ? 24 : 25)) & 1;
     }
-    if (jb >= w_mask || (BAND && jb < w_lo) || !keep)
-      rescale = softmax_phase<true, BAND>(
-          s0, s1, keep ? lim0 - jb * BC : -(1 << 30), lo0 - jb * BC, c2, st,
-          alpha, pk);
+    mphase(j, std::true_type{}, keep_prev, keep);
+    __syncthreads();
+    copies(j);
+    if (SPARSE && !keep)
+      rescale = false;  // nothing of this block enters this half's rows
+    else if (jb >= w_mask || (BAND && jb < w_lo))
+      rescale = softmax_phase<true, BAND>(s0, s1, lim0 - jb * BC,
+                                          lo0 - jb * BC, c2, st, alpha, pk);
     else
       rescale = softmax_phase<false>(s0, s1, lim0 - jb * BC, 0, c2, st,
                                      alpha, pk);
+    keep_prev = keep;
     if (group_a)
       wait_vmcnt<2 * OPS>();  // own copies of iteration j-2 have landed
     else
       wait_vmcnt<OPS>();      // own copies of iteration j-1 have landed
     __syncthreads();
   }
-  if (n_act > j0) mphase(n_act, std::false_type{});  // P V of the last block
+  if (n_act > j0)  // P V of the last block
+    mphase(n_act, std::false_type{}, SPARSE ? keep_prev : true);
   __syncthreads();
   if (group_a) __syncthreads();
 

@@ -48,6 +48,23 @@ def visible_keys(Nq, Nk, causal, window=None) -> int:
     return max(hi - lo + 1, 0)
 
 
+def block_pair_counts(Nq, Nk, causal, block_size):
+    """Visible (query row, key) pairs inside each (query block, key block)
+    of a block mask's grid: an array [ceil(Nq / bq), ceil(Nk / bk)]."""
+    import numpy as np
+    bq, bk = block_size
+    nqb, nkb = -(-Nq // bq), -(-Nk // bk)
+    c = np.arange(Nq, dtype=np.int64) + (Nk - Nq)       # each row's place
+    hi = np.minimum(c, Nk - 1) if causal else np.full(Nq, Nk - 1)
+    k0 = np.arange(nkb, dtype=np.int64) * bk
+    k1 = np.minimum(k0 + bk, Nk) - 1
+    per_row = np.clip(np.minimum(hi[:, None], k1[None, :]) - k0[None, :] + 1,
+                      0, None)                           # [Nq, nkb]
+    out = np.zeros((nqb, nkb), dtype=np.int64)
+    np.add.at(out, np.arange(Nq) // bq, per_row)
+    return out
+
+
 def attention_window_flops(B, Hq, Nq, Nk, d, causal, window) -> float:
     """Forward FLOPs of a windowed mask: 4 d per visible pair (the two
     products), counted exactly."""

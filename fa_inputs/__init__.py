@@ -30,7 +30,7 @@ import numpy as np
 __all__ = [
     "Workload", "WORKLOADS", "workload", "make_inputs", "make_qkv", "make_dout",
     "make_varlen", "VARLEN_PREFILL", "varlen_lengths", "make_paged",
-    "f32_to_e4m3", "make_fp8",
+    "f32_to_e4m3", "make_fp8", "sparse_block_mask",
     "f32_to_bf16_bits", "bf16_bits_to_f32", "bf16_bits_to_f64",
 ]
 
@@ -256,6 +256,24 @@ def varlen_lengths(total, lo, hi, seed=0):
         out.append(n)
         left -= n
     return out
+
+
+def sparse_block_mask(Hq, Nq, Nk, density, *, seed=0, block=(128, 64)):
+    """A block mask [1, Hq, ceil(Nq / 128), ceil(Nk / 64)] (uint8): each
+    block kept with probability ``density`` (``default_rng([seed, 0x73])``,
+    independent per head), plus, for every query block, the key blocks
+    that hold the keys at its rows' own places (i + Nk - Nq), so that every
+    row keeps its diagonal (local attention plus random blocks)."""
+    bq, bk = block
+    nqb, nkb = -(-Nq // bq), -(-Nk // bk)
+    rng = np.random.default_rng([seed, 0x73])
+    m = (rng.random((1, Hq, nqb, nkb)) < density).astype(np.uint8)
+    for qb in range(nqb):
+        lo = qb * bq + Nk - Nq
+        hi = min((qb + 1) * bq, Nq) - 1 + Nk - Nq
+        for kb in range(max(lo, 0) // bk, min(hi, Nk - 1) // bk + 1):
+            m[:, :, qb, kb] = 1
+    return m
 
 
 def make_inputs(w, seed=0):

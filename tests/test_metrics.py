@@ -107,3 +107,17 @@ def test_visible_keys_counts():
                                 (not causal or j <= c):
                             seen.add(j)
                 assert visible_keys(Nq, Nk, causal, w) == len(seen)
+
+
+def test_block_pair_counts_brute_force():
+    from exact_io_aware_05_amd.metrics import block_pair_counts
+    import numpy as np
+    for Nq, Nk, bs in ((7, 9, (2, 3)), (9, 5, (4, 2)), (6, 6, (3, 3))):
+        for causal in (False, True):
+            got = block_pair_counts(Nq, Nk, causal, bs)
+            want = np.zeros_like(got)
+            for i in range(Nq):
+                for j in range(Nk):
+                    if not causal or j <= i + Nk - Nq:
+                        want[i // bs[0], j // bs[1]] += 1
+            assert np.array_equal(got, want), (Nq, Nk, bs, causal)

@@ -82,16 +82,20 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
-        "fetch_kib": 71281.0, "write_kib": 66561.0},
+        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
+        "fetch_kib": 71228.3, "write_kib": 66560.0},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
-        "fetch_kib": 514058.8, "write_kib": 266359.1},
+        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
+        "fetch_kib": 514060.9, "write_kib": 266356.0},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "465e033d94f1a33bdc41a1cc25948da3176039962d7769588c498c1a563d73b7",
-        "fetch_kib": 67574.9, "write_kib": 66560.2},
+        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
+        "fetch_kib": 67528.2, "write_kib": 66560.1},
+    "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
+        "source": "fa_prefill.hip",
+        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
+        "fetch_kib": 73475.4, "write_kib": 70656.8},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
         "sha256": "33d71c45690d58cf5b66d4391cc8ffa33d06f4507deed0898e04e71093e312ae",

@@ -556,11 +556,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // b % 4.  In iteration j every wave issues its share of the copies of
   // K_{j+3} and V_{j+2} at the start of its softmax phase (vector memory
   // issue then overlaps vector ALU work).  A stage is refilled only after
-  // both groups' last reads of it.  The first reader of K_{j+3} / V_{j+2}
-  // is group A's matrix phase of iteration j+3, so group A (whose softmax
-  // phases end one interval earlier) waits for its copies of iteration j at
-  // the end of iteration j+2, keeping 2 * OPS in flight, and group B at the
-  // end of iteration j+1, keeping OPS in flight.
+  // both groups' last reads of it.  The copies are complete at the
+  // iteration's closing barrier: its release fence waits for every
+  // outstanding direct-to-LDS copy (they write LDS), so the explicit waits
+  // below only state the weakest order the ring needs (the first reader of
+  // K_{j+3} / V_{j+2} is group A's matrix phase of iteration j+3).
   constexpr int OPS = 2 * (L::NINS / NW);  // copy instructions per wave
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
   auto copies = [&](int j) {

@@ -11,5 +11,5 @@ from .attention import (  # noqa: F401
 from .backward import (  # noqa: F401
     reference_attention_backward, recompute_backward,
 )
-from .paged import paged_rows, paged_attention  # noqa: F401
+from .paged import paged_rows, paged_attention, kvlen_attention  # noqa: F401
 from .fp8 import decode_e4m3, reference_attention_fp8  # noqa: F401

@@ -20,7 +20,7 @@ import numpy as np
 
 from .attention import reference_attention
 
-__all__ = ["paged_rows", "paged_attention"]
+__all__ = ["paged_rows", "paged_attention", "kvlen_attention"]
 
 
 def paged_rows(cache, page_table_row, n: int):
@@ -52,6 +52,31 @@ def paged_attention(q, k_cache, v_cache, page_table, seqlen_k, *,
         k = paged_rows(k_cache, page_table[b], n).transpose(1, 0, 2)[None]
         v = paged_rows(v_cache, page_table[b], n).transpose(1, 0, 2)[None]
         Ob, lb = reference_attention(q[b:b + 1], k, v, causal=causal,
+                                     scale=scale, window=window)
+        O[b], lse[b] = Ob[0], lb[0]
+    return O, lse
+
+
+def kvlen_attention(q, k, v, seqlen_k, *, causal: bool, scale: float,
+                    window=None):
+    """Attention over a padded cache of unequal lengths.  q [B, Hq, Nq, d];
+    k, v [B, Hkv, Nk_max, d]; seqlen_k [B].  Sequence b attends to its
+    first ``seqlen_k[b]`` key rows only, with the causal and window
+    alignment taken at its own last key, the same rule as for the paged
+    cache (the rows past its length are padding and never read).  Returns
+    (O [B, Hq, Nq, d], lse [B, Hq, Nq]); a sequence with no keys gets
+    O = 0, lse = -inf."""
+    B, Hq, Nq, d = q.shape
+    O = np.zeros(q.shape)
+    lse = np.full((B, Hq, Nq), -np.inf)
+    for b in range(B):
+        length = int(seqlen_k[b])
+        if not 0 <= length <= k.shape[2]:
+            raise ValueError("sequence length out of range")
+        if length == 0:
+            continue
+        Ob, lb = reference_attention(q[b:b + 1], k[b:b + 1, :, :length],
+                                     v[b:b + 1, :, :length], causal=causal,
                                      scale=scale, window=window)
         O[b], lse[b] = Ob[0], lb[0]
     return O, lse

@@ -277,6 +277,42 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                                              splits, workspace, stream));
 }
 
+int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
+                 float* lse, const int* seqlens_k, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int d, int causal, int window_left,
+                 int window_right, float scale, int out_dtype, int num_splits,
+                 void* workspace, size_t workspace_bytes,
+                 hipStream_t stream) {
+  if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
+  if (!seqlens_k || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
+    return FA_ERR_INVALID_ARG;
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  // one K or V head is addressed with 32-bit byte offsets
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  const int splits = num_splits == 0 ? fa_default_num_splits(B, Hq, Hkv, Nq,
+                                                             Nk, d)
+                                     : num_splits;
+  if (splits < 1 || splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
+  if (workspace_bytes <
+      fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, splits))
+    return FA_ERR_INVALID_ARG;
+  const long long rowtiles = ((long long)Nq * (Hq / Hkv) + fa::kSplitRows - 1) /
+                             fa::kSplitRows;
+  if ((long long)B * Hkv * rowtiles * splits > (1LL << 31) - 64)
+    return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
+  return hip_status(fa::launch_splitkv_kvlen(q, k, v, o, lse, s, seqlens_k,
+                                             out_dtype == FA_OUT_F32, splits,
+                                             workspace, stream));
+}
+
 int fa_fwd_fp8(const void* q, const void* k, const void* vt,
                const float* q_descale, const float* k_descale,
                const float* v_descale, void* o, float* lse, int B, int Hq,

@@ -168,6 +168,15 @@ hipError_t launch_splitkv_paged(const void* q, const void* k_cache,
                                 bool out_f32, int num_splits, void* workspace,
                                 hipStream_t stream);
 
+// KV-split form over contiguous [B, Hkv, Nk, d] K/V of which sequence b
+// uses its first seqlen[b] rows (clamped to [0, Nk]; Shape::Nk is the
+// padded length).
+hipError_t launch_splitkv_kvlen(const void* q, const void* k, const void* v,
+                                void* o, float* lse, const Shape& s,
+                                const int* seqlen, bool out_f32,
+                                int num_splits, void* workspace,
+                                hipStream_t stream);
+
 size_t splitkv_workspace_bytes(long long rows, int d, int num_splits);
 
 // Backward pass: D and lse * log2(e) per query row in `workspace`, then the

@@ -213,9 +213,12 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   const int rt = t1 % n_rowtiles;
   const int bh = t1 / n_rowtiles;  // b * Hkv + hkv
   const int b = bh / Hkv, hkv = bh % Hkv;
-  // keys of this sequence: all of them, or (paged) its own cache length
+  // keys of this sequence: all of them, or its own cache length (paged, or
+  // a padded contiguous cache with lengths), clamped into the cache
   const int Nk =
-      PAGED ? min(max(pg.seqlen[b], 0), pg.max_pages * pg.page_size) : Nk_arg;
+      PAGED ? min(max(pg.seqlen[b], 0), pg.max_pages * pg.page_size)
+      : pg.seqlen ? min(max(pg.seqlen[b], 0), Nk_arg)
+                  : Nk_arg;
   const int G = Hq / Hkv;
   const int R = Nq * G;
   const int prow = rt * 32 + col;  // packed (query, head-in-group) row
@@ -236,8 +239,9 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
           bf16x8, row_ok ? ldg16(qp + 8 * t) : u32x4{0u, 0u, 0u, 0u});
   }
 
-  const uint16_t* kh = k + (int64_t)bh * Nk * D;
-  const uint16_t* vh = v + (int64_t)bh * Nk * D;
+  // (contiguous heads are Nk_arg rows apart, padded or not)
+  const uint16_t* kh = k + (int64_t)bh * Nk_arg * D;
+  const uint16_t* vh = v + (int64_t)bh * Nk_arg * D;
   // paged: bytes between the rows of one page and head, the chunk's first
   // page, and its page numbers, one per lane (clamped into the cache)
   const int rs = PAGED ? Hkv * D * 2 : 2 * D;
@@ -533,6 +537,22 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
   if (s.d == 64)
     return launch_d<64, false>(q, k, v, o, lse, s, out_f32, num_splits,
                                workspace, none, stream);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_splitkv_kvlen(const void* q, const void* k, const void* v,
+                                void* o, float* lse, const Shape& s,
+                                const int* seqlen, bool out_f32,
+                                int num_splits, void* workspace,
+                                hipStream_t stream) {
+  PagedKv lens{};
+  lens.seqlen = seqlen;
+  if (s.d == 128)
+    return launch_d<128, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                                workspace, lens, stream);
+  if (s.d == 64)
+    return launch_d<64, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                               workspace, lens, stream);
   return hipErrorInvalidValue;
 }
 

@@ -19,7 +19,7 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
-           "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged",
+           "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged", "fa_fwd_kvlen",
            "paged_num_splits", "fa_fwd_fp8", "fa_fwd_strided",
            "fa_fwd_block_sparse"]
 
@@ -285,6 +285,39 @@ def fa_fwd_paged(q, k_cache, v_cache, page_table, seqlens_k, causal=False,
         FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, splits,
         workspace.data_ptr(), workspace.numel(), _stream(q))
     check(st, "fa_fwd_paged")
+    return o, lse
+
+
+def fa_fwd_kvlen(q, k, v, seqlens_k, causal=False, scale=None,
+                 window=(-1, -1), out_dtype=torch.bfloat16, num_splits=0,
+                 o=None, lse=None, workspace=None):
+    """Variable-length decode over a padded cache through ``fa_fwd_kvlen``.
+
+    q [B, Hq, Nq, d] bf16; k, v [B, Hkv, Nk, d] bf16 padded to the longest
+    sequence; seqlens_k int32 [B] on the device (sequence b uses its first
+    seqlens_k[b] rows).  Returns ``(o, lse)`` shaped like ``fa_fwd``'s."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    if (not isinstance(seqlens_k, torch.Tensor)
+            or seqlens_k.dtype != torch.int32 or not seqlens_k.is_cuda
+            or not seqlens_k.is_contiguous()
+            or tuple(seqlens_k.shape) != (B,)):
+        raise ValueError("seqlens_k must be a contiguous int32 device "
+                         "tensor [B]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    splits = int(num_splits) or default_num_splits(B, Hq, Hkv, Nq, Nk, d)
+    if workspace is None:
+        need = splitkv_workspace_bytes(B, Hq, Nq, d, max(splits, 1))
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8,
+                                device=q.device)
+    left, right = (int(x) for x in window)
+    st = load().fa_fwd_kvlen(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), seqlens_k.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+        int(bool(causal)), left, right, scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, splits,
+        workspace.data_ptr(), workspace.numel(), _stream(q))
+    check(st, "fa_fwd_kvlen")
     return o, lse
 
 

@@ -264,6 +264,34 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                  size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Variable-length decode over a padded contiguous cache.  Serving engines
+ * keep the caches of a batch in one tensor padded to the longest sequence
+ * ("FlashAttention Analysis", ryotta.opik.net, closing section: the fused
+ * kernels run inside paged and cached decoding; as for the paged cache,
+ * each sequence attends to its own cache length).
+ *     q        [B, Hq, Nq, d] bf16            o [B, Hq, Nq, d] (FA_OUT_*)
+ *     k, v     [B, Hkv, Nk, d] bf16 (Nk: the padded length)
+ *     seqlens_k int32 [B] (DEVICE)            lse [B, Hq, Nq] fp32
+ * Sequence b's keys are its first seqlens_k[b] rows (clamped to [0, Nk] on
+ * the device); the rows past them are never read.  Its Nq queries attend
+ * to them as fa_fwd_window would (causal alignment at its own last key:
+ * query i sits at c = i + seqlens_k[b] - Nq; window bounds -1 for none).  A
+ * sequence with no keys gets O = 0 and lse = -inf.  The KV-split form runs
+ * (partial + merge kernels) with chunks cut from the padded length; chunks
+ * past a sequence's length weigh nothing.  num_splits = 0 takes
+ * fa_default_num_splits(B, Hq, Hkv, Nq, Nk, d), otherwise 1 .. 4096;
+ * `workspace` (16-byte aligned, device) holds at least
+ * fa_splitkv_workspace_bytes(B, Hq, Nq, d, splits) bytes.  Errors as for
+ * fa_fwd_splitkv; FA_ERR_INVALID_ARG also for a null or misaligned
+ * seqlens_k and a bound below -1.
+ */
+int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
+                 float* lse, const int* seqlens_k, int B, int Hq, int Hkv,
+                 int Nq, int Nk, int d, int causal, int window_left,
+                 int window_right, float scale, int out_dtype, int num_splits,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Forward over a packed batch of variable-length sequences (prefill form).
  * Sequence b has the query rows cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1
  * and the key/value rows cu_seqlens_k[b] .. cu_seqlens_k[b + 1] - 1 of the

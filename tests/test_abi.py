@@ -305,6 +305,37 @@ def test_paged_unsupported_and_splits(lib):
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 96, 32, 10) == 0
 
 
+def _kvlen(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, sl=P, B=2, Hq=4, Hkv=2, Nq=1, Nk=256,
+             d=64, causal=0, wl=-1, wr=-1, scale=0.125, out=0, S=0, ws=P,
+             wsb=1 << 20)
+    a.update(kw)
+    return lib.fa_fwd_kvlen(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                            a["sl"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                            a["Nk"], a["d"], a["causal"], a["wl"], a["wr"],
+                            a["scale"], a["out"], a["S"], a["ws"], a["wsb"],
+                            None)
+
+
+KVLEN_INVALID = [
+    dict(q=None), dict(k=P + 2), dict(v=None), dict(o=P + 4), dict(lse=None),
+    dict(sl=None), dict(sl=P + 2), dict(B=0), dict(Hq=3), dict(Nq=0),
+    dict(Nk=0), dict(wl=-2), dict(wr=-5), dict(scale=-1.0), dict(out=3),
+    dict(S=-1), dict(S=4097), dict(ws=None), dict(ws=P + 8), dict(wsb=0),
+]
+
+
+@pytest.mark.parametrize("kw", KVLEN_INVALID, ids=lambda k: str(k))
+def test_kvlen_invalid_arguments(lib, kw):
+    assert _kvlen(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_kvlen_unsupported(lib):
+    assert _kvlen(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _kvlen(lib, Nk=1 << 24, d=128) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+
+
 def _fp8(lib, **kw):
     a = dict(q=P, k=P, vt=P, qd=P, kd=P, vd=P, o=P, lse=P, B=1, Hq=4, Hkv=2,
              Nq=16, Nk=16, ldv=64, d=128, causal=0, scale=0.125, out=0)

@@ -82,20 +82,20 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
-        "fetch_kib": 71228.3, "write_kib": 66560.0},
+        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
+        "fetch_kib": 71236.5, "write_kib": 66560.3},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
-        "fetch_kib": 514060.9, "write_kib": 266356.0},
+        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
+        "fetch_kib": 514062.5, "write_kib": 266357.3},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
-        "fetch_kib": 67528.2, "write_kib": 66560.1},
+        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
+        "fetch_kib": 67524.3, "write_kib": 66560.7},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "595e03d614a2c91b2b09ffc9c38ea63dfe3342d86ecf1c9a860a1aa85c55465b",
-        "fetch_kib": 73475.4, "write_kib": 70656.8},
+        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
+        "fetch_kib": 73441.2, "write_kib": 70658.1},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
         "sha256": "33d71c45690d58cf5b66d4391cc8ffa33d06f4507deed0898e04e71093e312ae",
@@ -103,16 +103,16 @@ MEASURED_TRAFFIC = {
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "1acaafd5e45ab88efc2ce090301abffd1bbd4df094e09d001aa107b2a9f0ed79",
-        "fetch_kib": 1048893.5, "write_kib": 2112.0},
+        "sha256": "ef12408f9af29c548d316dc8a2310238f53e8fa1f08c46915755d881a86153f8",
+        "fetch_kib": 1048893.6, "write_kib": 2112.0},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "1acaafd5e45ab88efc2ce090301abffd1bbd4df094e09d001aa107b2a9f0ed79",
-        "fetch_kib": 132403.3, "write_kib": 2112.0},
+        "sha256": "ef12408f9af29c548d316dc8a2310238f53e8fa1f08c46915755d881a86153f8",
+        "fetch_kib": 132412.9, "write_kib": 2112.0},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "1acaafd5e45ab88efc2ce090301abffd1bbd4df094e09d001aa107b2a9f0ed79",
-        "fetch_kib": 1048918.7, "write_kib": 2112.0},
+        "sha256": "ef12408f9af29c548d316dc8a2310238f53e8fa1f08c46915755d881a86153f8",
+        "fetch_kib": 1048927.8, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",

@@ -5,7 +5,7 @@ TEST INFRASTRUCTURE ONLY: imported by the test suite, the package smoke
 check and the benchmark's CPU-baseline leg, never by the GPU library.
 """
 from .attention import (  # noqa: F401
-    visible_mask, kv_head_of, reference_attention, tiled_online_attention,
+    visible_mask, column_visible, kv_head_of, reference_attention, tiled_online_attention,
     splitkv_partials, merge_partials, splitkv_attention, split_bounds,
 )
 from .backward import (  # noqa: F401

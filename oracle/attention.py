@@ -102,6 +102,17 @@ def block_visible(rows, cols, block_mask_bh, block_size) -> np.ndarray:
     return bm[(rows // bq)[:, None], (cols // bk)[None, :]]
 
 
+def column_visible(rows, cols, col_bounds_b) -> np.ndarray:
+    """Boolean [len(rows), len(cols)] of one sequence's column mask:
+    ``col_bounds_b`` [Nk, 2] gives, per key column j, the query rows
+    [lo_j, hi_j) that may see key j (an empty range hides the key)."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    cb = np.asarray(col_bounds_b, dtype=np.int64)
+    lo, hi = cb[cols, 0], cb[cols, 1]
+    return (rows[:, None] >= lo[None, :]) & (rows[:, None] < hi[None, :])
+
+
 def _check(q, k, v):
     if q.ndim != 4 or k.ndim != 4 or v.ndim != 4:
         raise ValueError("q, k, v must be 4-D [B, H, N, d]")
@@ -114,7 +125,7 @@ def _check(q, k, v):
 
 def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
                         return_sp: bool = False, window=None, block_mask=None,
-                        block_size=(256, 64)):
+                        block_size=(256, 64), col_bounds=None):
     """The definition, with S and P materialised per head in float64.
 
     S[i, j] = scale * sum_c q[i, c] k[j, c], set to -inf where key j is not
@@ -124,7 +135,9 @@ def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
     per-head S and P arrays (shape [B, Hq, rows, Nk]).  ``window`` adds the
     sliding-window bounds (left, right) of ``visible_mask``; ``block_mask``
     ([B, Hq, nqb, nkb], broadcastable) keeps only the keys of non-zero
-    blocks of ``block_size`` (query rows, keys).
+    blocks of ``block_size`` (query rows, keys).  ``col_bounds`` ([B, Nk, 2],
+    one per sequence, shared by its heads) keeps key j only for the query
+    rows lo_j <= i < hi_j (``column_visible``), on top of the other masks.
     """
     B, Hq, Hkv, Nq, Nk, d = _check(q, k, v)
     rows = np.arange(Nq) if rows is None else np.asarray(rows, dtype=np.int64)
@@ -146,6 +159,9 @@ def reference_attention(q, k, v, *, causal: bool, scale: float, rows=None,
             if block_mask is not None:
                 vis_bh = vis & block_visible(rows, np.arange(Nk),
                                              block_mask[b, h], block_size)
+            if col_bounds is not None:
+                vis_bh = vis_bh & column_visible(rows, np.arange(Nk),
+                                                 col_bounds[b])
             S = np.where(vis_bh, S, -np.inf)
             m = S.max(axis=1)
             has = np.isfinite(m)

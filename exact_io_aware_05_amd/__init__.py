@@ -11,7 +11,7 @@ _LAZY = ("fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
          "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
          "fa_fwd_varlen", "fa_fwd_window",
          "fa_fwd_paged", "paged_num_splits", "fa_fwd_fp8", "fa_fwd_strided",
-         "fa_fwd_block_sparse", "fa_fwd_kvlen")
+         "fa_fwd_block_sparse", "fa_fwd_kvlen", "fa_fwd_colmask")
 
 
 def __getattr__(name):

@@ -32,6 +32,8 @@ SIGNATURES = {
     "fa_fwd_window": (_c_int, [_vp] * 5 + [_c_int] * 9 + [_c_float, _c_int,
                                                            _vp]),
     "fa_paged_num_splits": (_c_int, [_c_int] * 7),
+    "fa_fwd_colmask": (_c_int, [_vp] * 6 + [_c_int] * 7 + [_c_float, _c_int,
+                                                        _vp]),
     "fa_fwd_kvlen": (_c_int, [_vp] * 6 + [_c_int] * 9 + [_c_float, _c_int,
                                                       _c_int, _vp, _c_size,
                                                       _vp]),

@@ -409,6 +409,29 @@ int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
                                               stream));
 }
 
+int fa_fwd_colmask(const void* q, const void* k, const void* v, void* o,
+                   float* lse, const int* col_bounds, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, int causal, float scale,
+                   int out_dtype, hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  if (!col_bounds || (reinterpret_cast<uintptr_t>(col_bounds) & 7u))
+    return FA_ERR_INVALID_ARG;
+  const int nkb = (Nk + fa::kPrefillKeys - 1) / fa::kPrefillKeys;
+  if (nkb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  const fa::ColMask cm{col_bounds, (long long)Nk};
+  return hip_status(fa::launch_prefill_column(q, k, v, o, lse, s, cm,
+                                              out_dtype == FA_OUT_F32,
+                                              stream));
+}
+
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
                   float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
                   int B, int Hq, int Hkv, int total_q, int total_k,

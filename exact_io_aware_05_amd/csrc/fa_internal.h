@@ -122,6 +122,21 @@ struct BlockMask {
   int nkb;
 };
 
+// Column-interval mask of the prefill kernel: key j of sequence b may be
+// seen by the query rows bounds[2 (b mb + j)] .. bounds[2 (b mb + j) + 1]
+// - 1 (int32 pairs, shared by the sequence's heads), on top of the causal
+// flag.  The workgroup lists the key blocks that any of its rows may see
+// (at most kSparseMaxKeyBlocks) in the same LDS list as a block mask.
+struct ColMask {
+  const int* bounds;
+  long long mb;  // pairs between sequences
+};
+
+hipError_t launch_prefill_column(const void* q, const void* k, const void* v,
+                                 void* o, float* lse, const Shape& s,
+                                 const ColMask& cm, bool out_f32,
+                                 hipStream_t stream);
+
 hipError_t launch_prefill_sparse(const void* q, const void* k, const void* v,
                                  void* o, float* lse, const Shape& s,
                                  const BlockMask& bm, bool out_f32,

@@ -235,16 +235,29 @@ __device__ __forceinline__ void matrix_phase(const char* kp,
 // The rounded weights feed P V and their own row sum lb, so O = acc / lb
 // is an exact convex combination of V rows up to fp32 summation; the fp32
 // sum l of the unrounded weights gives lse.
-template <bool MASK, bool LOWER = false>
+// With COL, a column-interval mask as well: lane l of the wave holds the
+// row bounds [clo, chi) of key l of the block, read across lanes for each
+// of this lane's keys (key + 8 hh of the block) and tested against `row`.
+template <bool MASK, bool LOWER = false, bool COL = false>
 __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
                                               const f32x16& s1, int lim,
                                               int lo, float c2, RowState& st,
-                                              float& alpha, u32x4* pk) {
+                                              float& alpha, u32x4* pk,
+                                              int clo = 0, int chi = 0,
+                                              int row = 0, int hh = 0) {
   // The mask never overwrites the score registers (that would make the
   // masked and unmasked variants rejoin with copies): hidden keys are left
   // out of the max and get weight 0 after the exponential.
+  auto col_hidden = [&](int key) {
+    const int l0 = __builtin_amdgcn_readlane(clo, key);
+    const int l1 = __builtin_amdgcn_readlane(clo, key + 8);
+    const int h0 = __builtin_amdgcn_readlane(chi, key);
+    const int h1 = __builtin_amdgcn_readlane(chi, key + 8);
+    return row < (hh ? l1 : l0) || row >= (hh ? h1 : h0);
+  };
   auto hidden = [&](int key) {
-    return MASK && (key > lim || (LOWER && key < lo));
+    return (MASK && (key > lim || (LOWER && key < lo))) ||
+           (COL && col_hidden(key));
   };
   auto hide0 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7)); };
   auto hide1 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7) + 32); };
@@ -325,21 +338,27 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
 // kBand (iff i + Nk - Nq - wl <= j <= i + Nk - Nq + wr, wl and wr >= 0).
 constexpr int kNone = 0, kCausal = 1, kBand = 2;
 
-template <int D, int MODE, bool OUT_F32, bool SPARSE = false>
+template <int D, int MODE, bool OUT_F32, bool SPARSE = false,
+          bool COLUMN = false>
 __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, void* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int Nq_max, int Nk_max,
     float c2, int n_qblk, int n_items, SeqLayout lay, int wl, int wr,
-    BlockMask bmask) {
+    BlockMask bmask, ColMask cmask) {
   constexpr bool CAUSAL = MODE == kCausal;
   constexpr bool BAND = MODE == kBand;
   static_assert(!(SPARSE && BAND), "block masks go with no mask or causal");
+  static_assert(!(COLUMN && (SPARSE || BAND)),
+                "column masks go with no mask or causal");
+  // a list of key blocks in LDS drives the loop (block or column mask)
+  constexpr bool LISTED = SPARSE || COLUMN;
+  constexpr int BLKBITS = COLUMN ? 0xFFFF : 0xFFFFFF;
   using L = Layout<D>;
   // block-sparse: the key blocks this workgroup computes, in order (bits
   // 0..23 the block, bit 24 / 25 set when the rows of group A / B use it),
   // then their count
-  __shared__ int blist[SPARSE ? kSparseMaxKeyBlocks + 1 : 1];
+  __shared__ int blist[LISTED ? kSparseMaxKeyBlocks + 1 : 1];
   constexpr int NTILE = L::NTILE;
   constexpr int NSTEP = L::NSTEP;
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
@@ -448,11 +467,82 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     __syncthreads();
     n_act = __builtin_amdgcn_readfirstlane(blist[kSparseMaxKeyBlocks]);
   }
+  // ---- column mask: every wave classifies the key blocks wave, wave + NW,
+  // ... below nblk (lane = key of the block) into blist[block]: bits 0..15
+  // the block, bit 16 + w set when some key of the block is hidden from
+  // some row of wave w (that wave then tests every key), bits 24 / 25 when
+  // some row of half A / B may see some key.  Wave 0 then drops the blocks
+  // neither half sees, in place and in order.
+  if (COLUMN) {
+    const int* cb = cmask.bounds + 2 * ((int64_t)b * cmask.mb);
+    constexpr int UNR = 4;
+    for (int kb0 = wave; kb0 < nblk; kb0 += UNR * NW) {
+      int blo[UNR], bhi[UNR];
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int key = (kb0 + NW * u) * BC + lane;
+        blo[u] = 0;
+        bhi[u] = 0;
+        if (kb0 + NW * u < nblk && key < kv_end) {
+          const int2 x = *reinterpret_cast<const int2*>(cb + 2 * key);
+          blo[u] = x.x;
+          bhi[u] = x.y;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const int kb = kb0 + NW * u;
+        if (kb >= nblk) break;
+        const int key = kb * BC + lane;
+        const bool valid = key < kv_end;
+        // rows that may see this key: its interval, and (causal) from its
+        // place on
+        const int vlo = CAUSAL ? max(blo[u], key - off) : blo[u];
+        const int vhi = bhi[u];
+        uint32_t bits = 0;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const int r0 = q0 + 32 * w, r1 = min(r0 + 32, Nq);
+          const bool all_vis =
+              r0 >= r1 || !valid || (blo[u] <= r0 && bhi[u] >= r1);
+          if (__builtin_amdgcn_ballot_w64(all_vis) != ~0ull)
+            bits |= 1u << (16 + w);
+        }
+        const int ha1 = min(q0 + BR / 2, Nq), hb1 = min(q0 + BR, Nq);
+        if (__builtin_amdgcn_ballot_w64(valid && vlo < ha1 && vhi > q0 &&
+                                        vlo < vhi) != 0)
+          bits |= 1u << 24;
+        if (__builtin_amdgcn_ballot_w64(valid && vlo < hb1 &&
+                                        vhi > q0 + BR / 2 && vlo < vhi) != 0)
+          bits |= 1u << 25;
+        if (lane == 0) blist[kb] = kb | (int)bits;
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int cnt = 0;
+      for (int base = 0; base < nblk; base += 64) {
+        const int i = base + lane;
+        const int e = i < nblk ? blist[i] : 0;
+        const bool kept = ((e >> 24) & 3) != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
+        const int pos =
+            cnt + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
+        // (every lane has read its entry before any lane writes, and an
+        // entry moves only down, never past an unread one)
+        if (kept) blist[pos] = e;
+        cnt += (int)__builtin_popcountll(bal);
+      }
+      if (lane == 0) blist[kSparseMaxKeyBlocks] = cnt;
+    }
+    __syncthreads();
+    n_act = __builtin_amdgcn_readfirstlane(blist[kSparseMaxKeyBlocks]);
+  }
   // key block at ring position p: p itself, or the p-th listed block (past
   // the list: a block past Nk, whose copies are zeros)
   auto blk_at = [&](int p) {
-    if (!SPARSE) return p;
-    return p < n_act ? __builtin_amdgcn_readfirstlane(blist[p] & 0xFFFFFF)
+    if (!LISTED) return p;
+    return p < n_act ? __builtin_amdgcn_readfirstlane(blist[p] & BLKBITS)
                      : nblk + 1;
   };
 
@@ -542,7 +632,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const char* kp = smem + (j % L::NS) * L::KBYTES + k_rd;
     constexpr bool QK = decltype(qk_tag)::value;
     __builtin_amdgcn_s_setprio(1);
-    if (!SPARSE || (pv && qk)) {
+    if (!LISTED || (pv && qk)) {
       matrix_phase<D, true, QK>(kp, vp, qf, pk, acc, s0, s1);
     } else if (pv) {
       matrix_phase<D, true, false>(kp, vp, qf, pk, acc, s0, s1);
@@ -607,16 +697,33 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   for (int j = j0; j < n_act; ++j) {
     int jb = j;
     bool keep = true;
-    if (SPARSE) {
+    bool colm = false;  // column mask: this wave tests every key
+    if (LISTED) {
       const int e = __builtin_amdgcn_readfirstlane(blist[j]);
-      jb = e & 0xFFFFFF;
+      jb = e & BLKBITS;
       keep = (e >> (group_a ? 24 : 25)) & 1;
+      if (COLUMN) colm = keep && ((e >> (16 + wave)) & 1);
+    }
+    // the row bounds of the block's keys, one per lane, loaded before the
+    // matrix phase (keys past Nk are hidden by the limit anyway)
+    int clo = 0, chi = 0;
+    if (COLUMN && colm) {
+      const int key = jb * BC + lane;
+      if (key < Nk) {
+        const int2 x = *reinterpret_cast<const int2*>(
+            cmask.bounds + 2 * ((int64_t)b * cmask.mb + key));
+        clo = x.x;
+        chi = x.y;
+      }
     }
     mphase(j, std::true_type{}, keep_prev, keep);
     __syncthreads();
     copies(j);
-    if (SPARSE && !keep)
+    if (LISTED && !keep)
       rescale = false;  // nothing of this block enters this half's rows
+    else if (COLUMN && colm)
+      rescale = softmax_phase<true, false, true>(
+          s0, s1, lim0 - jb * BC, 0, c2, st, alpha, pk, clo, chi, qrow, h);
     else if (jb >= w_mask || (BAND && jb < w_lo))
       rescale = softmax_phase<true, BAND>(s0, s1, lim0 - jb * BC,
                                           lo0 - jb * BC, c2, st, alpha, pk);
@@ -631,7 +738,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     __syncthreads();
   }
   if (n_act > j0)  // P V of the last block
-    mphase(n_act, std::false_type{}, SPARSE ? keep_prev : true);
+    mphase(n_act, std::false_type{}, LISTED ? keep_prev : true);
   __syncthreads();
   if (group_a) __syncthreads();
 
@@ -665,10 +772,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   }
 }
 
-template <int D, int MODE, bool OUT_F32, bool SPARSE = false>
+template <int D, int MODE, bool OUT_F32, bool SPARSE = false,
+          bool COLUMN = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
                   float* lse, const Shape& s, const SeqLayout& lay, int wl,
-                  int wr, hipStream_t stream, const BlockMask& bm = {}) {
+                  int wr, hipStream_t stream, const BlockMask& bm = {},
+                  const ColMask& cm = {}) {
   const int n_qblk = (s.Nq + BR - 1) / BR;
   long long n_items = (long long)s.B * s.Hq * n_qblk;
   // packed batch: whole rounds of 8 units of G heads (the tail's surplus
@@ -682,12 +791,13 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   // below 2^-24 in magnitude, so each weight is exactly 1, and -inf scores
   // stay -inf (no 0 * inf)
   const float c2 = fmaxf(s.scale * kLog2e, 1.17549435e-38f);
-  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32, SPARSE>),
+  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32, SPARSE, COLUMN>),
                      dim3((unsigned)n_items), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, lse, s.Hq, s.Hkv,
-                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr, bm);
+                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr, bm,
+                     cm);
   return hipGetLastError();
 }
 
@@ -733,6 +843,34 @@ hipError_t launch_sparse_d(const void* q, const void* k, const void* v,
                                                 stream, bm)
                  : launch<D, kNone, false, true>(q, k, v, o, lse, s, lay, 0,
                                                  0, stream, bm);
+}
+
+template <int D>
+hipError_t launch_column_d(const void* q, const void* k, const void* v,
+                           void* o, float* lse, const Shape& s,
+                           const ColMask& cm, bool out_f32,
+                           hipStream_t stream) {
+  const SeqLayout lay = dense_layout(s);
+  if (s.causal)
+    return out_f32 ? launch<D, kCausal, true, false, true>(
+                         q, k, v, o, lse, s, lay, 0, 0, stream, {}, cm)
+                   : launch<D, kCausal, false, false, true>(
+                         q, k, v, o, lse, s, lay, 0, 0, stream, {}, cm);
+  return out_f32 ? launch<D, kNone, true, false, true>(q, k, v, o, lse, s, lay,
+                                                       0, 0, stream, {}, cm)
+                 : launch<D, kNone, false, false, true>(
+                       q, k, v, o, lse, s, lay, 0, 0, stream, {}, cm);
+}
+
+hipError_t launch_prefill_column(const void* q, const void* k, const void* v,
+                                 void* o, float* lse, const Shape& s,
+                                 const ColMask& cm, bool out_f32,
+                                 hipStream_t stream) {
+  if (s.d == 128)
+    return launch_column_d<128>(q, k, v, o, lse, s, cm, out_f32, stream);
+  if (s.d == 64)
+    return launch_column_d<64>(q, k, v, o, lse, s, cm, out_f32, stream);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_sparse(const void* q, const void* k, const void* v,

@@ -19,7 +19,7 @@ from ._lib import FA_OUT_BF16, FA_OUT_F32, check, load
 
 __all__ = ["fa_fwd", "fa_fwd_splitkv", "splitkv_workspace_bytes",
            "default_num_splits", "fa_bwd", "bwd_workspace_bytes",
-           "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged", "fa_fwd_kvlen",
+           "fa_fwd_varlen", "fa_fwd_window", "fa_fwd_paged", "fa_fwd_kvlen", "fa_fwd_colmask",
            "paged_num_splits", "fa_fwd_fp8", "fa_fwd_strided",
            "fa_fwd_block_sparse"]
 
@@ -285,6 +285,31 @@ def fa_fwd_paged(q, k_cache, v_cache, page_table, seqlens_k, causal=False,
         FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, splits,
         workspace.data_ptr(), workspace.numel(), _stream(q))
     check(st, "fa_fwd_paged")
+    return o, lse
+
+
+def fa_fwd_colmask(q, k, v, col_bounds, causal=False, scale=None,
+                   out_dtype=torch.bfloat16, o=None, lse=None):
+    """Forward with a column-interval mask through ``fa_fwd_colmask``.
+
+    col_bounds int32 [B, Nk, 2] on the device: key j of sequence b may be
+    seen by query rows col_bounds[b, j, 0] .. col_bounds[b, j, 1] - 1.
+    Returns ``(o, lse)`` shaped like ``fa_fwd``'s."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    if (not isinstance(col_bounds, torch.Tensor)
+            or col_bounds.dtype != torch.int32 or not col_bounds.is_cuda
+            or not col_bounds.is_contiguous()
+            or tuple(col_bounds.shape) != (B, Nk, 2)):
+        raise ValueError("col_bounds must be a contiguous int32 device "
+                         "tensor [B, Nk, 2]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    st = load().fa_fwd_colmask(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+        lse.data_ptr(), col_bounds.data_ptr(), B, Hq, Hkv, Nq, Nk, d,
+        int(bool(causal)), scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
+    check(st, "fa_fwd_colmask")
     return o, lse
 
 

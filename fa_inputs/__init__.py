@@ -282,3 +282,53 @@ def make_inputs(w, seed=0):
         w = workload(w)
     return make_qkv(w.B, w.Hq, w.Hkv, w.Nq, w.Nk, w.d, seed=seed,
                     outliers=w.outliers)
+
+
+def document_column_bounds(doc_lens, causal_docs=True):
+    """Column bounds [N, 2] int32 of documents packed back to back in one
+    sequence of N = sum(doc_lens) rows and keys: key j of the document
+    [s, e) is seen by rows j .. e - 1 (causal inside the document) or
+    s .. e - 1 (bidirectional)."""
+    import numpy as np
+    n = int(sum(doc_lens))
+    out = np.empty((n, 2), dtype=np.int32)
+    s = 0
+    for L in doc_lens:
+        e = s + int(L)
+        j = np.arange(s, e)
+        out[s:e, 0] = j if causal_docs else s
+        out[s:e, 1] = e
+        s = e
+    return out
+
+
+def prefix_lm_column_bounds(n, prefix):
+    """Column bounds [n, 2] int32 of a prefix-LM mask: keys of the prefix
+    seen by every row, later keys from their own row on."""
+    import numpy as np
+    j = np.arange(n)
+    return np.stack([np.where(j < prefix, 0, j), np.full(n, n)],
+                    axis=1).astype(np.int32)
+
+
+def random_column_bounds(nq, nk, *, seed=0):
+    """Column bounds [nk, 2] int32 with random row ranges inside [0, nq]
+    (some empty)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    a = rng.integers(0, nq + 1, size=nk)
+    b = rng.integers(0, nq + 1, size=nk)
+    return np.stack([np.minimum(a, b), np.maximum(a, b)],
+                    axis=1).astype(np.int32)
+
+
+def random_doc_lens(total, lo, hi, *, seed=0):
+    """Document lengths in [lo, hi] summing to ``total``."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    out, left = [], total
+    while left > 0:
+        L = int(min(left, rng.integers(lo, hi + 1)))
+        out.append(L)
+        left -= L
+    return out

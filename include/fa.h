@@ -201,6 +201,29 @@ int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
                         hipStream_t stream);
 
 /*
+ * Forward with a column-interval mask (prefill form).  "FlashAttention
+ * Analysis" and the Korean overview ("FlashAttention-2 (KO)", closing
+ * outlook) name FlashMask, an extension that expresses richer masks per key
+ * column; the pages give no representation.  Reading taken: each key
+ * column j of sequence b carries the query rows that may see it,
+ *     col_bounds  int32 [B, Nk, 2] (DEVICE): rows lo = [b][j][0] ..
+ *                 hi - 1 = [b][j][1] - 1 (an empty range hides the key),
+ * shared by the sequence's heads and applied on top of the causal flag
+ * (bottom-right alignment).  Document masks, prefix-LM masks and windows
+ * are such intervals.  q, k, v, o, lse as for fa_fwd.  The workgroup lists
+ * the 64-key blocks that any of its rows may see and skips the rest; a
+ * wave tests every key only where some key of a block is hidden from some
+ * of its rows.  Bounds are read on the device and used as given (rows
+ * outside [0, Nq) simply match no row).  Errors as for fa_fwd;
+ * FA_ERR_INVALID_ARG also for a null or not 8-byte aligned col_bounds;
+ * FA_ERR_UNSUPPORTED when Nk exceeds 8191 blocks of 64 keys.
+ */
+int fa_fwd_colmask(const void* q, const void* k, const void* v, void* o,
+                   float* lse, const int* col_bounds, int B, int Hq, int Hkv,
+                   int Nq, int Nk, int d, int causal, float scale,
+                   int out_dtype, hipStream_t stream);
+
+/*
  * Forward on strided tensors (views such as slices of a fused QKV
  * projection, [B, N, H, d] layouts, padded rows).  Each of q, k, v and o
  * is described by its element strides {batch, head, row} (a host array of

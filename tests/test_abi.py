@@ -336,6 +336,34 @@ def test_kvlen_unsupported(lib):
     assert lib.fa_last_hip_error() == 0
 
 
+def _colmask(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, cb=P, B=1, Hq=4, Hkv=2, Nq=64, Nk=64,
+             d=64, causal=1, scale=0.125, out=0)
+    a.update(kw)
+    return lib.fa_fwd_colmask(a["q"], a["k"], a["v"], a["o"], a["lse"],
+                              a["cb"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                              a["Nk"], a["d"], a["causal"], a["scale"],
+                              a["out"], None)
+
+
+COLMASK_INVALID = [
+    dict(q=None), dict(k=P + 2), dict(v=None), dict(o=P + 4), dict(lse=None),
+    dict(cb=None), dict(cb=P + 4), dict(B=0), dict(Hq=3), dict(Nq=0),
+    dict(Nk=0), dict(scale=-1.0), dict(out=3),
+]
+
+
+@pytest.mark.parametrize("kw", COLMASK_INVALID, ids=lambda k: str(k))
+def test_colmask_invalid_arguments(lib, kw):
+    assert _colmask(lib, **kw) == _lib.FA_ERR_INVALID_ARG
+
+
+def test_colmask_unsupported(lib):
+    assert _colmask(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _colmask(lib, Nk=64 * 8192) == _lib.FA_ERR_UNSUPPORTED
+    assert lib.fa_last_hip_error() == 0
+
+
 def _fp8(lib, **kw):
     a = dict(q=P, k=P, vt=P, qd=P, kd=P, vd=P, o=P, lse=P, B=1, Hq=4, Hkv=2,
              Nq=16, Nk=16, ldv=64, d=128, causal=0, scale=0.125, out=0)

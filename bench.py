@@ -29,6 +29,10 @@ with E4M3 inputs and reports TFLOP/s against the FP8 matrix-core peak.
 ``--workload gqa_prefill_sparse`` runs ``fa_fwd_block_sparse`` on the GQA
 prefill with a seeded block mask (a quarter of the 128 x 64 blocks plus the
 diagonal), priced at the visible pairs of the kept blocks.
+``--workload gqa_prefill_docmask`` runs ``fa_fwd_colmask`` on the GQA
+prefill's shape with the 8192 tokens split into causal documents of seeded
+lengths in [300, 2500] (a column-interval mask), priced at the exact visible
+pairs.
 ``--workload varlen_prefill`` runs ``fa_fwd_varlen`` over a packed batch of
 causal prompts (seeded log-uniform lengths in [256, 8192], 32768 tokens,
 the GQA heads above), priced at the causal FLOPs of each sequence.
@@ -51,21 +55,23 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from fa_inputs import (VARLEN_PREFILL, make_dout, make_fp8,  # noqa: E402
-                       make_inputs, make_paged, make_varlen,
-                       sparse_block_mask, varlen_lengths, workload)
+from fa_inputs import (VARLEN_PREFILL, document_column_bounds,  # noqa: E402
+                       make_dout, make_fp8, make_inputs, make_paged,
+                       make_varlen, random_doc_lens, sparse_block_mask,
+                       varlen_lengths, workload)
 from exact_io_aware_05_amd.metrics import (  # noqa: E402
     PEAK_BF16_MFMA_TFLOPS, PEAK_FP8_MFMA_TFLOPS, PEAK_HBM_GBS,
     attention_bwd_flops,
     attention_fwd_bytes, attention_fwd_flops, attention_window_flops,
-    block_pair_counts, visible_keys)
+    block_pair_counts, column_mask_pairs, visible_keys)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak (causal GQA d=128 N=8192)"
 WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "tiny": 0, "gqa_prefill_bwd": 3, "varlen_prefill": None,
              "gqa_prefill_window": 3, "decode_window": 4,
              "gqa_prefill_window_bwd": 3, "decode_paged": None,
-             "gqa_prefill_fp8": None, "gqa_prefill_sparse": None}
+             "gqa_prefill_fp8": None, "gqa_prefill_sparse": None,
+             "gqa_prefill_docmask": None}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
 # (and fa_bwd_window)
 WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
@@ -525,6 +531,80 @@ def bench_sparse(args):
     return 0
 
 
+DOCMASK_LENS = (300, 2500)
+
+
+def bench_docmask(args):
+    """One fa_fwd_colmask call on the GQA prefill's shape, the tokens split
+    into causal documents (a column-interval mask), priced at 4 d FLOPs per
+    visible pair."""
+    import torch
+    from exact_io_aware_05_amd import ops
+    w = workload(3)
+    q, k, v = make_inputs(w, seed=0)
+    lens = random_doc_lens(w.Nk, *DOCMASK_LENS, seed=0)
+    cb = np.ascontiguousarray(document_column_bounds(lens)[None])
+    Q, K, V = _dev_tensor(q), _dev_tensor(k), _dev_tensor(v)
+    CB = torch.from_numpy(cb).cuda()
+    o = torch.empty((w.B, w.Hq, w.Nq, w.d), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((w.B, w.Hq, w.Nq), dtype=torch.float32, device="cuda")
+
+    def step():
+        ops.fa_fwd_colmask(Q, K, V, CB, causal=w.causal, scale=w.scale, o=o,
+                           lse=lse)
+
+    ms, kern_ms = _time_steps(step, args.steps, args.warmup,
+                              torch.cuda.current_stream())
+    pairs = column_mask_pairs(cb[0], w.Nq, w.Nk, w.causal)
+    flops = 4.0 * w.d * w.B * w.Hq * pairs
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    name = w.name + "_docmask"
+    out = {
+        "metric": f"attn fwd TFLOP/s ({name})",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) fp32 rounded to bf16; seeded "
+                "document lengths)",
+        "config": {"workload": name, "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "Nq": w.Nq, "Nk": w.Nk, "d": w.d, "causal": w.causal,
+                   "scale": w.scale, "documents": len(lens),
+                   "doc_len_range": list(DOCMASK_LENS),
+                   "visible_pair_fraction": round(
+                       pairs / float(w.Nq * (w.Nq + 1) // 2), 4),
+                   "out_dtype": "bf16", "kernel_ms": round(kern_ms, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+                     "traffic": measured_traffic(name)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        from fa_inputs import bf16_bits_to_f64
+        from oracle import reference_attention
+        G = w.Hq // w.Hkv
+        t_total, done = 0.0, 0
+        while done < w.Hq and t_total < 10.0:
+            h = done
+            t0 = time.perf_counter()
+            reference_attention(bf16_bits_to_f64(q[:1, h:h + 1]),
+                                bf16_bits_to_f64(k[:1, h // G:h // G + 1]),
+                                bf16_bits_to_f64(v[:1, h // G:h // G + 1]),
+                                causal=w.causal,
+                                scale=float(np.float32(w.scale)),
+                                col_bounds=cb)
+            t_total += time.perf_counter() - t0
+            done += 1
+        out["cpu_baseline"] = {
+            "value": round(4.0 * w.d * pairs * done / t_total / 1e12, 6),
+            "unit": "TFLOP/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
+                      f"float64 numpy; {t_total:.1f} s"}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -560,6 +640,8 @@ def main(argv=None):
         return bench_fp8(args)
     if args.workload == "gqa_prefill_sparse":
         return bench_sparse(args)
+    if args.workload == "gqa_prefill_docmask":
+        return bench_docmask(args)
     w = workload(WORKLOADS[args.workload])
     backward = args.workload.endswith("_bwd")
     window = WINDOWS.get(args.workload)

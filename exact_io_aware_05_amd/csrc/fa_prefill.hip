@@ -235,32 +235,27 @@ __device__ __forceinline__ void matrix_phase(const char* kp,
 // The rounded weights feed P V and their own row sum lb, so O = acc / lb
 // is an exact convex combination of V rows up to fp32 summation; the fp32
 // sum l of the unrounded weights gives lse.
-// With COL, a column-interval mask as well: lane l of the wave holds the
-// row bounds [clo, chi) of key l of the block, read across lanes for each
-// of this lane's keys (key + 8 hh of the block) and tested against `row`.
+// With COL, a column-interval mask as well: bit i of `cbits` hides this
+// lane's key of score register i (i < 16: s0, else s1 register i - 16).
 template <bool MASK, bool LOWER = false, bool COL = false>
 __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
                                               const f32x16& s1, int lim,
                                               int lo, float c2, RowState& st,
                                               float& alpha, u32x4* pk,
-                                              int clo = 0, int chi = 0,
-                                              int row = 0, int hh = 0) {
+                                              uint32_t cbits = 0) {
   // The mask never overwrites the score registers (that would make the
   // masked and unmasked variants rejoin with copies): hidden keys are left
   // out of the max and get weight 0 after the exponential.
-  auto col_hidden = [&](int key) {
-    const int l0 = __builtin_amdgcn_readlane(clo, key);
-    const int l1 = __builtin_amdgcn_readlane(clo, key + 8);
-    const int h0 = __builtin_amdgcn_readlane(chi, key);
-    const int h1 = __builtin_amdgcn_readlane(chi, key + 8);
-    return row < (hh ? l1 : l0) || row >= (hh ? h1 : h0);
-  };
   auto hidden = [&](int key) {
-    return (MASK && (key > lim || (LOWER && key < lo))) ||
-           (COL && col_hidden(key));
+    return MASK && (key > lim || (LOWER && key < lo));
   };
-  auto hide0 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7)); };
-  auto hide1 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7) + 32); };
+  auto hide0 = [&](int r) {
+    return hidden(16 * (r >> 3) + (r & 7)) | (COL && ((cbits >> r) & 1u));
+  };
+  auto hide1 = [&](int r) {
+    return hidden(16 * (r >> 3) + (r & 7) + 32) |
+           (COL && ((cbits >> (16 + r)) & 1u));
+  };
   // weights p = 2^(s c2 - msub) (0 for hidden keys), rounded to bf16 once
   // into pk; partial sums of the fp32 and of the rounded weights
   auto weights = [&](float msub, float* rs, float* rb) {
@@ -721,9 +716,22 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     copies(j);
     if (LISTED && !keep)
       rescale = false;  // nothing of this block enters this half's rows
-    else if (COLUMN && colm)
-      rescale = softmax_phase<true, false, true>(
-          s0, s1, lim0 - jb * BC, 0, c2, st, alpha, pk, clo, chi, qrow, h);
+    else if (COLUMN && colm) {
+      // this lane's 32 keys against its row: key 16 (i / 8 % 2) + i % 8
+      // + 8 h (+ 32 for i >= 16) of the block, its bounds fetched from the
+      // lane that loaded them
+      uint32_t cbits = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int r = i & 15;
+        const int key = 16 * (r >> 3) + (r & 7) + 8 * h + 32 * (i >> 4);
+        const int klo = __builtin_amdgcn_ds_bpermute(4 * key, clo);
+        const int khi = __builtin_amdgcn_ds_bpermute(4 * key, chi);
+        cbits |= (uint32_t)((qrow < klo) | (qrow >= khi)) << i;
+      }
+      rescale = softmax_phase<true, false, true>(s0, s1, lim0 - jb * BC, 0,
+                                                 c2, st, alpha, pk, cbits);
+    }
     else if (jb >= w_mask || (BAND && jb < w_lo))
       rescale = softmax_phase<true, BAND>(s0, s1, lim0 - jb * BC,
                                           lo0 - jb * BC, c2, st, alpha, pk);

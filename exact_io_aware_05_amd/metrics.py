@@ -65,6 +65,19 @@ def block_pair_counts(Nq, Nk, causal, block_size):
     return out
 
 
+def column_mask_pairs(bounds, Nq, Nk, causal) -> int:
+    """Visible (query row, key) pairs of one head under a column-interval
+    mask: key j (``bounds[j] = (lo, hi)``) is seen by rows lo .. hi - 1,
+    from its causal place j - (Nk - Nq) on when causal."""
+    import numpy as np
+    b = np.asarray(bounds, dtype=np.int64)
+    lo = np.maximum(b[:, 0], 0)
+    if causal:
+        lo = np.maximum(lo, np.arange(Nk, dtype=np.int64) - (Nk - Nq))
+    hi = np.minimum(b[:, 1], Nq)
+    return int(np.maximum(hi - lo, 0).sum())
+
+
 def attention_window_flops(B, Hq, Nq, Nk, d, causal, window) -> float:
     """Forward FLOPs of a windowed mask: 4 d per visible pair (the two
     products), counted exactly."""

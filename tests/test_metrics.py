@@ -121,3 +121,18 @@ def test_block_pair_counts_brute_force():
                     if not causal or j <= i + Nk - Nq:
                         want[i // bs[0], j // bs[1]] += 1
             assert np.array_equal(got, want), (Nq, Nk, bs, causal)
+
+
+def test_column_mask_pairs_brute_force():
+    import numpy as np
+    from exact_io_aware_05_amd.metrics import column_mask_pairs
+    rng = np.random.default_rng(3)
+    for Nq, Nk in ((7, 7), (5, 9), (9, 4)):
+        a = rng.integers(-2, Nq + 3, size=Nk)
+        c = rng.integers(-2, Nq + 3, size=Nk)
+        b = np.stack([np.minimum(a, c), np.maximum(a, c)], axis=1)
+        for causal in (False, True):
+            want = sum(1 for i in range(Nq) for j in range(Nk)
+                       if b[j, 0] <= i < b[j, 1]
+                       and (not causal or j <= i + Nk - Nq))
+            assert column_mask_pairs(b, Nq, Nk, causal) == want

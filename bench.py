@@ -88,20 +88,24 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
-        "fetch_kib": 71236.5, "write_kib": 66560.3},
+        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "fetch_kib": 71225.5, "write_kib": 66560.0},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
-        "fetch_kib": 514062.5, "write_kib": 266357.3},
+        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "fetch_kib": 514061.6, "write_kib": 266356.0},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
-        "fetch_kib": 67524.3, "write_kib": 66560.7},
+        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "fetch_kib": 67564.8, "write_kib": 66565.5},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "3e51daa7ec8386f724fb47f26b08b61829efb9b3318f5ef037012c2e3f912ddb",
-        "fetch_kib": 73441.2, "write_kib": 70658.1},
+        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "fetch_kib": 73478.6, "write_kib": 70657.9},
+    "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
+        "source": "fa_prefill.hip",
+        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "fetch_kib": 56167.0, "write_kib": 80295.4},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
         "sha256": "33d71c45690d58cf5b66d4391cc8ffa33d06f4507deed0898e04e71093e312ae",

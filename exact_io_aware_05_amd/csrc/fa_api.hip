@@ -26,7 +26,7 @@ bool aligned16(const void* p) {
 // Checks shared by both forward entry points; pure host arithmetic.
 int check_common(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
-                 int d, float scale, int out_dtype) {
+                 int d, float scale, int out_dtype, bool decode = false) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
@@ -37,7 +37,8 @@ int check_common(const void* q, const void* k, const void* v, const void* o,
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (out_dtype != FA_OUT_BF16 && out_dtype != FA_OUT_F32)
     return FA_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  // (the KV-split form also takes d = 256)
+  if (d != 64 && d != 128 && !(decode && d == 256)) return FA_ERR_UNSUPPORTED;
   // element counts must stay well inside 64-bit offsets and 32-bit rows
   const long long rows_q = (long long)B * Hq * Nq;
   const long long rows_k = (long long)B * Hkv * Nk;
@@ -121,7 +122,7 @@ size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) 
 
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv) return 0;
-  if (d != 64 && d != 128) return 0;
+  if (d != 64 && d != 128 && d != 256) return 0;
   return default_splits(B, Hq, Hkv, Nq, Nk);
 }
 
@@ -131,7 +132,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                    void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype);
+                        out_dtype, true);
   if (st != FA_OK) return st;
   if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
@@ -207,7 +208,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
 int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
                         int max_pages_per_seq) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Hq % Hkv) return 0;
-  if (d != 64 && d != 128) return 0;
+  if (d != 64 && d != 128 && d != 256) return 0;
   if (page_size < fa::kSplitKeys || (page_size & (page_size - 1)) ||
       max_pages_per_seq < 1)
     return 0;
@@ -243,7 +244,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
   const long long nk = (long long)page_size * max_pages_per_seq;
   if (nk > (1LL << 30)) return FA_ERR_UNSUPPORTED;
   int st = check_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, (int)nk,
-                        d, scale, out_dtype);
+                        d, scale, out_dtype, true);
   if (st != FA_OK) return st;
   if ((long long)num_pages * page_size * Hkv * d > (1LL << 46))
     return FA_ERR_UNSUPPORTED;
@@ -287,7 +288,7 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
   if (!seqlens_k || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return FA_ERR_INVALID_ARG;
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype);
+                        out_dtype, true);
   if (st != FA_OK) return st;
   // one K or V head is addressed with 32-bit byte offsets
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;

@@ -48,7 +48,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // operand chunk of 16 different rows then hit 16 different bank groups.
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
-  return D == 128 ? (r & 15) : ((r >> 1) & 7);
+  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
 }
 
 // Per-wave state of one 32-key block: K copied HBM -> LDS by buffer_load
@@ -92,7 +92,12 @@ struct KvRegs {
       for (int e = 0; e < 8; ++e) {
         const int vrow = kb + 16 * s + 8 * h + e;
         const int off = vrow * (2 * D) + 2 * CPL * col;
-        if (CPL == 4) {
+        if (CPL == 8) {
+          const u32x4 x = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStreamAux));
+#pragma unroll
+          for (int c = 0; c < CPL / 2; ++c) vr[s][e][c] = x[c];
+        } else if (CPL == 4) {
           const u32x2 x = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
           vr[s][e][0] = x[0];
@@ -128,7 +133,12 @@ struct KvRegs {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int off = (16 * s + 8 * h + e) * rs + 2 * CPL * col;
-        if (CPL == 4) {
+        if (CPL == 8) {
+          const u32x4 x = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, kStreamAux));
+#pragma unroll
+          for (int c = 0; c < CPL / 2; ++c) vr[s][e][c] = x[c];
+        } else if (CPL == 4) {
           const u32x2 x = __builtin_bit_cast(
               u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
           vr[s][e][0] = x[0];
@@ -288,7 +298,8 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   // step is HBM-bound, and one wave per SIMD needs that many bytes in
   // flight to cover the memory latency).  The loop is unrolled by PF so
   // that every buffer index is a compile-time constant.
-  constexpr int PF = 4;
+  // (d = 256: two buffers, so that the four waves' K slots fit in LDS)
+  constexpr int PF = D == 256 ? 2 : 4;
   using KV = KvRegs<D>;
   __shared__ __attribute__((aligned(1024))) char kring[NT / 64][PF][KV::KBYTES];
   char (*slots)[KV::KBYTES] = kring[wave];
@@ -411,10 +422,12 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int a = 8 * gg + 4 * h + e;  // operand row -> columns CPL*a + tt
-        if (CPL == 4) {
-          *reinterpret_cast<f32x4*>(op + 4 * a) =
-              f32x4{acc[0][4 * gg + e], acc[1][4 * gg + e],
-                    acc[2][4 * gg + e], acc[3][4 * gg + e]};
+        if (CPL >= 4) {
+#pragma unroll
+          for (int c = 0; c < CPL; c += 4)
+            *reinterpret_cast<f32x4*>(op + CPL * a + c) =
+                f32x4{acc[c][4 * gg + e], acc[c + 1][4 * gg + e],
+                      acc[c + 2][4 * gg + e], acc[c + 3][4 * gg + e]};
         } else {
           *reinterpret_cast<float2*>(op + CPL * a) =
               float2{acc[0][4 * gg + e], acc[CPL - 1][4 * gg + e]};
@@ -459,7 +472,11 @@ __global__ __launch_bounds__(NT) void splitkv_merge_kernel(
     for (int i = 0; i < CPL; ++i) dst[i] = a[i] * inv;
   } else {
     uint16_t* dst = static_cast<uint16_t*>(o) + row * D + CPL * lane;
-    if (CPL == 2) {
+    if (CPL == 4) {
+      *reinterpret_cast<u32x2*>(dst) =
+          u32x2{pack_bf16x2(a[0] * inv, a[1] * inv),
+                pack_bf16x2(a[2] * inv, a[CPL - 1] * inv)};
+    } else if (CPL == 2) {
       *reinterpret_cast<uint32_t*>(dst) = pack_bf16x2(a[0] * inv, a[CPL - 1] * inv);
     } else {
       const uint32_t pk = pack_bf16x2(a[0] * inv, 0.f);
@@ -531,6 +548,9 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
                           int num_splits, void* workspace,
                           hipStream_t stream) {
   const PagedKv none{};
+  if (s.d == 256)
+    return launch_d<256, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                                workspace, none, stream);
   if (s.d == 128)
     return launch_d<128, false>(q, k, v, o, lse, s, out_f32, num_splits,
                                 workspace, none, stream);
@@ -547,6 +567,9 @@ hipError_t launch_splitkv_kvlen(const void* q, const void* k, const void* v,
                                 hipStream_t stream) {
   PagedKv lens{};
   lens.seqlen = seqlen;
+  if (s.d == 256)
+    return launch_d<256, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                                workspace, lens, stream);
   if (s.d == 128)
     return launch_d<128, false>(q, k, v, o, lse, s, out_f32, num_splits,
                                 workspace, lens, stream);
@@ -561,6 +584,9 @@ hipError_t launch_splitkv_paged(const void* q, const void* k_cache,
                                 const Shape& s, const PagedKv& pg,
                                 bool out_f32, int num_splits, void* workspace,
                                 hipStream_t stream) {
+  if (s.d == 256)
+    return launch_d<256, true>(q, k_cache, v_cache, o, lse, s, out_f32,
+                               num_splits, workspace, pg, stream);
   if (s.d == 128)
     return launch_d<128, true>(q, k_cache, v_cache, o, lse, s, out_f32,
                                num_splits, workspace, pg, stream);

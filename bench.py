@@ -29,6 +29,8 @@ with E4M3 inputs and reports TFLOP/s against the FP8 matrix-core peak.
 ``--workload gqa_prefill_sparse`` runs ``fa_fwd_block_sparse`` on the GQA
 prefill with a seeded block mask (a quarter of the 128 x 64 blocks plus the
 diagonal), priced at the visible pairs of the kept blocks.
+``--workload decode_d256`` runs the decode with head dimension 256 over
+16384 keys (the same K/V bytes as the decode workload).
 ``--workload gqa_prefill_docmask`` runs ``fa_fwd_colmask`` on the GQA
 prefill's shape with the 8192 tokens split into causal documents of seeded
 lengths in [300, 2500] (a column-interval mask), priced at the exact visible
@@ -43,6 +45,7 @@ added one at a time until about 10 s of CPU work has been done.
 """
 from __future__ import annotations
 
+import dataclasses
 import argparse
 import json
 import math
@@ -71,7 +74,11 @@ WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "gqa_prefill_window": 3, "decode_window": 4,
              "gqa_prefill_window_bwd": 3, "decode_paged": None,
              "gqa_prefill_fp8": None, "gqa_prefill_sparse": None,
-             "gqa_prefill_docmask": None}
+             "gqa_prefill_docmask": None, "decode_d256": 4}
+# workloads that change one configuration's shape: head dimension 256 on
+# the decode (half the keys, so the same K/V bytes)
+VARIANTS = {"decode_d256": dict(name="decode_b16_hq32_hkv8_nq1_nk16384_d256",
+                                Nk=16384, d=256, scale=0.0625)}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
 # (and fa_bwd_window)
 WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
@@ -113,15 +120,19 @@ MEASURED_TRAFFIC = {
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "ef12408f9af29c548d316dc8a2310238f53e8fa1f08c46915755d881a86153f8",
-        "fetch_kib": 1048893.6, "write_kib": 2112.0},
+        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
+        "fetch_kib": 1048895.8, "write_kib": 2112.0},
+    "decode_b16_hq32_hkv8_nq1_nk16384_d256": {
+        "source": "fa_splitkv.hip",
+        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
+        "fetch_kib": 1050162.6, "write_kib": 6720.1},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "ef12408f9af29c548d316dc8a2310238f53e8fa1f08c46915755d881a86153f8",
-        "fetch_kib": 132412.9, "write_kib": 2112.0},
+        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
+        "fetch_kib": 132424.3, "write_kib": 2112.0},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "ef12408f9af29c548d316dc8a2310238f53e8fa1f08c46915755d881a86153f8",
+        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
         "fetch_kib": 1048927.8, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
@@ -647,6 +658,8 @@ def main(argv=None):
     if args.workload == "gqa_prefill_docmask":
         return bench_docmask(args)
     w = workload(WORKLOADS[args.workload])
+    if args.workload in VARIANTS:
+        w = dataclasses.replace(w, **VARIANTS[args.workload])
     backward = args.workload.endswith("_bwd")
     window = WINDOWS.get(args.workload)
     q, k, v = make_inputs(w, seed=0)

@@ -37,8 +37,9 @@ int check_common(const void* q, const void* k, const void* v, const void* o,
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (out_dtype != FA_OUT_BF16 && out_dtype != FA_OUT_F32)
     return FA_ERR_INVALID_ARG;
-  // (the KV-split form also takes d = 256)
-  if (d != 64 && d != 128 && !(decode && d == 256)) return FA_ERR_UNSUPPORTED;
+  // (the KV-split form also takes d = 32 and 256)
+  if (d != 64 && d != 128 && !(decode && (d == 32 || d == 256)))
+    return FA_ERR_UNSUPPORTED;
   // element counts must stay well inside 64-bit offsets and 32-bit rows
   const long long rows_q = (long long)B * Hq * Nq;
   const long long rows_k = (long long)B * Hkv * Nk;
@@ -122,7 +123,7 @@ size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) 
 
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv) return 0;
-  if (d != 64 && d != 128 && d != 256) return 0;
+  if (d != 32 && d != 64 && d != 128 && d != 256) return 0;
   return default_splits(B, Hq, Hkv, Nq, Nk);
 }
 
@@ -208,7 +209,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
 int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
                         int max_pages_per_seq) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Hq % Hkv) return 0;
-  if (d != 64 && d != 128 && d != 256) return 0;
+  if (d != 32 && d != 64 && d != 128 && d != 256) return 0;
   if (page_size < fa::kSplitKeys || (page_size & (page_size - 1)) ||
       max_pages_per_seq < 1)
     return 0;

@@ -48,7 +48,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // operand chunk of 16 different rows then hit 16 different bank groups.
 template <int D>
 __device__ __forceinline__ int kswz(int r) {
-  return D >= 128 ? (r & 15) : ((r >> 1) & 7);
+  return D >= 128 ? (r & 15) : D == 64 ? ((r >> 1) & 7) : ((r >> 1) & 3);
 }
 
 // Per-wave state of one 32-key block: K copied HBM -> LDS by buffer_load
@@ -63,7 +63,7 @@ struct KvRegs {
   static constexpr int RPK = 1024 / (2 * D);  // K rows per instruction
   static constexpr int OPS = NI + 16;         // loads per block
   // V: [k-step s][row e] -> CPL bf16 values (CPL/2 dwords)
-  uint32_t vr[2][8][CPL / 2];
+  uint32_t vr[2][8][CPL >= 2 ? CPL / 2 : 1];
 
   // source offset of this lane within copy instruction i: row RPK i +
   // lane / CPR of the block, the chunk that the swizzle puts at lane % CPR
@@ -102,9 +102,12 @@ struct KvRegs {
               u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
           vr[s][e][0] = x[0];
           vr[s][e][CPL / 2 - 1] = x[1];
-        } else {
+        } else if (CPL == 2) {
           vr[s][e][0] =
               __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, kStreamAux);
+        } else {
+          vr[s][e][0] =
+              __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, kStreamAux);
         }
       }
     }
@@ -143,9 +146,12 @@ struct KvRegs {
               u32x2, __builtin_amdgcn_raw_buffer_load_b64(vrs, off, 0, kStreamAux));
           vr[s][e][0] = x[0];
           vr[s][e][CPL / 2 - 1] = x[1];
-        } else {
+        } else if (CPL == 2) {
           vr[s][e][0] =
               __builtin_amdgcn_raw_buffer_load_b32(vrs, off, 0, kStreamAux);
+        } else {
+          vr[s][e][0] =
+              __builtin_amdgcn_raw_buffer_load_b16(vrs, off, 0, kStreamAux);
         }
       }
     }
@@ -428,9 +434,11 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
             *reinterpret_cast<f32x4*>(op + CPL * a + c) =
                 f32x4{acc[c][4 * gg + e], acc[c + 1][4 * gg + e],
                       acc[c + 2][4 * gg + e], acc[c + 3][4 * gg + e]};
-        } else {
+        } else if (CPL == 2) {
           *reinterpret_cast<float2*>(op + CPL * a) =
               float2{acc[0][4 * gg + e], acc[CPL - 1][4 * gg + e]};
+        } else {
+          op[a] = acc[0][4 * gg + e];
         }
       }
     }
@@ -438,14 +446,16 @@ __global__ __launch_bounds__(NT, 1) void splitkv_partial_kernel(
   }
 }
 
-// One wave per output row; each lane owns D/64 columns.
+// One wave per output row; each lane owns D/64 columns (d = 32: lanes
+// 0..31 one column each, the others idle).
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(NT) void splitkv_merge_kernel(
     const float* __restrict__ ws_o, const f32x4* __restrict__ ws_ml,
     void* __restrict__ o, float* __restrict__ lse, long long n_rows,
     int num_splits) {
-  constexpr int CPL = D / 64;
+  constexpr int CPL = D >= 64 ? D / 64 : 1;
   const int lane = threadIdx.x & 63;
+  const bool has_col = CPL * lane < D;
   const long long row = (long long)blockIdx.x * (NT / 64) + (threadIdx.x >> 6);
   if (row >= n_rows) return;
   const f32x4* ml = ws_ml + row * num_splits;
@@ -463,10 +473,13 @@ __global__ __launch_bounds__(NT) void splitkv_merge_kernel(
     L += w * x[1];
     LB += w * x[2];
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) a[i] += w * op[(int64_t)s * D + i];
+    for (int i = 0; i < CPL; ++i)
+      if (has_col) a[i] += w * op[(int64_t)s * D + i];
   }
   const float inv = LB > 0.f ? 1.f / LB : 0.f;
-  if (OUT_F32) {
+  if (!has_col) {
+    // no column of this row for this lane
+  } else if (OUT_F32) {
     float* dst = static_cast<float*>(o) + row * D + CPL * lane;
 #pragma unroll
     for (int i = 0; i < CPL; ++i) dst[i] = a[i] * inv;
@@ -557,6 +570,9 @@ hipError_t launch_splitkv(const void* q, const void* k, const void* v,
   if (s.d == 64)
     return launch_d<64, false>(q, k, v, o, lse, s, out_f32, num_splits,
                                workspace, none, stream);
+  if (s.d == 32)
+    return launch_d<32, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                               workspace, none, stream);
   return hipErrorInvalidValue;
 }
 
@@ -576,6 +592,9 @@ hipError_t launch_splitkv_kvlen(const void* q, const void* k, const void* v,
   if (s.d == 64)
     return launch_d<64, false>(q, k, v, o, lse, s, out_f32, num_splits,
                                workspace, lens, stream);
+  if (s.d == 32)
+    return launch_d<32, false>(q, k, v, o, lse, s, out_f32, num_splits,
+                               workspace, lens, stream);
   return hipErrorInvalidValue;
 }
 
@@ -592,6 +611,9 @@ hipError_t launch_splitkv_paged(const void* q, const void* k_cache,
                                num_splits, workspace, pg, stream);
   if (s.d == 64)
     return launch_d<64, true>(q, k_cache, v_cache, o, lse, s, out_f32,
+                              num_splits, workspace, pg, stream);
+  if (s.d == 32)
+    return launch_d<32, true>(q, k_cache, v_cache, o, lse, s, out_f32,
                               num_splits, workspace, pg, stream);
   return hipErrorInvalidValue;
 }

@@ -1,5 +1,5 @@
-"""Head dimension 256 in the KV-split (decode) form against the float64
-oracles: the contiguous call (several split counts, causal, several
+"""Head dimensions 32 and 256 in the KV-split (decode) form against the
+float64 oracles: the contiguous call (several split counts, causal, several
 queries per sequence, GQA), a paged cache and a padded cache of unequal
 lengths (NaN padding), and a sliding window."""
 import numpy as np
@@ -13,8 +13,11 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 
-D = 256
-SCALE = float(np.float32(1.0 / np.sqrt(D)))
+DIMS = [32, 256]
+
+
+def _scale(D):
+    return float(np.float32(1.0 / np.sqrt(D)))
 
 
 def _ops():
@@ -31,11 +34,13 @@ CASES = [(2, 8, 2, 1, 1000, False, 4), (1, 4, 4, 3, 777, True, 1),
          (2, 16, 4, 4, 2048, True, 7), (3, 8, 8, 1, 65, False, 2)]
 
 
+@pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"B{c[0]}h{c[1]}/{c[2]}q{c[3]}k{c[4]}"
                          f"{'-causal' if c[5] else ''}-s{c[6]}")
-def test_splitkv_d256_matches_oracle(case):
+def test_splitkv_dims_match_oracle(case, D):
     B, Hq, Hkv, Nq, Nk, causal, splits = case
-    print(f"d256 splitkv {case}", flush=True)
+    SCALE = _scale(D)
+    print(f"d{D} splitkv {case}", flush=True)
     q, k, v = make_qkv(B, Hq, Hkv, Nq, Nk, D, seed=71)
     ops = _ops()
     o32, l32 = ops.fa_fwd_splitkv(dev(q), dev(k), dev(v), splits,
@@ -48,13 +53,15 @@ def test_splitkv_d256_matches_oracle(case):
     assert torch.equal(l32, l16)
     O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=causal,
                                        scale=SCALE)
-    compare(host(o32), host(l32), O_ref, L_ref, what=f"d256 {case}")
+    compare(host(o32), host(l32), O_ref, L_ref, what=f"d{D} {case}")
 
 
-def test_paged_d256_matches_oracle():
+@pytest.mark.parametrize("D", DIMS)
+def test_paged_dims_match_oracle(D):
+    SCALE = _scale(D)
     B, Hq, Hkv, Nq, P, maxp = 3, 8, 2, 2, 64, 10
     lens = [1, 400, 640]
-    print("d256 paged", flush=True)
+    print(f"d{D} paged", flush=True)
     q, kc, vc, table, sl = make_paged(B, Hq, Hkv, Nq, D, P, maxp, lens,
                                       seed=72)
     o, lse = _ops().fa_fwd_paged(dev(q), dev(kc), dev(vc), _i32(table),
@@ -63,14 +70,16 @@ def test_paged_d256_matches_oracle():
     torch.cuda.synchronize()
     O_ref, L_ref = paged_attention(f64(q), f64(kc), f64(vc), table, sl,
                                    causal=True, scale=SCALE)
-    compare(host(o), host(lse), O_ref, L_ref, what="d256 paged")
+    compare(host(o), host(lse), O_ref, L_ref, what=f"d{D} paged")
 
 
+@pytest.mark.parametrize("D", DIMS)
 @pytest.mark.parametrize("window", [(-1, -1), (200, 0)])
-def test_kvlen_d256_matches_oracle(window):
+def test_kvlen_dims_match_oracle(window, D):
+    SCALE = _scale(D)
     B, Hq, Hkv, Nq, Nk = 3, 8, 2, 2, 900
     lens = [900, 0, 333]
-    print(f"d256 kvlen {window}", flush=True)
+    print(f"d{D} kvlen {window}", flush=True)
     q, k, v = make_qkv(B, Hq, Hkv, Nq, Nk, D, seed=73)
     k, v = k.copy(), v.copy()
     for b, n in enumerate(lens):
@@ -82,4 +91,4 @@ def test_kvlen_d256_matches_oracle(window):
     torch.cuda.synchronize()
     O_ref, L_ref = kvlen_attention(f64(q), f64(k), f64(v), lens, causal=True,
                                    scale=SCALE, window=window)
-    compare(host(o), host(lse), O_ref, L_ref, what=f"d256 kvlen {window}")
+    compare(host(o), host(lse), O_ref, L_ref, what=f"d{D} kvlen {window}")

@@ -120,20 +120,20 @@ MEASURED_TRAFFIC = {
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
-        "fetch_kib": 1048895.8, "write_kib": 2112.0},
+        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "fetch_kib": 1048879.2, "write_kib": 2112.0},
     "decode_b16_hq32_hkv8_nq1_nk16384_d256": {
         "source": "fa_splitkv.hip",
-        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
-        "fetch_kib": 1050162.6, "write_kib": 6720.1},
+        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "fetch_kib": 1050163.8, "write_kib": 6720.2},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
-        "fetch_kib": 132424.3, "write_kib": 2112.0},
+        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "fetch_kib": 132424.4, "write_kib": 2112.1},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "d145c27a7c9019a71e0498ad0c9c257a6b32ec288ef6a424b305b6586ec58480",
-        "fetch_kib": 1048927.8, "write_kib": 2112.0},
+        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "fetch_kib": 1048925.9, "write_kib": 2112.1},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",

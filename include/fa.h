@@ -39,7 +39,7 @@
  *   lse = -inf.
  * - scale must be finite and >= 0 (1/sqrt(d) is the usual value).
  * - d must be 64 or 128; the KV-split entry points (fa_fwd_splitkv,
- *   fa_fwd_paged, fa_fwd_kvlen) also take d = 256.
+ *   fa_fwd_paged, fa_fwd_kvlen) also take d = 32 and d = 256.
  * - Every call is asynchronous: it validates its arguments on the host,
  *   enqueues kernels on `stream` and returns.  Results are valid once the
  *   stream has been synchronised; buffers must stay alive until then.
@@ -108,7 +108,8 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
  * fa_splitkv_workspace_bytes(B, Hq, Nq, d, num_splits) bytes, 16-byte
  * aligned; its contents on entry do not matter and on return are scratch.
  * num_splits must be in [1, 4096].  Nk * d * 2 must stay below 2^31, as
- * for fa_fwd (FA_ERR_UNSUPPORTED otherwise).  d may be 64, 128 or 256.
+ * for fa_fwd (FA_ERR_UNSUPPORTED otherwise).  d may be 32, 64, 128 or
+ * 256.
  */
 size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d,
                                   int num_splits);

@@ -88,30 +88,31 @@ WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
 # dispatch; summaries under profiles/).  Each counter is scaled by what it
 # reads for a plain device copy of known size (``--calibrate-copy``): a
 # 1 GiB copy reads FETCH_SIZE = 524301 KiB and WRITE_SIZE = 1048576 KiB.
-# A figure is reported only while the kernel source still hashes to the
-# value it was taken on; otherwise traffic is null.
+# A figure is reported only while the kernel source and the headers it
+# includes still hash to the value it was taken on; otherwise traffic is
+# null.
 FETCH_SCALE = 1048576.0 / 524301.0
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
         "fetch_kib": 71225.5, "write_kib": 66560.0},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
         "fetch_kib": 514061.6, "write_kib": 266356.0},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
         "fetch_kib": 67564.8, "write_kib": 66565.5},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
         "fetch_kib": 73478.6, "write_kib": 70657.9},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "79eaa0c7e1578c8507f16c460177a6b1be77c9697d394c3d7427b25497e32a1a",
+        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
         "fetch_kib": 56167.0, "write_kib": 80295.4},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
@@ -120,19 +121,19 @@ MEASURED_TRAFFIC = {
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
         "fetch_kib": 1048879.2, "write_kib": 2112.0},
     "decode_b16_hq32_hkv8_nq1_nk16384_d256": {
         "source": "fa_splitkv.hip",
-        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
         "fetch_kib": 1050163.8, "write_kib": 6720.2},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
         "fetch_kib": 132424.4, "write_kib": 2112.1},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "71994db8b19c253b106eb90e75252ae445c1fce780d52a49621327a61dfb2b85",
+        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
         "fetch_kib": 1048925.9, "write_kib": 2112.1},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
@@ -146,17 +147,27 @@ MEASURED_TRAFFIC = {
 }
 
 
+def kernel_source_hash(source):
+    """SHA-256 over a kernel source and the headers every kernel source
+    includes (names, lengths and contents)."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in (source, "fa_device.h", "fa_internal.h"):
+        path = os.path.join(ROOT, "exact_io_aware_05_amd", "csrc", name)
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(name.encode() + b"\0" + len(data).to_bytes(8, "little") + data)
+    return h.hexdigest()
+
+
 def measured_traffic(name):
     """HBM bytes per launch (counter-based) or None if not measured for the
     current kernel source."""
-    import hashlib
     rec = MEASURED_TRAFFIC.get(name)
     if rec is None:
         return None
-    path = os.path.join(ROOT, "exact_io_aware_05_amd", "csrc", rec["source"])
-    with open(path, "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["sha256"]:
-            return None
+    if kernel_source_hash(rec["source"]) != rec["sha256"]:
+        return None
     return int(round((rec["fetch_kib"] * FETCH_SCALE +
                       rec["write_kib"] * WRITE_SCALE) * 1024))
 
@@ -164,6 +175,19 @@ def measured_traffic(name):
 def _dev_tensor(bits):
     import torch
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _cpu_model():
+    """The host CPU's model name (first processor in /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def _blas_threads():
@@ -211,6 +235,7 @@ def cpu_baseline(w, q, k, v, budget_s=10.0, do=None, window=None):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
+        "cpu": _cpu_model(),
         "sample": f"{'gradients of ' if do is not None else ''}"
                   f"{done} of {w.B * w.Hq} heads (batch 0, heads 0..{done - 1}), "
                   f"all {w.Nq} query rows each, float64 numpy; {t_total:.1f} s",
@@ -283,6 +308,7 @@ def cpu_baseline_varlen(spec, lens, q, k, v, cu, budget_s=10.0):
         done += 1
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(_blas_threads()), "kind": "oracle",
+            "cpu": _cpu_model(),
             "sample": f"{done} of {len(pairs)} (sequence, head) pairs, in "
                       f"order from sequence 0 head 0, float64 numpy; "
                       f"{t_total:.1f} s"}
@@ -466,6 +492,7 @@ def bench_fp8(args):
             "value": round(attention_fwd_flops(1, done, w.Nq, w.Nk, w.d,
                                                w.causal) / t_total / 1e12, 6),
             "unit": "TFLOP/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "cpu": _cpu_model(),
             "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
                       f"float64 numpy on the decoded inputs; {t_total:.1f} s"}
     print(json.dumps(out), flush=True)
@@ -540,6 +567,7 @@ def bench_sparse(args):
         out["cpu_baseline"] = {
             "value": round(fl / t_total / 1e12, 6), "unit": "TFLOP/s",
             "cores": int(_blas_threads()), "kind": "oracle",
+            "cpu": _cpu_model(),
             "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
                       f"float64 numpy; {t_total:.1f} s"}
     print(json.dumps(out), flush=True)
@@ -614,6 +642,7 @@ def bench_docmask(args):
         out["cpu_baseline"] = {
             "value": round(4.0 * w.d * pairs * done / t_total / 1e12, 6),
             "unit": "TFLOP/s", "cores": int(_blas_threads()), "kind": "oracle",
+            "cpu": _cpu_model(),
             "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
                       f"float64 numpy; {t_total:.1f} s"}
     print(json.dumps(out), flush=True)

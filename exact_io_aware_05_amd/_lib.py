@@ -55,6 +55,7 @@ SIGNATURES = {
                                                            _vp, _c_size, _vp]),
     "fa_status_string": (ctypes.c_char_p, [_c_int]),
     "fa_last_hip_error": (_c_int, []),
+    "fa_source_hash": (ctypes.c_char_p, []),
 }
 
 _lock = threading.Lock()
@@ -71,19 +72,48 @@ class FAError(RuntimeError):
         self.status = status
 
 
+class StaleLibraryError(RuntimeError):
+    """libfa.so was built from other sources than the ones beside it."""
+
+
+def _fresh_or_rebuild():
+    """Make sure libfa.so exists and was built from the sources on disk:
+    build it when it is missing or stale and hipcc is available, otherwise
+    raise StaleLibraryError.  Returns the expected source hash."""
+    from . import build as _build
+    want = _build.source_hash()
+    have = _build.embedded_hash(LIB_PATH)
+    if have == want:
+        return want
+    try:
+        _build.hipcc()
+    except RuntimeError:
+        raise StaleLibraryError(
+            f"{LIB_PATH} was built from other sources (library {have}, "
+            f"sources {want}) and hipcc is not available to rebuild it")
+    _build.build()
+    if _build.embedded_hash(LIB_PATH) != want:
+        raise StaleLibraryError(f"rebuilt {LIB_PATH} does not match its sources")
+    return want
+
+
 def load():
-    """Load libfa.so, building it first if it is not there."""
+    """Load libfa.so, building it first if it is missing or was built from
+    other sources than the ones on disk (see ``fa_source_hash``)."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(LIB_PATH):
-                from .build import build
-                build()
+            want = _fresh_or_rebuild()
             lib = ctypes.CDLL(LIB_PATH)
             for name, (res, args) in SIGNATURES.items():
                 fn = getattr(lib, name)
                 fn.restype = res
                 fn.argtypes = args
+            got = lib.fa_source_hash().decode()
+            if got != want:
+                raise StaleLibraryError(
+                    f"loaded {LIB_PATH} reports source hash {got}, "
+                    f"sources hash to {want}")
             _lib = lib
     return _lib
 

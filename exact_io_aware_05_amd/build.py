@@ -5,10 +5,17 @@
 Each source is compiled to an object in parallel, then the objects are
 linked into one shared library that exports the C interface of
 ``include/fa.h``.
+
+The library carries the SHA-256 of what it was built from (every file under
+``csrc/``, ``include/fa.h`` and the compiler flags), as the string
+``FA_SOURCE_HASH=<hex>`` and through ``fa_source_hash()``.  The loader
+compares it with the sources on disk, so a library left over from older
+sources is rebuilt (or refused) instead of run.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -48,6 +55,48 @@ def _flags():
     ]
 
 
+def source_files():
+    """Every input of the build, in a fixed order: the HIP sources and
+    headers under csrc/, then the public header."""
+    names = sorted(n for n in os.listdir(CSRC) if n.endswith((".hip", ".h")))
+    return [os.path.join(CSRC, n) for n in names] + [os.path.join(INCLUDE, "fa.h")]
+
+
+def source_hash() -> str:
+    """SHA-256 over the build's inputs (file names and contents) and the
+    compiler flags; the library is stale when its embedded value differs."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as f:
+            data = f.read()
+        h.update(len(data).to_bytes(8, "little") + data)
+    flags = _flags() + [f"{k}:{' '.join(v)}" for k, v in sorted(EXTRA.items())]
+    h.update("\0".join(flags).encode())
+    return h.hexdigest()
+
+
+HASH_MARK = b"FA_SOURCE_HASH="
+
+
+def embedded_hash(lib_path: str = LIB):
+    """The source hash recorded in a built library (read from the file,
+    without loading it), or None when it has none."""
+    try:
+        with open(lib_path, "rb") as f:
+            data = f.read()
+    except OSError:
+        return None
+    i = data.find(HASH_MARK)
+    if i < 0:
+        return None
+    hexd = data[i + len(HASH_MARK):i + len(HASH_MARK) + 64]
+    try:
+        return hexd.decode("ascii") if len(hexd) == 64 and int(hexd, 16) >= 0 else None
+    except ValueError:
+        return None
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -64,18 +113,24 @@ def _run(cmd, verbose):
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     cc = hipcc()
+    digest = source_hash()
     objs = []
     jobs = []
     for src in SOURCES:
         obj = os.path.join(BUILD_DIR, src.replace(".hip", ".o"))
         objs.append(obj)
-        jobs.append([cc, *_flags(), *EXTRA.get(src, []), "-c",
+        extra = list(EXTRA.get(src, []))
+        if src == "fa_api.hip":
+            extra.append(f'-DFA_SOURCE_HASH="{digest}"')
+        jobs.append([cc, *_flags(), *extra, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), jobs))
     tmp = LIB + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp],
          verbose)
+    if embedded_hash(tmp) != digest:
+        raise RuntimeError("built library does not carry its source hash")
     os.replace(tmp, LIB)
     return LIB
 

@@ -116,6 +116,15 @@ const char* fa_status_string(int status) {
 
 int fa_last_hip_error(void) { return g_last_hip_error; }
 
+// The build passes the SHA-256 of its inputs; the marker lets a loader read
+// it from the file without loading the library.
+#ifndef FA_SOURCE_HASH
+#define FA_SOURCE_HASH "unknown"
+#endif
+static const char kSourceHash[] = "FA_SOURCE_HASH=" FA_SOURCE_HASH;
+
+const char* fa_source_hash(void) { return kSourceHash + 15; }
+
 size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) {
   if (B < 1 || Hq < 1 || Nq < 1 || d < 1 || num_splits < 1) return 0;
   return fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, num_splits);

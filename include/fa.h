@@ -403,6 +403,13 @@ const char* fa_status_string(int status);
 /* The hipError_t (as int) behind the last FA_ERR_HIP on this thread. */
 int fa_last_hip_error(void);
 
+/* Build identity: the SHA-256 (64 lowercase hex digits) of the sources and
+ * compiler flags this library was built from, as a static string.  Loaders
+ * compare it with the sources at hand and refuse or rebuild a stale
+ * library.  The same digits follow the marker "FA_SOURCE_HASH=" in the
+ * library file.  Never fails. */
+const char* fa_source_hash(void);
+
 #ifdef __cplusplus
 }
 #endif

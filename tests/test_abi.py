@@ -451,3 +451,63 @@ def test_sparse_unsupported(lib):
     assert _sparse(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
     assert _sparse(lib, Nk=8191 * 64 + 1) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
+
+
+def test_library_matches_its_sources(lib):
+    """The loaded library reports the hash of the sources on disk, and the
+    same digits sit behind the file's marker."""
+    from exact_io_aware_05_amd import build
+    want = build.source_hash()
+    assert lib.fa_source_hash().decode() == want
+    assert build.embedded_hash(_lib.LIB_PATH) == want
+    assert re.fullmatch(r"[0-9a-f]{64}", want)
+
+
+def test_source_hash_covers_headers_and_flags(monkeypatch, tmp_path):
+    """Editing any kernel source or header, or the flags, changes the hash."""
+    from exact_io_aware_05_amd import build
+    base = build.source_hash()
+    files = build.source_files()
+    names = {os.path.basename(f) for f in files}
+    assert {"fa_prefill.hip", "fa_device.h", "fa_internal.h", "fa.h"} <= names
+    victim = next(f for f in files if f.endswith("fa_device.h"))
+    orig_open = open
+
+    def patched_open(path, mode="r", *a, **k):
+        if os.path.abspath(path) == victim and "b" in mode:
+            data = orig_open(path, mode, *a, **k).read() + b"\n// edit\n"
+            p = tmp_path / "edited"
+            p.write_bytes(data)
+            return orig_open(p, mode, *a, **k)
+        return orig_open(path, mode, *a, **k)
+
+    monkeypatch.setattr("builtins.open", patched_open)
+    assert build.source_hash() != base
+    monkeypatch.undo()
+    assert build.source_hash() == base
+    monkeypatch.setattr(build, "EXTRA", {**build.EXTRA, "fa_api.hip": ["-O1"]})
+    assert build.source_hash() != base
+
+
+def test_stale_library_is_refused_without_a_compiler(monkeypatch, tmp_path):
+    """A library whose embedded hash differs from the sources is never
+    loaded: with no hipcc to rebuild it, load() raises."""
+    import shutil
+    from exact_io_aware_05_amd import build
+    stale = tmp_path / "libfa.so"
+    shutil.copy(_lib.LIB_PATH, stale)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(stale))
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(build, "source_hash", lambda: "0" * 64)
+
+    def no_hipcc():
+        raise RuntimeError("hipcc not found")
+
+    monkeypatch.setattr(build, "hipcc", no_hipcc)
+    with pytest.raises(_lib.StaleLibraryError):
+        _lib.load()
+    # a library with no marker at all is stale too
+    stale.write_bytes(b"\x7fELF not a library")
+    assert build.embedded_hash(str(stale)) is None
+    with pytest.raises(_lib.StaleLibraryError):
+        _lib.load()

@@ -28,7 +28,9 @@
 //   LDS through the transposing read ds_read_b64_tr_b16.
 // * K/V tiles move HBM -> LDS with buffer_load ... lds (no staging
 //   registers, no VALU); a buffer resource per head makes reads past the
-//   last key return zeros, so tails need no branches.  K is stored
+//   last key return zeros, so tails need no branches.  The copies stay in
+//   flight across the loop's barriers (which carry no memory fence), up to
+//   three blocks ahead; explicit vmcnt waits order them.  K is stored
 //   column-major in 16-byte chunks (chunk c of all 64 rows is one
 //   contiguous KiB), V row-major with 8-byte chunks XOR-swizzled by row:
 //   each DMA instruction then reads from a per-lane base plus a scalar
@@ -95,10 +97,36 @@ __device__ __forceinline__ int vswz(int r) {
   return D == 128 ? 8 * (r & 3) : 8 * ((r >> 1) & 1);
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base,
-                                                       uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)bytes, 0x00020000);
+// One 1 KiB HBM -> LDS copy instruction (buffer_load_dwordx4 ... lds):
+// lane l reads 16 bytes at byte offset voff of the buffer [base, base +
+// bytes) (zeros past its end) and writes them to LDS at dst + 16 l.  It is
+// written in assembly so that the compiler does not track it: its own
+// tracking of such copies cannot tell ring stages apart and would wait for
+// every copy in flight before each LDS read.  The explicit vmcnt waits of
+// the caller order the copies.  (The copy reads its LDS address from M0, one
+// wait state after M0 is written.)
+__device__ __forceinline__ void dma16(char* dst, const char* base,
+                                      uint32_t bytes, uint32_t voff) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const u32x4 r = {
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) &
+          0xFFFFu,
+      (uint32_t)__builtin_amdgcn_readfirstlane((int)bytes), 0x00020000u};
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(
+      (int)(uint32_t)reinterpret_cast<uintptr_t>((lds_char*)dst));
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(r), "{m0}"(m));
+}
+
+// Workgroup barrier that neither waits for outstanding copies nor lets the
+// compiler move memory accesses across it (the explicit vmcnt waits before
+// it give the order the ring needs).
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Starts the HBM -> LDS copy of block `blk` (64 rows) of one K or V head
@@ -124,10 +152,8 @@ __device__ __forceinline__ void copy_block(char* dst, const char* head,
   for (int n = 0; n < L::NINS / NW; ++n) {
     const int i = wave + NW * n;
     const int left = rem - step * i;
-    const __amdgpu_buffer_rsrc_t r =
-        rsrc(base + step * i, (uint32_t)(left > 0 ? left : 0));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        r, (lds_void*)(dst + 1024 * i), 16, lane_off, 0, 0, 0);
+    dma16(dst + 1024 * i, base + step * i, (uint32_t)(left > 0 ? left : 0),
+          lane_off);
   }
 }
 
@@ -641,11 +667,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // b % 4.  In iteration j every wave issues its share of the copies of
   // K_{j+3} and V_{j+2} at the start of its softmax phase (vector memory
   // issue then overlaps vector ALU work).  A stage is refilled only after
-  // both groups' last reads of it.  The copies are complete at the
-  // iteration's closing barrier: its release fence waits for every
-  // outstanding direct-to-LDS copy (they write LDS), so the explicit waits
-  // below only state the weakest order the ring needs (the first reader of
-  // K_{j+3} / V_{j+2} is group A's matrix phase of iteration j+3).
+  // both groups' last reads of it.  The loop's barriers carry no memory
+  // fence, so copies stay in flight across them: a wave waits only for its
+  // own copies that the next reads need (group A: those of iteration j-2,
+  // group B, one barrier behind: those of iteration j-1), and the barrier
+  // after that wait makes every wave's share of the block visible.  The
+  // first reader of K_{j+3} / V_{j+2} is group A's matrix phase of
+  // iteration j+3, three barriers after group B's wait for them.
   constexpr int OPS = 2 * (L::NINS / NW);  // copy instructions per wave
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
   auto copies = [&](int j) {
@@ -712,7 +740,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       }
     }
     mphase(j, std::true_type{}, keep_prev, keep);
-    __syncthreads();
+    barrier();
     copies(j);
     if (LISTED && !keep)
       rescale = false;  // nothing of this block enters this half's rows
@@ -743,10 +771,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       wait_vmcnt<2 * OPS>();  // own copies of iteration j-2 have landed
     else
       wait_vmcnt<OPS>();      // own copies of iteration j-1 have landed
-    __syncthreads();
+    barrier();
   }
   if (n_act > j0)  // P V of the last block
     mphase(n_act, std::false_type{}, LISTED ? keep_prev : true);
+  wait_vmcnt<0>();  // no copy may be in flight when the wave ends
   __syncthreads();
   if (group_a) __syncthreads();
 

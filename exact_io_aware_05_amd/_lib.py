@@ -14,6 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+FA_ERR_TOO_LARGE = 4
 FA_OUT_BF16, FA_OUT_F32 = 0, 1
 
 _c_int, _c_float, _c_size, _vp = (ctypes.c_int, ctypes.c_float,
@@ -23,6 +24,10 @@ _c_int, _c_float, _c_size, _vp = (ctypes.c_int, ctypes.c_float,
 SIGNATURES = {
     "fa_fwd": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int,
                         _c_int, _c_int, _c_int, _c_int, _c_float, _c_int, _vp]),
+    "fa_fwd_noalloc": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int,
+                                _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_float, _c_int, _vp]),
+    "fa_noalloc_scratch_bytes": (_c_size, []),
     "fa_splitkv_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int,
                                              _c_int]),
     "fa_fwd_splitkv": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int,

@@ -6,6 +6,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "fa.h"
 #include "fa_internal.h"
 
@@ -100,6 +102,42 @@ int run_forward(const void* q, const void* k, const void* v, void* o,
   return hip_status(e2);
 }
 
+// ---- scratch of the allocation-free entry point (fa_fwd_noalloc)
+//
+// The KV-split partials of one call live in this file-scope device array
+// instead of memory taken per call.  Every GPU the library runs on holds its
+// own copy until the process ends, at its own address: host code reaches it
+// only through the pointer hipGetSymbolAddress returns with that device
+// current (the array's name, used in host code, is a host-side stand-in and
+// not a device address).  The partial kernel writes every (row, chunk) entry
+// the merge kernel reads, so nothing needs clearing between calls; calls
+// that overlap on one device (different streams) share the array and race.
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch, looked up once per
+// device.
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> guard(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr) return FA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -110,6 +148,9 @@ const char* fa_status_string(int status) {
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported shape or device";
     case FA_ERR_HIP: return "FA_ERR_HIP: HIP runtime error (see fa_last_hip_error)";
+    case FA_ERR_TOO_LARGE:
+      return "FA_ERR_TOO_LARGE: the call needs more scratch than the "
+             "allocation-free entry point holds (fa_noalloc_scratch_bytes)";
     default: return "unknown fa status";
   }
 }
@@ -180,6 +221,38 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
   const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
   return run_forward(q, k, v, o, lse, s, splits, out_dtype == FA_OUT_F32,
                      stream);
+}
+
+size_t fa_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int out_dtype, hipStream_t stream) {
+  int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
+                        out_dtype);
+  if (st != FA_OK) return st;
+  const int splits = default_splits(B, Hq, Hkv, Nq, Nk);
+  const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
+  if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
+  const size_t bytes =
+      splits == 0 ? 0
+                  : fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d,
+                                                splits);
+  if (bytes > kNoAllocScratchBytes) return FA_ERR_TOO_LARGE;
+  st = check_device();
+  if (st != FA_OK) return st;
+  const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  const bool f32 = out_dtype == FA_OUT_F32;
+  if (splits == 0)
+    return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
+                                         fa::dense_layout(s), f32, stream));
+  void* ws = nullptr;
+  st = scratch_on_device(&ws);
+  if (st != FA_OK) return st;
+  return hip_status(fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws,
+                                       stream));
 }
 
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o,

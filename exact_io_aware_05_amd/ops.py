@@ -76,6 +76,22 @@ def fa_fwd(q, k, v, causal=False, scale=None, out_dtype=torch.bfloat16,
     return o, lse
 
 
+def fa_fwd_noalloc(q, k, v, causal=False, scale=None,
+                   out_dtype=torch.bfloat16, o=None, lse=None):
+    """``fa_fwd`` through ``fa_fwd_noalloc`` (the library allocates no
+    device memory; KV-split partials use its fixed scratch array).  Returns
+    ``(o, lse)``."""
+    B, Hq, Hkv, Nq, Nk, d = _dims(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    st = load().fa_fwd_noalloc(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), scale,
+        FA_OUT_F32 if out_dtype == torch.float32 else FA_OUT_BF16, _stream(q))
+    check(st, "fa_fwd_noalloc")
+    return o, lse
+
+
 def fa_fwd_window(q, k, v, window, causal=False, scale=None,
                   out_dtype=torch.bfloat16, o=None, lse=None):
     """Sliding-window forward through ``fa_fwd_window``; ``window`` is

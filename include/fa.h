@@ -56,6 +56,8 @@
  *   FA_ERR_UNSUPPORTED  d not 64 or 128, sizes beyond the 64-bit/grid
  *                       limits or the 32-bit per-head K/V range of the
  *                       prefill form, or the current device is not gfx950.
+ *   FA_ERR_TOO_LARGE    (fa_fwd_noalloc only) the call needs more scratch
+ *                       than the library's fixed scratch array holds.
  *   FA_ERR_HIP          a HIP runtime or launch error; the hipError_t is
  *                       available from fa_last_hip_error() on the same
  *                       thread.  Outputs are then undefined.
@@ -76,7 +78,8 @@ enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1,
   FA_ERR_UNSUPPORTED = 2,
-  FA_ERR_HIP = 3
+  FA_ERR_HIP = 3,
+  FA_ERR_TOO_LARGE = 4
 };
 
 enum { FA_OUT_BF16 = 0, FA_OUT_F32 = 1 };
@@ -96,6 +99,28 @@ enum { FA_OUT_BF16 = 0, FA_OUT_F32 = 1 };
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
            float scale, int out_dtype, hipStream_t stream);
+
+/*
+ * fa_fwd for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, choice of form, results and errors as fa_fwd, bit for
+ * bit; it never calls hipMalloc, hipMallocAsync, hipFree or any allocating
+ * routine.  When the KV-split form is chosen, its partials go to a
+ * fixed-size scratch array inside the library (one per device, held until
+ * the process ends), so:
+ *   - a call whose partials need more than fa_noalloc_scratch_bytes()
+ *     bytes (fa_splitkv_workspace_bytes at fa_default_num_splits chunks)
+ *     returns FA_ERR_TOO_LARGE before any HIP call;
+ *   - calls that overlap on one device (e.g. on two streams) share that
+ *     array and race: serialise them.
+ * The prefill form uses no scratch at all.
+ */
+int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
+                   float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int out_dtype, hipStream_t stream);
+
+/* Size in bytes of the scratch array behind fa_fwd_noalloc (16 MiB). */
+size_t fa_noalloc_scratch_bytes(void);
 
 /*
  * KV-split (Flash-Decoding) forward with a caller-owned workspace.

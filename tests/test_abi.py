@@ -511,3 +511,24 @@ def test_stale_library_is_refused_without_a_compiler(monkeypatch, tmp_path):
     assert build.embedded_hash(str(stale)) is None
     with pytest.raises(_lib.StaleLibraryError):
         _lib.load()
+
+
+def test_noalloc_scratch_limit(lib):
+    """fa_fwd_noalloc refuses, before any HIP call, a KV-split call whose
+    partials exceed its fixed scratch array; the limit is reported."""
+    cap = lib.fa_noalloc_scratch_bytes()
+    assert cap == 16 << 20
+    B, Hq, Hkv, Nq, Nk, d = 1024, 32, 8, 1, 32768, 128
+    S = lib.fa_default_num_splits(B, Hq, Hkv, Nq, Nk, d)
+    assert S >= 1
+    need = lib.fa_splitkv_workspace_bytes(B, Hq, Nq, d, S)
+    assert need > cap
+    st = lib.fa_fwd_noalloc(P, P, P, P, P, B, Hq, Hkv, Nq, Nk, d, 0, 0.088,
+                            0, None)
+    assert st == _lib.FA_ERR_TOO_LARGE
+    assert b"FA_ERR_TOO_LARGE" in lib.fa_status_string(st)
+    # invalid arguments are still reported as such
+    assert lib.fa_fwd_noalloc(None, P, P, P, P, 1, 4, 2, 1, 64, 64, 0, 0.125,
+                              0, None) == _lib.FA_ERR_INVALID_ARG
+    assert lib.fa_fwd_noalloc(P, P, P, P, P, 1, 4, 2, 1, 64, 96, 0, 0.125,
+                              0, None) == _lib.FA_ERR_UNSUPPORTED

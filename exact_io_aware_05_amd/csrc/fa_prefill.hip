@@ -30,7 +30,8 @@
 //   registers, no VALU); a buffer resource per head makes reads past the
 //   last key return zeros, so tails need no branches.  The copies stay in
 //   flight across the loop's barriers (which carry no memory fence), up to
-//   three blocks ahead; explicit vmcnt waits order them.  K is stored
+//   three blocks ahead at d = 128 and seven at d = 64 (a ring of 4 or 8
+//   stages); explicit vmcnt waits order them.  K is stored
 //   column-major in 16-byte chunks (chunk c of all 64 rows is one
 //   contiguous KiB), V row-major with 8-byte chunks XOR-swizzled by row:
 //   each DMA instruction then reads from a per-lane base plus a scalar
@@ -78,13 +79,13 @@ __device__ __forceinline__ int key_slot(int j) {
   return (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
 }
 
-template <int D>
+template <int D, int NS_ = 4>
 struct Layout {
   static constexpr int ROWB = 2 * D;          // bytes of one K/V row
   static constexpr int KBYTES = BC * ROWB;    // one K buffer (16 KiB at 128)
   static constexpr int VBYTES = BC * ROWB;    // one V buffer
-  static constexpr int NS = 4;                // ring stages of K and of V
-  static constexpr int VBASE = NS * KBYTES;   // [K0..K3 | V0..V3]
+  static constexpr int NS = NS_;              // ring stages of K and of V
+  static constexpr int VBASE = NS * KBYTES;   // [K stages | V stages]
   static constexpr int TOTAL = NS * (KBYTES + VBYTES);
   static constexpr int NINS = KBYTES / 1024;  // 1 KiB DMA instructions
   static constexpr int NTILE = D / 32;        // O^T accumulator tiles
@@ -145,9 +146,10 @@ __device__ __forceinline__ void copy_block(char* dst, const char* head,
   // (Nk here: number of rows that may be read; later rows read as zeros.
   // A head spans less than 2^31 bytes, so 32-bit offsets suffice.)
   using L = Layout<D>;
-  const int kb = min(blk * BC, Nk);
+  // (a block before the first, blk < 0, is a copy of zeros too)
+  const int kb = min(max(blk, 0) * BC, Nk);
   const char* base = head + (int64_t)kb * rsb;
-  const int rem = kb < Nk ? (Nk - kb - 1) * rsb + L::ROWB : 0;
+  const int rem = (blk >= 0 && kb < Nk) ? (Nk - kb - 1) * rsb + L::ROWB : 0;
 #pragma unroll
   for (int n = 0; n < L::NINS / NW; ++n) {
     const int i = wave + NW * n;
@@ -375,7 +377,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // a list of key blocks in LDS drives the loop (block or column mask)
   constexpr bool LISTED = SPARSE || COLUMN;
   constexpr int BLKBITS = COLUMN ? 0xFFFF : 0xFFFFFF;
-  using L = Layout<D>;
+  // K/V ring depth: 8 stages of 8 KiB blocks at d = 64, 4 of 16 KiB at
+  // d = 128 (128 KiB of LDS either way, leaving 32 KiB for the block list
+  // of the listed variants; a fifth stage at d = 128 measured slower)
+  constexpr int NSTG = D == 64 ? 8 : 4;
+  using L = Layout<D, NSTG>;
   // block-sparse: the key blocks this workgroup computes, in order (bits
   // 0..23 the block, bit 24 / 25 set when the rows of group A / B use it),
   // then their count
@@ -408,6 +414,18 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     if (u >= n_bh * n_qblk) return;
     jq = u / n_bh;
     bh = u % n_bh;
+  } else if (((n_items / (n_qblk * G)) & 7) == 0) {
+    // equal sequences, KV heads a multiple of 8: each XCD (which receives
+    // every 8th workgroup in launch order) takes whole KV heads, so a KV
+    // head's Q blocks share that XCD's L2, and runs their items Q-block
+    // rank first: the heaviest blocks of all its heads go first, which
+    // keeps the in-order dispatch balanced under the causal mask
+    const int per = (n_items / (n_qblk * G)) >> 3;  // KV heads per XCD
+    const int x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+    g = sx % G;
+    const int t1 = sx / G;
+    bh = x * per + t1 % per;
+    jq = t1 / per;
   } else {
     // equal sequences: each XCD takes one contiguous range of items
     // (b, kv head, Q block, head in group), so a KV head's Q blocks share
@@ -663,43 +681,35 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // ---- K/V ring: NS = 4 stages each; block b's K and V live in stage
-  // b % 4.  In iteration j every wave issues its share of the copies of
-  // K_{j+3} and V_{j+2} at the start of its softmax phase (vector memory
-  // issue then overlaps vector ALU work).  A stage is refilled only after
-  // both groups' last reads of it.  The loop's barriers carry no memory
-  // fence, so copies stay in flight across them: a wave waits only for its
-  // own copies that the next reads need (group A: those of iteration j-2,
-  // group B, one barrier behind: those of iteration j-1), and the barrier
-  // after that wait makes every wave's share of the block visible.  The
-  // first reader of K_{j+3} / V_{j+2} is group A's matrix phase of
-  // iteration j+3, three barriers after group B's wait for them.
+  // ---- K/V ring: NS stages each; block b's K and V live in stage b % NS.
+  // Group g of copies is K_g and V_{g-1}; iteration j issues group
+  // j + NS - 1 at the start of its softmax phase (vector memory issue then
+  // overlaps vector ALU work).  A stage is refilled only after both groups'
+  // last reads of it (those of block j - 1, before this iteration's first
+  // barrier).  The loop's barriers carry no memory fence, so copies stay
+  // in flight across them: at the end of iteration j group A waits for its
+  // own copies of iteration j - (NS - 2) and group B (one barrier behind)
+  // for those of iteration j - (NS - 3); the first reader of K_{j+NS-1} /
+  // V_{j+NS-2}, group A's matrix phase of iteration j + NS - 1, comes after
+  // both waits and a barrier.
   constexpr int OPS = 2 * (L::NINS / NW);  // copy instructions per wave
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
-  auto copies = [&](int j) {
-    copy_block<D>(smem + ((j + 3) % L::NS) * L::KBYTES, kh, kv_rows,
-                  blk_at(j + 3), wave, k_off, 16, rsb);
-    copy_block<D>(smem + L::VBASE + ((j + 2) % L::NS) * L::VBYTES, vh,
-                  kv_rows, blk_at(j + 2), wave, v_off, v_step, rsbv);
+  // (V_{j0-1}, before the first block, is a copy of zeros: block j0's
+  // matrix phase multiplies it by the all-zero "previous" P, and 0 *
+  // (stale NaN/Inf bits) would not be 0)
+  auto group = [&](int g) {
+    copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, blk_at(g),
+                  wave, k_off, 16, rsb);
+    copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
+                  vh, kv_rows, g > j0 ? blk_at(g - 1) : -1, wave, v_off,
+                  v_step, rsbv);
   };
-  // prologue: K_j0, K_j0+1, K_j0+2, V_j0, V_j0+1 (all waves), fully
-  // waited (j0 = 0 unless a band starts later).  The V stage before j0 is
-  // zeroed: block j0's matrix phase multiplies it by the all-zero
-  // "previous" P, and 0 * (stale NaN/Inf bits) would not be 0.
-#pragma unroll
-  for (int b0 = 0; b0 < 3; ++b0)
-    copy_block<D>(smem + ((j0 + b0) % L::NS) * L::KBYTES, kh, kv_rows,
-                  blk_at(j0 + b0), wave, k_off, 16, rsb);
-#pragma unroll
-  for (int b0 = 0; b0 < 2; ++b0)
-    copy_block<D>(smem + L::VBASE + ((j0 + b0) % L::NS) * L::VBYTES, vh,
-                  kv_rows, blk_at(j0 + b0), wave, v_off, v_step, rsbv);
-#pragma unroll
-  for (int i = tid; i < L::VBYTES / 16; i += NT)
-    reinterpret_cast<u32x4*>(smem + L::VBASE +
-                             ((j0 + L::NS - 1) % L::NS) * L::VBYTES)[i] =
-        u32x4{0u, 0u, 0u, 0u};
-  wait_vmcnt<0>();
+  auto copies = [&](int j) { group(j + L::NS - 1); };
+  // prologue: groups j0 .. j0 + NS - 2.  The first two must have landed for
+  // every wave before the loop: group B's first wait in the loop comes one
+  // barrier too late for group j0 + 1.
+  for (int g = j0; g < j0 + L::NS - 1; ++g) group(g);
+  wait_vmcnt<(L::NS - 3) * OPS>();
   __syncthreads();
 
   // ---- main loop.  Every wave runs the same code, one barrier after each
@@ -768,9 +778,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
                                      alpha, pk);
     keep_prev = keep;
     if (group_a)
-      wait_vmcnt<2 * OPS>();  // own copies of iteration j-2 have landed
+      wait_vmcnt<(L::NS - 2) * OPS>();
     else
-      wait_vmcnt<OPS>();      // own copies of iteration j-1 have landed
+      wait_vmcnt<(L::NS - 3) * OPS>();
     barrier();
   }
   if (n_act > j0)  // P V of the last block

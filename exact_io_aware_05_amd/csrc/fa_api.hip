@@ -25,10 +25,33 @@ bool aligned16(const void* p) {
   return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
 }
 
-// Checks shared by both forward entry points; pure host arithmetic.
+// Head dimensions an entry point takes, as bit sets.  The prefill kernel
+// runs d = 32 and 96 in its 64- and 128-column tiles (the columns past d
+// masked); the KV-split kernel has instances for 32, 64, 128 and 256;
+// fa_fwd and its variants take all five (d = 256 in the KV-split form,
+// d = 96 in the prefill kernel); the backward kernels 64 and 128.
+enum : unsigned { kD32 = 1, kD64 = 2, kD96 = 4, kD128 = 8, kD256 = 16 };
+constexpr unsigned kDimsPrefill = kD32 | kD64 | kD96 | kD128;
+constexpr unsigned kDimsAny = kDimsPrefill | kD256;
+constexpr unsigned kDimsSplit = kD32 | kD64 | kD128 | kD256;
+constexpr unsigned kDimsBwd = kD64 | kD128;
+
+unsigned dim_bit(int d) {
+  switch (d) {
+    case 32: return kD32;
+    case 64: return kD64;
+    case 96: return kD96;
+    case 128: return kD128;
+    case 256: return kD256;
+    default: return 0;
+  }
+}
+
+// Checks shared by the entry points; pure host arithmetic.
 int check_common(const void* q, const void* k, const void* v, const void* o,
                  const float* lse, int B, int Hq, int Hkv, int Nq, int Nk,
-                 int d, float scale, int out_dtype, bool decode = false) {
+                 int d, float scale, int out_dtype,
+                 unsigned dims = kDimsPrefill) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) ||
       (reinterpret_cast<uintptr_t>(lse) & 3u))
@@ -39,9 +62,7 @@ int check_common(const void* q, const void* k, const void* v, const void* o,
   if (!isfinite(scale) || scale < 0.f) return FA_ERR_INVALID_ARG;
   if (out_dtype != FA_OUT_BF16 && out_dtype != FA_OUT_F32)
     return FA_ERR_INVALID_ARG;
-  // (the KV-split form also takes d = 32 and 256)
-  if (d != 64 && d != 128 && !(decode && (d == 32 || d == 256)))
-    return FA_ERR_UNSUPPORTED;
+  if (!(dim_bit(d) & dims)) return FA_ERR_UNSUPPORTED;
   // element counts must stay well inside 64-bit offsets and 32-bit rows
   const long long rows_q = (long long)B * Hq * Nq;
   const long long rows_k = (long long)B * Hkv * Nk;
@@ -81,6 +102,23 @@ int default_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   if (s > fa::kMaxSplits) s = fa::kMaxSplits;
   if (s < 1) s = 1;
   return (int)s;
+}
+
+// The chunk count of fa_fwd's choice for this shape (0: the prefill kernel),
+// by head dimension: d = 96 has only the prefill kernel, d = 256 only the
+// KV-split form (one chunk at least).
+int forward_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
+  int s = default_splits(B, Hq, Hkv, Nq, Nk);
+  if (d == 96) s = 0;
+  if (d == 256 && s == 0) s = 1;
+  return s;
+}
+
+// Sizes the KV-split form cannot address (its wave count fits in an int).
+bool splitkv_too_large(int B, int Hq, int Hkv, int Nq, int splits) {
+  const long long rowtiles =
+      ((long long)Nq * (Hq / Hkv) + fa::kSplitRows - 1) / fa::kSplitRows;
+  return (long long)B * Hkv * rowtiles * splits > (1LL << 31) - 64;
 }
 
 // The prefill kernel (splits == 0) or the KV-split form with a workspace
@@ -173,8 +211,8 @@ size_t fa_splitkv_workspace_bytes(int B, int Hq, int Nq, int d, int num_splits) 
 
 int fa_default_num_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Nk < 1 || Hq % Hkv) return 0;
-  if (d != 32 && d != 64 && d != 128 && d != 256) return 0;
-  return default_splits(B, Hq, Hkv, Nq, Nk);
+  if (!dim_bit(d)) return 0;
+  return forward_splits(B, Hq, Hkv, Nq, Nk, d);
 }
 
 int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
@@ -183,7 +221,7 @@ int fa_fwd_splitkv(const void* q, const void* k, const void* v, void* o,
                    void* workspace, size_t workspace_bytes,
                    hipStream_t stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype, true);
+                        out_dtype, kDimsSplit);
   if (st != FA_OK) return st;
   if (num_splits < 1 || num_splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
@@ -208,11 +246,13 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,
            float scale, int out_dtype, hipStream_t stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype);
+                        out_dtype, kDimsAny);
   if (st != FA_OK) return st;
-  const int splits = default_splits(B, Hq, Hkv, Nq, Nk);
+  const int splits = forward_splits(B, Hq, Hkv, Nq, Nk, d);
   const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
   if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  if (splits > 0 && splitkv_too_large(B, Hq, Hkv, Nq, splits))
     return FA_ERR_UNSUPPORTED;
   // both kernels address one K/V head with 32-bit byte offsets
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
@@ -229,11 +269,13 @@ int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o,
                    float* lse, int B, int Hq, int Hkv, int Nq, int Nk, int d,
                    int causal, float scale, int out_dtype, hipStream_t stream) {
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype);
+                        out_dtype, kDimsAny);
   if (st != FA_OK) return st;
-  const int splits = default_splits(B, Hq, Hkv, Nq, Nk);
+  const int splits = forward_splits(B, Hq, Hkv, Nq, Nk, d);
   const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
   if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  if (splits > 0 && splitkv_too_large(B, Hq, Hkv, Nq, splits))
     return FA_ERR_UNSUPPORTED;
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   const size_t bytes =
@@ -261,7 +303,7 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
                   int out_dtype, hipStream_t stream) {
   if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype);
+                        out_dtype, kDimsAny);
   if (st != FA_OK) return st;
   fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
   s.win_left = window_left;
@@ -277,9 +319,11 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
   const long long span =
       (long long)fa::band_tile_blocks(s, mb, fa::kSplitKeys) * fa::kSplitKeys;
   const int splits =
-      default_splits(B, Hq, Hkv, Nq, (int)(span < Nk ? span : Nk));
+      forward_splits(B, Hq, Hkv, Nq, (int)(span < Nk ? span : Nk), d);
   const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
   if (splits == 0 && (long long)B * Hq * qblk > (1LL << 31) - 1)
+    return FA_ERR_UNSUPPORTED;
+  if (splits > 0 && splitkv_too_large(B, Hq, Hkv, Nq, splits))
     return FA_ERR_UNSUPPORTED;
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   st = check_device();
@@ -327,7 +371,7 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
   const long long nk = (long long)page_size * max_pages_per_seq;
   if (nk > (1LL << 30)) return FA_ERR_UNSUPPORTED;
   int st = check_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, (int)nk,
-                        d, scale, out_dtype, true);
+                        d, scale, out_dtype, kDimsSplit);
   if (st != FA_OK) return st;
   if ((long long)num_pages * page_size * Hkv * d > (1LL << 46))
     return FA_ERR_UNSUPPORTED;
@@ -371,7 +415,7 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
   if (!seqlens_k || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return FA_ERR_INVALID_ARG;
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype, true);
+                        out_dtype, kDimsSplit);
   if (st != FA_OK) return st;
   // one K or V head is addressed with 32-bit byte offsets
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
@@ -581,7 +625,7 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o,
                   hipStream_t stream) {
   if (window_left < -1 || window_right < -1) return FA_ERR_INVALID_ARG;
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        grad_dtype);
+                        grad_dtype, kDimsBwd);
   if (st != FA_OK) return st;
   if (!dout || !dq || !dk || !dv || !aligned16(dout) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv))

@@ -137,23 +137,27 @@ __device__ __forceinline__ void barrier() {
 // `lane_off` plus `step * i` bytes.  Rows at or past Nk read as zeros
 // (buffer range check on the per-instruction resource, which ends at the
 // end of row Nk - 1); a block wholly past Nk is a copy of zeros, which
-// keeps the number of copies per loop iteration fixed.
+// keeps the number of copies per loop iteration fixed.  `rowb`: bytes of a
+// row in memory (2 d, less than the tile's row when the head dimension d is
+// narrower than the tile); instructions i >= `zero_from` copy zeros (the K
+// chunks of columns past d).
 template <int D>
 __device__ __forceinline__ void copy_block(char* dst, const char* head,
                                            int Nk, int blk, int wave,
                                            uint32_t lane_off, int step,
-                                           int rsb) {
+                                           int rsb, int rowb,
+                                           int zero_from = 1 << 30) {
   // (Nk here: number of rows that may be read; later rows read as zeros.
   // A head spans less than 2^31 bytes, so 32-bit offsets suffice.)
   using L = Layout<D>;
   // (a block before the first, blk < 0, is a copy of zeros too)
   const int kb = min(max(blk, 0) * BC, Nk);
   const char* base = head + (int64_t)kb * rsb;
-  const int rem = (blk >= 0 && kb < Nk) ? (Nk - kb - 1) * rsb + L::ROWB : 0;
+  const int rem = (blk >= 0 && kb < Nk) ? (Nk - kb - 1) * rsb + rowb : 0;
 #pragma unroll
   for (int n = 0; n < L::NINS / NW; ++n) {
     const int i = wave + NW * n;
-    const int left = rem - step * i;
+    const int left = i < zero_from ? rem - step * i : 0;
     dma16(dst + 1024 * i, base + step * i, (uint32_t)(left > 0 ? left : 0),
           lane_off);
   }
@@ -368,7 +372,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ v, void* __restrict__ o,
     float* __restrict__ lse, int Hq, int Hkv, int Nq_max, int Nk_max,
     float c2, int n_qblk, int n_items, SeqLayout lay, int wl, int wr,
-    BlockMask bmask, ColMask cmask) {
+    BlockMask bmask, ColMask cmask, int dq) {
   constexpr bool CAUSAL = MODE == kCausal;
   constexpr bool BAND = MODE == kBand;
   static_assert(!(SPARSE && BAND), "block masks go with no mask or causal");
@@ -611,7 +615,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   }
   const int v_step = (1024 / L::ROWB) * rsbv;  // rows of one KiB
 
-  // ---- Q^T operand fragments: lane holds q[row][16t + 8h .. +7]
+  // ---- Q^T operand fragments: lane holds q[row][16t + 8h .. +7]; zeros
+  // past the head dimension dq (a narrower head in this tile: with the K
+  // columns past dq copied as zeros too, the scores are those of dq)
   const int qrow = wrow0 + col;
   bf16x8 qf[NSTEP];
   {
@@ -619,7 +625,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* qp = q + qbase + (ok ? qrow : 0) * lay.q_r + 8 * h;
 #pragma unroll
     for (int t = 0; t < NSTEP; ++t) {
-      u32x4 x = ok ? ldg16(qp + 16 * t) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 x = (ok && 16 * t + 8 * h < dq) ? ldg16(qp + 16 * t)
+                                            : u32x4{0u, 0u, 0u, 0u};
       qf[t] = __builtin_bit_cast(bf16x8, x);
     }
   }
@@ -699,10 +706,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // (stale NaN/Inf bits) would not be 0)
   auto group = [&](int g) {
     copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, blk_at(g),
-                  wave, k_off, 16, rsb);
+                  wave, k_off, 16, rsb, 2 * dq, dq / 8);
     copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
                   vh, kv_rows, g > j0 ? blk_at(g - 1) : -1, wave, v_off,
-                  v_step, rsbv);
+                  v_step, rsbv, 2 * dq);
   };
   auto copies = [&](int j) { group(j + L::NS - 1); };
   // prologue: groups j0 .. j0 + NS - 2.  The first two must have landed for
@@ -799,6 +806,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const int64_t orow = obase + qrow * lay.o_r;
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt) {
+      if (32 * tt >= dq) break;  // (columns past the head dimension)
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg) {
         const int c = 32 * tt + 8 * gg + 4 * h;
@@ -844,7 +852,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
                      static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), o, lse, s.Hq, s.Hkv,
                      s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr, bm,
-                     cm);
+                     cm, s.d);
   return hipGetLastError();
 }
 
@@ -913,9 +921,9 @@ hipError_t launch_prefill_column(const void* q, const void* k, const void* v,
                                  void* o, float* lse, const Shape& s,
                                  const ColMask& cm, bool out_f32,
                                  hipStream_t stream) {
-  if (s.d == 128)
+  if (s.d == 128 || s.d == 96)
     return launch_column_d<128>(q, k, v, o, lse, s, cm, out_f32, stream);
-  if (s.d == 64)
+  if (s.d == 64 || s.d == 32)
     return launch_column_d<64>(q, k, v, o, lse, s, cm, out_f32, stream);
   return hipErrorInvalidValue;
 }
@@ -924,9 +932,9 @@ hipError_t launch_prefill_sparse(const void* q, const void* k, const void* v,
                                  void* o, float* lse, const Shape& s,
                                  const BlockMask& bm, bool out_f32,
                                  hipStream_t stream) {
-  if (s.d == 128)
+  if (s.d == 128 || s.d == 96)
     return launch_sparse_d<128>(q, k, v, o, lse, s, bm, out_f32, stream);
-  if (s.d == 64)
+  if (s.d == 64 || s.d == 32)
     return launch_sparse_d<64>(q, k, v, o, lse, s, bm, out_f32, stream);
   return hipErrorInvalidValue;
 }
@@ -935,9 +943,12 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s,
                           const SeqLayout& lay, bool out_f32,
                           hipStream_t stream) {
-  if (s.d == 128)
+  // head dimension 96 runs in the 128-column tile and 32 in the 64-column
+  // one, the columns past d masked (Q and K read as zeros, O not stored)
+  if (s.d == 128 || s.d == 96)
     return launch_d<128>(q, k, v, o, lse, s, lay, out_f32, stream);
-  if (s.d == 64) return launch_d<64>(q, k, v, o, lse, s, lay, out_f32, stream);
+  if (s.d == 64 || s.d == 32)
+    return launch_d<64>(q, k, v, o, lse, s, lay, out_f32, stream);
   return hipErrorInvalidValue;
 }
 

@@ -38,8 +38,16 @@
  *   no key at all (only possible when causal and Nq > Nk) gets O = 0 and
  *   lse = -inf.
  * - scale must be finite and >= 0 (1/sqrt(d) is the usual value).
- * - d must be 64 or 128; the KV-split entry points (fa_fwd_splitkv,
- *   fa_fwd_paged, fa_fwd_kvlen) also take d = 32 and d = 256.
+ * - Head dimensions by entry point:
+ *     fa_fwd, fa_fwd_noalloc, fa_fwd_window      32, 64, 96, 128, 256
+ *     fa_fwd_varlen, fa_fwd_strided,
+ *     fa_fwd_block_sparse, fa_fwd_colmask        32, 64, 96, 128
+ *     fa_fwd_splitkv, fa_fwd_paged, fa_fwd_kvlen 32, 64, 128, 256
+ *     fa_bwd, fa_bwd_window                      64, 128
+ *     fa_fwd_fp8                                 128
+ *   32 and 96 run in the 64- and 128-column tiles of the prefill kernel
+ *   with the columns past d masked; fa_fwd and fa_fwd_window take d = 96
+ *   always in the prefill kernel and d = 256 always in the KV-split form.
  * - Every call is asynchronous: it validates its arguments on the host,
  *   enqueues kernels on `stream` and returns.  Results are valid once the
  *   stream has been synchronised; buffers must stay alive until then.
@@ -53,9 +61,10 @@
  *   FA_ERR_INVALID_ARG  null or misaligned pointer, a size < 1, Hq not a
  *                       multiple of Hkv, scale not finite or negative, bad
  *                       out_dtype, workspace too small, num_splits < 1.
- *   FA_ERR_UNSUPPORTED  d not 64 or 128, sizes beyond the 64-bit/grid
- *                       limits or the 32-bit per-head K/V range of the
- *                       prefill form, or the current device is not gfx950.
+ *   FA_ERR_UNSUPPORTED  d not taken by the entry point (list above),
+ *                       sizes beyond the 64-bit/grid limits or the 32-bit
+ *                       per-head K/V range of the prefill form, or the
+ *                       current device is not gfx950.
  *   FA_ERR_TOO_LARGE    (fa_fwd_noalloc only) the call needs more scratch
  *                       than the library's fixed scratch array holds.
  *   FA_ERR_HIP          a HIP runtime or launch error; the hipError_t is
@@ -393,7 +402,7 @@ int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,
  * row), 16-byte aligned, scratch on return.  Three kernels are enqueued on
  * `stream`; each output element is written by exactly one workgroup (no
  * atomics), so results are deterministic.  Argument checks and status
- * codes as for fa_fwd (d 64 or 128); FA_ERR_INVALID_ARG also for a missing
+ * codes as for fa_fwd (d 64 or 128 only); FA_ERR_INVALID_ARG also for a missing
  * or small workspace; FA_ERR_UNSUPPORTED also when one head of Q or K
  * spans 2^31 bytes or more ((N + 128) * d * 2 >= 2^31 for N = Nq or Nk).
  */

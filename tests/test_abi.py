@@ -2,6 +2,7 @@
 every function the header declares, and rejects bad arguments with the
 documented status codes before touching the GPU (no compute call here)."""
 import ctypes
+import threading
 import math
 import os
 import re
@@ -25,6 +26,17 @@ def _declared_functions():
 def lib():
     return _lib.load()
 
+
+
+def _fresh(call):
+    """Run ``call`` on a new thread and return its result: a call that gets
+    as far as the device query (FA_ERR_HIP on this host) then leaves the
+    per-thread last HIP error of the test thread untouched."""
+    out = []
+    t = threading.Thread(target=lambda: out.append(call()))
+    t.start()
+    t.join()
+    return out[0]
 
 def test_header_declares_the_interface():
     assert _declared_functions() == sorted(_lib.SIGNATURES)
@@ -83,18 +95,50 @@ def test_fwd_invalid_arguments(lib, kw):
     assert _fwd(lib, **kw) == _lib.FA_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("d", [32, 96, 256, 100])
+@pytest.mark.parametrize("d", [16, 48, 100, 160, 512])
 def test_fwd_unsupported_head_dim(lib, d):
     assert _fwd(lib, d=d) == _lib.FA_ERR_UNSUPPORTED
 
 
+# On this host (no GPU) a call whose arguments pass every check stops at the
+# device query with FA_ERR_HIP: that is how a supported head dimension shows.
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+def test_fwd_head_dims_pass_validation(lib, d):
+    assert _fresh(lambda: _fwd(lib, d=d)) == _lib.FA_ERR_HIP
+    assert _fresh(lambda: _fwd(lib, d=d, Nq=1, Nk=4096)) == _lib.FA_ERR_HIP
+    assert _fresh(lambda: lib.fa_fwd_noalloc(P, P, P, P, P, 1, 4, 2, 16, 16, d,
+                                             0, 0.125, 0, None)) == \
+        _lib.FA_ERR_HIP
+
+
+def test_fwd_form_by_head_dim(lib):
+    """fa_fwd's form: d = 96 always runs the prefill kernel (0 chunks),
+    d = 256 always the KV-split form (at least one chunk)."""
+    assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 128) == 0
+    assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 128) > 1
+    assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 96) == 0
+    assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 96) == 0
+    assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 256) == 1
+    assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 256) > 1
+    assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 100) == 0
+
+
 def test_fwd_prefill_kv_head_range(lib):
-    # one K/V head of the prefill form must span < 2^31 bytes
-    assert _fwd(lib, Hq=1, Hkv=1, Nq=4096, Nk=1 << 23, d=128) == \
-        _lib.FA_ERR_UNSUPPORTED
-    assert _fwd(lib, Hq=1, Hkv=1, Nq=4096, Nk=1 << 24, d=64) == \
-        _lib.FA_ERR_UNSUPPORTED
-    assert lib.fa_last_hip_error() == 0
+    # one K/V head of the prefill form must span < 2^31 bytes; the refusal
+    # comes before any HIP call (the last HIP error is per thread, so a
+    # fresh thread starts from 0)
+    out = {}
+
+    def calls():
+        out["a"] = _fwd(lib, Hq=1, Hkv=1, Nq=4096, Nk=1 << 23, d=128)
+        out["b"] = _fwd(lib, Hq=1, Hkv=1, Nq=4096, Nk=1 << 24, d=64)
+        out["hip"] = lib.fa_last_hip_error()
+
+    t = threading.Thread(target=calls)
+    t.start()
+    t.join()
+    assert out == {"a": _lib.FA_ERR_UNSUPPORTED, "b": _lib.FA_ERR_UNSUPPORTED,
+                   "hip": 0}
 
 
 @pytest.mark.parametrize("kw", INVALID + [dict(S=0), dict(S=5000), dict(ws=None),
@@ -202,7 +246,10 @@ def test_varlen_invalid_arguments(lib, kw):
 
 
 def test_varlen_unsupported(lib):
-    assert _varlen(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _varlen(lib, d=256) == _lib.FA_ERR_UNSUPPORTED
+    assert _varlen(lib, d=100) == _lib.FA_ERR_UNSUPPORTED
+    assert _fresh(lambda: _varlen(lib, d=96)) == _lib.FA_ERR_HIP
+    assert _fresh(lambda: _varlen(lib, d=32)) == _lib.FA_ERR_HIP
     # one sequence's K/V rows of one head span (mk - 1) * Hkv * d * 2 + 2d
     assert _varlen(lib, Hkv=8, Hq=8, mk=(1 << 20) + 2, d=128) == \
         _lib.FA_ERR_UNSUPPORTED
@@ -234,8 +281,10 @@ def test_window_invalid_arguments(lib, kw):
 
 
 def test_window_unsupported(lib):
-    assert _win(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
-    assert _win(lib, d=96, wl=-1, wr=-1) == _lib.FA_ERR_UNSUPPORTED
+    assert _win(lib, d=100) == _lib.FA_ERR_UNSUPPORTED
+    assert _win(lib, d=100, wl=-1, wr=-1) == _lib.FA_ERR_UNSUPPORTED
+    for d in (32, 96, 256):
+        assert _fresh(lambda: _win(lib, d=d)) == _lib.FA_ERR_HIP
     assert _win(lib, Nk=(1 << 23) + 1, d=128) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
 
@@ -359,7 +408,8 @@ def test_colmask_invalid_arguments(lib, kw):
 
 
 def test_colmask_unsupported(lib):
-    assert _colmask(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _colmask(lib, d=256) == _lib.FA_ERR_UNSUPPORTED
+    assert _fresh(lambda: _colmask(lib, d=96)) == _lib.FA_ERR_HIP
     assert _colmask(lib, Nk=64 * 8192) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
 
@@ -422,9 +472,12 @@ def test_strided_invalid_arguments(lib, kw):
 
 
 def test_strided_unsupported(lib):
-    assert _strided(lib, d=96, qs=(4096, 1024, 96), ks=(2048, 1024, 96),
-                    vs=(2048, 1024, 96), os_=(4096, 1024, 96)) == \
+    assert _strided(lib, d=256, qs=(4096, 1024, 256), ks=(2048, 1024, 256),
+                    vs=(2048, 1024, 256), os_=(4096, 1024, 256)) == \
         _lib.FA_ERR_UNSUPPORTED
+    assert _fresh(lambda: _strided(
+        lib, d=96, qs=(4096, 1024, 96), ks=(2048, 1024, 96),
+        vs=(2048, 1024, 96), os_=(4096, 1024, 96))) == _lib.FA_ERR_HIP
     # one K head spans (Nk - 1) * row stride * 2 + 2d bytes
     assert _strided(lib, Nk=(1 << 16) + 2, ks=(0, 0, 1 << 14)) == \
         _lib.FA_ERR_UNSUPPORTED
@@ -448,7 +501,8 @@ def test_sparse_invalid_arguments(lib, kw):
 
 
 def test_sparse_unsupported(lib):
-    assert _sparse(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _sparse(lib, d=256) == _lib.FA_ERR_UNSUPPORTED
+    assert _fresh(lambda: _sparse(lib, d=96)) == _lib.FA_ERR_HIP
     assert _sparse(lib, Nk=8191 * 64 + 1) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
 
@@ -530,5 +584,5 @@ def test_noalloc_scratch_limit(lib):
     # invalid arguments are still reported as such
     assert lib.fa_fwd_noalloc(None, P, P, P, P, 1, 4, 2, 1, 64, 64, 0, 0.125,
                               0, None) == _lib.FA_ERR_INVALID_ARG
-    assert lib.fa_fwd_noalloc(P, P, P, P, P, 1, 4, 2, 1, 64, 96, 0, 0.125,
+    assert lib.fa_fwd_noalloc(P, P, P, P, P, 1, 4, 2, 1, 64, 100, 0, 0.125,
                               0, None) == _lib.FA_ERR_UNSUPPORTED

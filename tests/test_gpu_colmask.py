@@ -45,6 +45,8 @@ CASES = [
     (2, 4, 1, 300, 520, 128, False, "random"),
     (1, 8, 8, 500, 777, 64, True, "random"),
     (1, 4, 2, 257, 257, 128, True, "docs_bidir"),
+    (1, 4, 2, 600, 600, 96, True, "docs_causal"),
+    (1, 4, 4, 500, 777, 32, False, "random"),
 ]
 
 

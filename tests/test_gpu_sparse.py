@@ -31,7 +31,8 @@ def _nb(N, b):
 
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("shape", [(2, 4, 2, 700, 900, 128), (1, 8, 8, 333, 333, 64),
-                                   (1, 2, 1, 300, 2000, 128)],
+                                   (1, 2, 1, 300, 2000, 128), (1, 4, 2, 333, 500, 96),
+                                   (1, 2, 2, 300, 300, 32)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_random_masks_per_head(shape, causal):
     B, Hq, Hkv, Nq, Nk, d = shape

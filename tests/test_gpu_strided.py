@@ -33,7 +33,8 @@ def _fused(q, k, v):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("shape", [(2, 8, 2, 333, 64), (1, 4, 4, 1000, 128)],
+@pytest.mark.parametrize("shape", [(2, 8, 2, 333, 64), (1, 4, 4, 1000, 128),
+                                   (2, 4, 2, 333, 96), (1, 4, 4, 300, 32)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_fused_qkv_views(shape, causal):
     B, Hq, Hkv, N, d = shape

@@ -46,6 +46,8 @@ CASES = [
     ([130, 7, 300], [70, 3, 300], 4, 1, 64, True),        # Nq > Nk: empty rows
     ([0, 100, 0, 33], [10, 0, 0, 33], 2, 2, 128, False),  # empty sequences
     ([1000], [1000], 2, 1, 128, True),
+    ([17, 300, 1, 256, 511], [17, 300, 1, 256, 511], 4, 2, 96, True),
+    ([130, 7, 300], [70, 3, 300], 4, 1, 32, True),
 ]
 
 

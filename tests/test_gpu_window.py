@@ -49,6 +49,13 @@ CASES = [
     (1, 32, 8, 2, 32768, 128, False, (4096, 3)),
     (3, 6, 2, 20, 3000, 128, True, (100, -1)),
     (2, 4, 1, 3, 100, 128, False, (40, 1)),
+    # head dimensions 96 and 32 (prefill kernel, columns past d masked) and
+    # 256 (KV-split form at every size)
+    (1, 4, 2, 700, 700, 96, False, (100, 0)),
+    (1, 2, 2, 600, 600, 32, True, (257, -1)),
+    (2, 8, 2, 1, 5000, 96, False, (1000, -1)),
+    (1, 4, 2, 300, 300, 256, True, (64, -1)),
+    (2, 8, 2, 3, 3000, 256, False, (500, 2)),
 ]
 
 

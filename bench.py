@@ -96,8 +96,16 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
-        "fetch_kib": 71225.5, "write_kib": 66560.0},
+        "sha256": "c51b95d35374dd7c4c002ffd79fb3ed6f9ec0f4be612ebe221c74d34b565a8f6",
+        "fetch_kib": 71261.5, "write_kib": 66566.1},
+    "mha_b4_h16_n2048_d64": {
+        "source": "fa_prefill.hip",
+        "sha256": "c51b95d35374dd7c4c002ffd79fb3ed6f9ec0f4be612ebe221c74d34b565a8f6",
+        "fetch_kib": 41047.5, "write_kib": 16896.0},
+    "causal_outlier_b2_h16_n4096_d128": {
+        "source": "fa_prefill.hip",
+        "sha256": "c51b95d35374dd7c4c002ffd79fb3ed6f9ec0f4be612ebe221c74d34b565a8f6",
+        "fetch_kib": 76713.8, "write_kib": 33432.7},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
         "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",

@@ -11,7 +11,8 @@
 // K/V byte once.  The step is HBM-bound; the waves of a workgroup are
 // independent (no barrier), each streaming its 32-key blocks through a
 // ring of 4 (the loads of the next 3 blocks in flight while one is
-// computed), with non-temporal loads:
+// computed; at d = 256 a ring of 2, so that the four waves' K slots fit in
+// LDS), with non-temporal loads:
 // * K moves HBM -> LDS with buffer_load ... lds, each instruction reading
 //   four whole rows (coalesced), into a per-wave LDS slot in a swizzled
 //   row-major layout; S^T = K Q^T on v_mfma_f32_32x32x16_bf16 then reads

@@ -1,7 +1,8 @@
 """Head dimensions 32 and 256 in the KV-split (decode) form against the
 float64 oracles: the contiguous call (several split counts, causal, several
-queries per sequence, GQA), a paged cache and a padded cache of unequal
-lengths (NaN padding), and a sliding window."""
+queries per sequence, GQA, several 32-row tiles of packed rows), a paged
+cache and a padded cache of unequal lengths (NaN padding), and a sliding
+window; bf16 outputs are the round-to-nearest-even of the fp32 ones."""
 import numpy as np
 import pytest
 
@@ -31,7 +32,9 @@ def _i32(a):
 
 # B, Hq, Hkv, Nq, Nk, causal, splits
 CASES = [(2, 8, 2, 1, 1000, False, 4), (1, 4, 4, 3, 777, True, 1),
-         (2, 16, 4, 4, 2048, True, 7), (3, 8, 8, 1, 65, False, 2)]
+         (2, 16, 4, 4, 2048, True, 7), (3, 8, 8, 1, 65, False, 2),
+         # several 32-row tiles of packed (query, head) rows per KV head
+         (1, 16, 2, 9, 1500, True, 3), (2, 32, 4, 5, 2000, True, 5)]
 
 
 @pytest.mark.parametrize("D", DIMS)
@@ -58,16 +61,22 @@ def test_splitkv_dims_match_oracle(case, D):
 
 @pytest.mark.parametrize("D", DIMS)
 def test_paged_dims_match_oracle(D):
+    """fp32 output against the oracle; the bf16 output of the same call is
+    the round-to-nearest-even of the fp32 one, with the same lse."""
     SCALE = _scale(D)
     B, Hq, Hkv, Nq, P, maxp = 3, 8, 2, 2, 64, 10
     lens = [1, 400, 640]
     print(f"d{D} paged", flush=True)
     q, kc, vc, table, sl = make_paged(B, Hq, Hkv, Nq, D, P, maxp, lens,
                                       seed=72)
-    o, lse = _ops().fa_fwd_paged(dev(q), dev(kc), dev(vc), _i32(table),
-                                 _i32(sl), causal=True, scale=SCALE,
+    args = (dev(q), dev(kc), dev(vc), _i32(table), _i32(sl))
+    o, lse = _ops().fa_fwd_paged(*args, causal=True, scale=SCALE,
                                  out_dtype=torch.float32)
+    o16, l16 = _ops().fa_fwd_paged(*args, causal=True, scale=SCALE,
+                                   out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    assert torch.equal(o.to(torch.bfloat16), o16), "bf16 O != RNE(fp32 O)"
+    assert torch.equal(lse, l16)
     O_ref, L_ref = paged_attention(f64(q), f64(kc), f64(vc), table, sl,
                                    causal=True, scale=SCALE)
     compare(host(o), host(lse), O_ref, L_ref, what=f"d{D} paged")
@@ -85,10 +94,14 @@ def test_kvlen_dims_match_oracle(window, D):
     for b, n in enumerate(lens):
         k[b, :, n:] = np.uint16(0x7FC0)
         v[b, :, n:] = np.uint16(0x7FC0)
-    o, lse = _ops().fa_fwd_kvlen(dev(q), dev(k), dev(v), _i32(lens),
-                                 causal=True, scale=SCALE, window=window,
-                                 out_dtype=torch.float32)
+    args = (dev(q), dev(k), dev(v), _i32(lens))
+    o, lse = _ops().fa_fwd_kvlen(*args, causal=True, scale=SCALE,
+                                 window=window, out_dtype=torch.float32)
+    o16, l16 = _ops().fa_fwd_kvlen(*args, causal=True, scale=SCALE,
+                                   window=window, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    assert torch.equal(o.to(torch.bfloat16), o16), "bf16 O != RNE(fp32 O)"
+    assert torch.equal(lse, l16)
     O_ref, L_ref = kvlen_attention(f64(q), f64(k), f64(v), lens, causal=True,
                                    scale=SCALE, window=window)
     compare(host(o), host(lse), O_ref, L_ref, what=f"d{D} kvlen {window}")

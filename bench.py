@@ -24,7 +24,10 @@ pair, counted exactly.  ``--workload decode_window`` runs the decode workload th
 ``fa_fwd_window`` with a 4096-key window (KV split over the window's keys),
 priced at the bytes of the keys it must read.  ``--workload decode_paged`` runs ``fa_fwd_paged`` on the decode workload's
 shape stored in 256-key pages scattered over the pool, priced like the
-decode.  ``--workload gqa_prefill_fp8`` runs ``fa_fwd_fp8`` on the GQA prefill's shape
+decode.  ``--workload gqa_prefill_paged`` runs ``fa_fwd_paged`` on the GQA
+prefill's shape stored in 256-key pages scattered over the pool (the tiled
+prefill kernel reading each block from its page), priced like the GQA
+prefill.  ``--workload gqa_prefill_fp8`` runs ``fa_fwd_fp8`` on the GQA prefill's shape
 with E4M3 inputs and reports TFLOP/s against the FP8 matrix-core peak.
 ``--workload gqa_prefill_sparse`` runs ``fa_fwd_block_sparse`` on the GQA
 prefill with a seeded block mask (a quarter of the 128 x 64 blocks plus the
@@ -74,7 +77,8 @@ WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "gqa_prefill_window": 3, "decode_window": 4,
              "gqa_prefill_window_bwd": 3, "decode_paged": None,
              "gqa_prefill_fp8": None, "gqa_prefill_sparse": None,
-             "gqa_prefill_docmask": None, "decode_d256": 4}
+             "gqa_prefill_docmask": None, "decode_d256": 4,
+             "gqa_prefill_paged": None}
 # workloads that change one configuration's shape: head dimension 256 on
 # the decode (half the keys, so the same K/V bytes)
 VARIANTS = {"decode_d256": dict(name="decode_b16_hq32_hkv8_nq1_nk16384_d256",
@@ -376,59 +380,78 @@ def bench_varlen(args):
 
 
 # the decode workload's shape over a paged cache: 256-key pages, 128 per
-# sequence, scattered over the pool
+# sequence, scattered over the pool (KV-split form)
 PAGED_DECODE = dict(name="decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256",
                     B=16, Hq=32, Hkv=8, Nq=1, d=128, page_size=256,
-                    max_pages=128, scale=1.0 / math.sqrt(128))
+                    max_pages=128, causal=False, scale=1.0 / math.sqrt(128))
+# the GQA prefill's shape over a paged cache: 8192 queries over their own
+# 8192 keys in 32 scattered 256-key pages (prefill form)
+PAGED_PREFILL = dict(
+    name="gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256",
+    B=1, Hq=32, Hkv=8, Nq=8192, d=128, page_size=256, max_pages=32,
+    causal=True, scale=1.0 / math.sqrt(128))
 
 
-def bench_paged(args):
-    """One fa_fwd_paged call (partial + merge kernels, workspace allocated
-    once) over the decode workload's shape stored in scattered pages."""
+def bench_paged(args, sp):
+    """One fa_fwd_paged call over a shape stored in scattered pages: the
+    decode (partial + merge kernels, workspace allocated once), priced at
+    its K/V bytes, or the prefill (the tiled kernel reading each block from
+    its page), priced at the forward FLOPs."""
     import torch
     from exact_io_aware_05_amd import ops
-    sp = PAGED_DECODE
     B, Hq, Hkv, Nq, d = sp["B"], sp["Hq"], sp["Hkv"], sp["Nq"], sp["d"]
     P, maxp = sp["page_size"], sp["max_pages"]
-    lens = [P * maxp] * B
+    Nk = P * maxp
+    lens = [Nk] * B
     q, kc, vc, table, sl = make_paged(B, Hq, Hkv, Nq, d, P, maxp, lens, seed=0)
     Q, KC, VC = _dev_tensor(q), _dev_tensor(kc), _dev_tensor(vc)
     del kc, vc
     T = torch.from_numpy(table).cuda()
     SL = torch.from_numpy(sl).cuda()
     splits = ops.paged_num_splits(B, Hq, Hkv, Nq, d, P, maxp)
-    ws = torch.empty(ops.splitkv_workspace_bytes(B, Hq, Nq, d, splits),
+    ws = torch.empty(max(ops.splitkv_workspace_bytes(B, Hq, Nq, d, splits)
+                         if splits else 0, 16),
                      dtype=torch.uint8, device="cuda")
     o = torch.empty((B, Hq, Nq, d), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device="cuda")
 
     def step():
-        ops.fa_fwd_paged(Q, KC, VC, T, SL, scale=sp["scale"], o=o, lse=lse,
-                         num_splits=splits, workspace=ws)
+        ops.fa_fwd_paged(Q, KC, VC, T, SL, causal=sp["causal"],
+                         scale=sp["scale"], o=o, lse=lse, num_splits=splits,
+                         workspace=ws)
 
     ms, kern_ms = _time_steps(step, args.steps, args.warmup,
                               torch.cuda.current_stream())
-    nbytes = attention_fwd_bytes(B, Hq, Hkv, Nq, P * maxp, d)
-    achieved = nbytes / (kern_ms * 1e-3) / 1e9
-    out = {
-        "metric": f"attn decode HBM GB/s ({sp['name']})",
-        "value": round(nbytes / (ms * 1e-3) / 1e9, 3), "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) fp32 rounded to bf16; seeded "
-                "page permutation)",
-        "config": {"workload": sp["name"], "B": B, "Hq": Hq, "Hkv": Hkv,
-                   "Nq": Nq, "Nk": P * maxp, "d": d, "page_size": P,
-                   "pages_per_seq": maxp, "causal": False,
-                   "scale": sp["scale"], "out_dtype": "bf16",
-                   "kv_splits": splits, "kernel_ms": round(kern_ms, 4)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 2),
-                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": measured_traffic(sp["name"])},
-        "cpu_baseline": None,
-    }
+    data = ("synthetic (seeded N(0,1) fp32 rounded to bf16; seeded page "
+            "permutation)")
+    config = {"workload": sp["name"], "B": B, "Hq": Hq, "Hkv": Hkv, "Nq": Nq,
+              "Nk": Nk, "d": d, "page_size": P, "pages_per_seq": maxp,
+              "causal": sp["causal"], "scale": sp["scale"],
+              "out_dtype": "bf16", "kv_splits": splits,
+              "kernel_ms": round(kern_ms, 4)}
+    if splits:
+        nbytes = attention_fwd_bytes(B, Hq, Hkv, Nq, Nk, d)
+        achieved = nbytes / (kern_ms * 1e-3) / 1e9
+        out = {"metric": f"attn decode HBM GB/s ({sp['name']})",
+               "value": round(nbytes / (ms * 1e-3) / 1e9, 3), "unit": "GB/s"}
+        roof = {"bound": "hbm", "achieved": round(achieved, 2),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        flops = attention_fwd_flops(B, Hq, Nq, Nk, d, sp["causal"])
+        achieved = flops / (kern_ms * 1e-3) / 1e12
+        out = {"metric": f"attn fwd TFLOP/s ({sp['name']})",
+               "value": round(flops / (ms * 1e-3) / 1e12, 3),
+               "unit": "TFLOP/s"}
+        roof = {"bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4)}
+    roof["traffic"] = measured_traffic(sp["name"])
+    out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": round(ms, 4), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                "data": data, "config": config, "roofline": roof,
+                "cpu_baseline": None})
     print(json.dumps(out), flush=True)
     return 0
 
@@ -687,7 +710,9 @@ def main(argv=None):
     if args.workload == "varlen_prefill":
         return bench_varlen(args)
     if args.workload == "decode_paged":
-        return bench_paged(args)
+        return bench_paged(args, PAGED_DECODE)
+    if args.workload == "gqa_prefill_paged":
+        return bench_paged(args, PAGED_PREFILL)
     if args.workload == "gqa_prefill_fp8":
         return bench_fp8(args)
     if args.workload == "gqa_prefill_sparse":

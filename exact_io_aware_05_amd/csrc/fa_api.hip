@@ -332,25 +332,55 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o,
                      stream);
 }
 
-int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
-                        int max_pages_per_seq) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Hq % Hkv) return 0;
-  if (d != 32 && d != 64 && d != 128 && d != 256) return 0;
+}  // extern "C" (reopened below)
+
+namespace {
+
+// Can a paged call run the prefill kernel?  Its 64-key blocks must lie
+// inside one page (pages of at least 64 keys), a sequence's page numbers
+// must fit the kernel's LDS list, and 64 rows of a page are addressed with
+// 32-bit byte offsets.
+bool paged_prefill_ok(int Hkv, int d, int page_size, int max_pages) {
+  return (dim_bit(d) & kDimsPrefill) &&
+         page_size >= fa::kPagedPrefillMinPage &&
+         max_pages <= fa::kPagedPrefillMaxPages &&
+         (long long)fa::kPrefillKeys * Hkv * d * 2 < (1LL << 31);
+}
+
+// The form a paged call with num_splits = 0 runs: 0 for the prefill kernel
+// (many query rows per KV head, as fa_fwd decides, or d = 96), otherwise
+// the KV-split form's chunk count (as fa_fwd would split a cache of the
+// longest length, and enough chunks that none spans 64 pages); -1 when no
+// form takes the shape.  Pure host arithmetic.
+int paged_form(int B, int Hq, int Hkv, int Nq, int d, int page_size,
+               int max_pages_per_seq) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Nq < 1 || Hq % Hkv) return -1;
+  if (!(dim_bit(d) & kDimsAny)) return -1;
   if (page_size < fa::kSplitKeys || (page_size & (page_size - 1)) ||
       max_pages_per_seq < 1)
-    return 0;
+    return -1;
   const long long nk = (long long)page_size * max_pages_per_seq;
-  if (nk > (1LL << 30)) return 0;
-  // as fa_fwd would split a cache of the longest length (at least one
-  // chunk: the paged form is always the KV-split form), and enough chunks
-  // that none spans 64 pages
+  if (nk > (1LL << 30)) return -1;
+  const bool pre = paged_prefill_ok(Hkv, d, page_size, max_pages_per_seq);
   int s = default_splits(B, Hq, Hkv, Nq, (int)nk);
+  if (d == 96) return pre ? 0 : -1;
+  if (s == 0 && pre) return 0;
   if (s < 1) s = 1;
   const long long nblk = (nk + fa::kSplitKeys - 1) / fa::kSplitKeys;
   const long long per = fa::paged_max_blocks_per_chunk(page_size);
   const long long need = (nblk + per - 1) / per;
   if (s < need) s = (int)need;
-  return s <= fa::kMaxSplits ? s : 0;
+  return s <= fa::kMaxSplits ? s : -1;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
+                        int max_pages_per_seq) {
+  const int f = paged_form(B, Hq, Hkv, Nq, d, page_size, max_pages_per_seq);
+  return f > 0 ? f : 0;
 }
 
 int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
@@ -371,16 +401,50 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
   const long long nk = (long long)page_size * max_pages_per_seq;
   if (nk > (1LL << 30)) return FA_ERR_UNSUPPORTED;
   int st = check_common(q, k_cache, v_cache, o, lse, B, Hq, Hkv, Nq, (int)nk,
-                        d, scale, out_dtype, kDimsSplit);
+                        d, scale, out_dtype, kDimsAny);
   if (st != FA_OK) return st;
   if ((long long)num_pages * page_size * Hkv * d > (1LL << 46))
     return FA_ERR_UNSUPPORTED;
-  const int need = fa_paged_num_splits(B, Hq, Hkv, Nq, d, page_size,
-                                       max_pages_per_seq);
-  if (need == 0) return FA_ERR_UNSUPPORTED;
-  const int splits = num_splits == 0 ? need : num_splits;
+  if (num_splits < 0) return FA_ERR_INVALID_ARG;
+  fa::Shape s{B, Hq, Hkv, Nq, (int)nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  int splits = num_splits;
+  if (splits == 0) {
+    splits = paged_form(B, Hq, Hkv, Nq, d, page_size, max_pages_per_seq);
+    if (splits < 0) return FA_ERR_UNSUPPORTED;
+    if (splits == 0) {
+      // prefill form: the tiled kernel reads each 64-key block from its
+      // page; no workspace
+      st = check_device();
+      if (st != FA_OK) return st;
+      fa::SeqLayout lay{};
+      lay.q_r = d;
+      lay.q_h = (long long)Nq * d;
+      lay.q_b = lay.q_h * Hq;
+      lay.k_r = (long long)Hkv * d;
+      lay.k_h = d;
+      lay.k_b = 0;
+      lay.l_r = 1;
+      lay.l_h = Nq;
+      lay.l_b = (long long)Hq * Nq;
+      fa::same_vo(lay);
+      lay.seqlen_k = seqlens_k;
+      lay.page_table = page_table;
+      lay.max_pages = max_pages_per_seq;
+      lay.page_shift = shift;
+      lay.num_pages = num_pages;
+      return hip_status(fa::launch_prefill(q, k_cache, v_cache, o, lse, s,
+                                           lay, out_dtype == FA_OUT_F32,
+                                           stream));
+    }
+  }
+  // KV-split form
+  if (!(dim_bit(d) & kDimsSplit)) return FA_ERR_UNSUPPORTED;
   const long long nblk = (nk + fa::kSplitKeys - 1) / fa::kSplitKeys;
-  if (splits < 1 || splits > fa::kMaxSplits ||
+  if (splits > fa::kMaxSplits ||
       (nblk + splits - 1) / splits > fa::paged_max_blocks_per_chunk(page_size))
     return FA_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
@@ -393,11 +457,6 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
     return FA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != FA_OK) return st;
-  fa::Shape s{B, Hq, Hkv, Nq, (int)nk, d, causal, scale};
-  s.win_left = window_left;
-  s.win_right = window_right;
-  int shift = 0;
-  while ((1 << shift) < page_size) ++shift;
   const fa::PagedKv pg{page_table, seqlens_k, max_pages_per_seq, page_size,
                        num_pages, shift};
   return hip_status(fa::launch_splitkv_paged(q, k_cache, v_cache, o, lse, s,
@@ -415,14 +474,28 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
   if (!seqlens_k || (reinterpret_cast<uintptr_t>(seqlens_k) & 3u))
     return FA_ERR_INVALID_ARG;
   int st = check_common(q, k, v, o, lse, B, Hq, Hkv, Nq, Nk, d, scale,
-                        out_dtype, kDimsSplit);
+                        out_dtype, kDimsAny);
   if (st != FA_OK) return st;
   // one K or V head is addressed with 32-bit byte offsets
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
-  const int splits = num_splits == 0 ? fa_default_num_splits(B, Hq, Hkv, Nq,
-                                                             Nk, d)
+  if (num_splits < 0) return FA_ERR_INVALID_ARG;
+  fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
+  s.win_left = window_left;
+  s.win_right = window_right;
+  const int splits = num_splits == 0 ? forward_splits(B, Hq, Hkv, Nq, Nk, d)
                                      : num_splits;
-  if (splits < 1 || splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
+  if (splits == 0) {
+    // prefill form (many query rows per KV head, or d = 96): the tiled
+    // kernel with each sequence's key count; no workspace
+    st = check_device();
+    if (st != FA_OK) return st;
+    fa::SeqLayout lay = fa::dense_layout(s);
+    lay.seqlen_k = seqlens_k;
+    return hip_status(fa::launch_prefill(q, k, v, o, lse, s, lay,
+                                         out_dtype == FA_OUT_F32, stream));
+  }
+  if (!(dim_bit(d) & kDimsSplit)) return FA_ERR_UNSUPPORTED;
+  if (splits > fa::kMaxSplits) return FA_ERR_INVALID_ARG;
   if (!workspace || !aligned16(workspace)) return FA_ERR_INVALID_ARG;
   if (workspace_bytes <
       fa::splitkv_workspace_bytes((long long)B * Hq * Nq, d, splits))
@@ -433,9 +506,6 @@ int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
     return FA_ERR_UNSUPPORTED;
   st = check_device();
   if (st != FA_OK) return st;
-  fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
-  s.win_left = window_left;
-  s.win_right = window_right;
   return hip_status(fa::launch_splitkv_kvlen(q, k, v, o, lse, s, seqlens_k,
                                              out_dtype == FA_OUT_F32, splits,
                                              workspace, stream));

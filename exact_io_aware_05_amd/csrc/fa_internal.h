@@ -58,7 +58,12 @@ inline int band_tile_blocks(const Shape& s, const MaskBounds& m, int kb) {
 // cu_k = nullptr.  Packed variable-length batches take sequence b's rows
 // from cu_q[b] .. cu_q[b + 1] (and cu_k for K/V), the batch strides unused;
 // Nq / Nk of the Shape are then the maximum lengths and total_q / total_k
-// the row counts of the packed tensors.
+// the row counts of the packed tensors.  Fixed-length batches may give each
+// sequence its own key count, seqlen_k[b] (device, clamped to [0, Nk]; the
+// rows past it are never read).  A paged cache (the paged instances of the
+// prefill kernel) keeps key row r of sequence b in row r % page_size of
+// page page_table[b][r / page_size], rows k_r elements apart across pages
+// too, head h at h * k_h; k_b and v_b are then 0.
 struct SeqLayout {
   long long q_b, q_h, q_r;
   long long k_b, k_h, k_r;
@@ -69,6 +74,9 @@ struct SeqLayout {
   int n_seq;  // sequences of a packed batch (cu_q, cu_k: n_seq + 1 entries)
   long long v_b, v_h, v_r;  // V (same as K unless given apart)
   long long o_b, o_h, o_r;  // O (same as Q unless given apart)
+  const int* seqlen_k;      // per-sequence key counts, or nullptr
+  const int* page_table;    // paged: [B, max_pages] page numbers
+  int max_pages, page_shift, num_pages;  // page_size = 1 << page_shift
 };
 
 // V laid out like K and O like Q.
@@ -105,6 +113,8 @@ constexpr int kSplitKeys = 32;
 constexpr int kSplitRows = 32;
 constexpr int kMaxSplits = 4096;
 
+// The tiled prefill kernel over the rows `lay` describes; a layout with a
+// page table runs the paged instances (k and v are then the caches).
 hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           void* o, float* lse, const Shape& s,
                           const SeqLayout& lay, bool out_f32,
@@ -116,6 +126,10 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
 // share a mask).  A zero byte skips the block.
 constexpr int kSparseRows = 128;
 constexpr int kSparseMaxKeyBlocks = 8191;  // the key-block list fills LDS
+// Pages per sequence that the paged prefill form keeps in the same LDS
+// list (one int per page); its pages hold whole 64-key blocks.
+constexpr int kPagedPrefillMaxPages = 8192;
+constexpr int kPagedPrefillMinPage = 64;
 struct BlockMask {
   const uint8_t* mask;
   long long mb, mh;

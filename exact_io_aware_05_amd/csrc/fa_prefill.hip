@@ -141,6 +141,23 @@ __device__ __forceinline__ void barrier() {
 // row in memory (2 d, less than the tile's row when the head dimension d is
 // narrower than the tile); instructions i >= `zero_from` copy zeros (the K
 // chunks of columns past d).
+// The copy instructions of one block whose row 0 is at `base`, of which
+// the first `rem` bytes may be read (0: a copy of zeros).
+template <int D>
+__device__ __forceinline__ void copy_rows(char* dst, const char* base,
+                                          int rem, int wave,
+                                          uint32_t lane_off, int step,
+                                          int zero_from) {
+  using L = Layout<D>;
+#pragma unroll
+  for (int n = 0; n < L::NINS / NW; ++n) {
+    const int i = wave + NW * n;
+    const int left = i < zero_from ? rem - step * i : 0;
+    dma16(dst + 1024 * i, base + step * i, (uint32_t)(left > 0 ? left : 0),
+          lane_off);
+  }
+}
+
 template <int D>
 __device__ __forceinline__ void copy_block(char* dst, const char* head,
                                            int Nk, int blk, int wave,
@@ -149,18 +166,26 @@ __device__ __forceinline__ void copy_block(char* dst, const char* head,
                                            int zero_from = 1 << 30) {
   // (Nk here: number of rows that may be read; later rows read as zeros.
   // A head spans less than 2^31 bytes, so 32-bit offsets suffice.)
-  using L = Layout<D>;
   // (a block before the first, blk < 0, is a copy of zeros too)
   const int kb = min(max(blk, 0) * BC, Nk);
   const char* base = head + (int64_t)kb * rsb;
   const int rem = (blk >= 0 && kb < Nk) ? (Nk - kb - 1) * rsb + rowb : 0;
-#pragma unroll
-  for (int n = 0; n < L::NINS / NW; ++n) {
-    const int i = wave + NW * n;
-    const int left = i < zero_from ? rem - step * i : 0;
-    dma16(dst + 1024 * i, base + step * i, (uint32_t)(left > 0 ? left : 0),
-          lane_off);
-  }
+  copy_rows<D>(dst, base, rem, wave, lane_off, step, zero_from);
+}
+
+// The same for a block of a paged cache: `roff` is the byte offset of the
+// block's row 0 from `head` (its page's row), or negative for a block that
+// is not read (a copy of zeros); rows from `rows` on read as zeros.  The
+// block lies inside one page, so 32-bit lane offsets suffice.
+template <int D>
+__device__ __forceinline__ void copy_block_paged(char* dst, const char* head,
+                                                 int64_t roff, int rows,
+                                                 int wave, uint32_t lane_off,
+                                                 int step, int rsb, int rowb,
+                                                 int zero_from = 1 << 30) {
+  const int rem = roff >= 0 ? (min(rows, BC) - 1) * rsb + rowb : 0;
+  copy_rows<D>(dst, head + (roff >= 0 ? roff : 0), rem, wave, lane_off, step,
+               zero_from);
 }
 
 // s_waitcnt with vmcnt = N (expcnt, lgkmcnt left free); gfx9 encoding.
@@ -366,7 +391,7 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
 constexpr int kNone = 0, kCausal = 1, kBand = 2;
 
 template <int D, int MODE, bool OUT_F32, bool SPARSE = false,
-          bool COLUMN = false>
+          bool COLUMN = false, bool PAGED = false>
 __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, void* __restrict__ o,
@@ -380,6 +405,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
                 "column masks go with no mask or causal");
   // a list of key blocks in LDS drives the loop (block or column mask)
   constexpr bool LISTED = SPARSE || COLUMN;
+  static_assert(!(PAGED && LISTED), "paged caches go with the band masks");
   constexpr int BLKBITS = COLUMN ? 0xFFFF : 0xFFFFFF;
   // K/V ring depth: 8 stages of 8 KiB blocks at d = 64, 4 of 16 KiB at
   // d = 128 (128 KiB of LDS either way, leaving 32 KiB for the block list
@@ -389,7 +415,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // block-sparse: the key blocks this workgroup computes, in order (bits
   // 0..23 the block, bit 24 / 25 set when the rows of group A / B use it),
   // then their count
-  __shared__ int blist[LISTED ? kSparseMaxKeyBlocks + 1 : 1];
+  // paged cache: the page numbers of the pages this workgroup reads
+  __shared__ int blist[LISTED  ? kSparseMaxKeyBlocks + 1
+                       : PAGED ? kPagedPrefillMaxPages
+                               : 1];
   constexpr int NTILE = L::NTILE;
   constexpr int NSTEP = L::NSTEP;
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
@@ -461,6 +490,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     obase = qs * lay.o_r + hq * lay.o_h;
     lbase = qs * lay.l_r + hq * lay.l_h;
   } else {
+    // (a sequence's own key count, clamped into the cache)
+    if (lay.seqlen_k) Nk = min(max(lay.seqlen_k[b], 0), Nk_max);
     qbase = b * lay.q_b + hq * lay.q_h;
     kbase = b * lay.k_b + hkv * lay.k_h;
     vbase = b * lay.v_b + hkv * lay.v_h;
@@ -485,6 +516,21 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     j0 = max(0, q0 + off - wl) / BC;
   }
   const int nblk = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+
+  // ---- paged cache: the page numbers of the pages that hold blocks j0 ..
+  // nblk - 1, clamped into the pool, go to LDS (the host keeps a sequence's
+  // pages within the list, and its length within its pages: the last page
+  // read is at most max_pages - 1)
+  int p0 = 0;
+  if (PAGED) {
+    p0 = (j0 * BC) >> lay.page_shift;
+    const int np =
+        nblk > j0 ? ((nblk * BC - 1) >> lay.page_shift) - p0 + 1 : 0;
+    const int* tb = lay.page_table + (int64_t)b * lay.max_pages + p0;
+    for (int i = tid; i < np; i += NT)
+      blist[i] = min(max(tb[i], 0), lay.num_pages - 1);
+    __syncthreads();
+  }
 
   // ---- block-sparse: wave 0 lists the key blocks below nblk that either
   // 128-row half of this workgroup keeps (mask rows 2 qblk and 2 qblk + 1)
@@ -704,12 +750,36 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // (V_{j0-1}, before the first block, is a copy of zeros: block j0's
   // matrix phase multiplies it by the all-zero "previous" P, and 0 *
   // (stale NaN/Inf bits) would not be 0)
+  // paged cache: byte offset of block blk's row 0 from the head's base
+  // (its page's row, K and V alike), negative for a block past the keys;
+  // groups are issued in order, so V_{g-1} reuses K_{g-1}'s offset
+  int64_t prev_ro = -1;
+  auto page_off = [&](int blk) -> int64_t {
+    const int kb = blk * BC;
+    if (kb >= kv_rows) return -1;
+    const int pg = __builtin_amdgcn_readfirstlane(
+        blist[(kb >> lay.page_shift) - p0]);
+    return (((int64_t)pg << lay.page_shift) |
+            (kb & ((1 << lay.page_shift) - 1))) * rsb;
+  };
   auto group = [&](int g) {
-    copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, blk_at(g),
-                  wave, k_off, 16, rsb, 2 * dq, dq / 8);
-    copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
-                  vh, kv_rows, g > j0 ? blk_at(g - 1) : -1, wave, v_off,
-                  v_step, rsbv, 2 * dq);
+    if constexpr (PAGED) {
+      const int64_t ro = page_off(g);
+      copy_block_paged<D>(smem + (g % L::NS) * L::KBYTES, kh, ro,
+                          kv_rows - g * BC, wave, k_off, 16, rsb, 2 * dq,
+                          dq / 8);
+      copy_block_paged<D>(
+          smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES, vh,
+          g > j0 ? prev_ro : -1, kv_rows - (g - 1) * BC, wave, v_off, v_step,
+          rsbv, 2 * dq);
+      prev_ro = ro;
+    } else {
+      copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, blk_at(g),
+                    wave, k_off, 16, rsb, 2 * dq, dq / 8);
+      copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
+                    vh, kv_rows, g > j0 ? blk_at(g - 1) : -1, wave, v_off,
+                    v_step, rsbv, 2 * dq);
+    }
   };
   auto copies = [&](int j) { group(j + L::NS - 1); };
   // prologue: groups j0 .. j0 + NS - 2.  The first two must have landed for
@@ -828,7 +898,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
 }
 
 template <int D, int MODE, bool OUT_F32, bool SPARSE = false,
-          bool COLUMN = false>
+          bool COLUMN = false, bool PAGED = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
                   float* lse, const Shape& s, const SeqLayout& lay, int wl,
                   int wr, hipStream_t stream, const BlockMask& bm = {},
@@ -846,7 +916,7 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   // below 2^-24 in magnitude, so each weight is exactly 1, and -inf scores
   // stay -inf (no 0 * inf)
   const float c2 = fmaxf(s.scale * kLog2e, 1.17549435e-38f);
-  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32, SPARSE, COLUMN>),
+  hipLaunchKernelGGL((prefill_kernel<D, MODE, OUT_F32, SPARSE, COLUMN, PAGED>),
                      dim3((unsigned)n_items), dim3(NT), 0, stream,
                      static_cast<const uint16_t*>(q),
                      static_cast<const uint16_t*>(k),
@@ -856,29 +926,29 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
   return hipGetLastError();
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool PAGED>
 hipError_t launch_mode(const void* q, const void* k, const void* v, void* o,
                        float* lse, const Shape& s, const SeqLayout& lay,
                        int wl, int wr, bool out_f32, hipStream_t stream) {
-  return out_f32 ? launch<D, MODE, true>(q, k, v, o, lse, s, lay, wl, wr,
-                                         stream)
-                 : launch<D, MODE, false>(q, k, v, o, lse, s, lay, wl, wr,
-                                          stream);
+  return out_f32 ? launch<D, MODE, true, false, false, PAGED>(
+                       q, k, v, o, lse, s, lay, wl, wr, stream)
+                 : launch<D, MODE, false, false, false, PAGED>(
+                       q, k, v, o, lse, s, lay, wl, wr, stream);
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_d(const void* q, const void* k, const void* v, void* o,
                     float* lse, const Shape& s, const SeqLayout& lay,
                     bool out_f32, hipStream_t stream) {
   const MaskBounds m = mask_bounds(s);
   if (m.kind == 0)
-    return launch_mode<D, kNone>(q, k, v, o, lse, s, lay, 0, 0, out_f32,
-                                 stream);
+    return launch_mode<D, kNone, PAGED>(q, k, v, o, lse, s, lay, 0, 0,
+                                        out_f32, stream);
   if (m.kind == 1)
-    return launch_mode<D, kCausal>(q, k, v, o, lse, s, lay, 0, 0, out_f32,
-                                   stream);
-  return launch_mode<D, kBand>(q, k, v, o, lse, s, lay, m.wl, m.wr, out_f32,
-                               stream);
+    return launch_mode<D, kCausal, PAGED>(q, k, v, o, lse, s, lay, 0, 0,
+                                          out_f32, stream);
+  return launch_mode<D, kBand, PAGED>(q, k, v, o, lse, s, lay, m.wl, m.wr,
+                                      out_f32, stream);
 }
 
 }  // namespace
@@ -945,10 +1015,15 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           hipStream_t stream) {
   // head dimension 96 runs in the 128-column tile and 32 in the 64-column
   // one, the columns past d masked (Q and K read as zeros, O not stored)
+  const bool paged = lay.page_table != nullptr;
   if (s.d == 128 || s.d == 96)
-    return launch_d<128>(q, k, v, o, lse, s, lay, out_f32, stream);
+    return paged ? launch_d<128, true>(q, k, v, o, lse, s, lay, out_f32, stream)
+                 : launch_d<128, false>(q, k, v, o, lse, s, lay, out_f32,
+                                        stream);
   if (s.d == 64 || s.d == 32)
-    return launch_d<64>(q, k, v, o, lse, s, lay, out_f32, stream);
+    return paged ? launch_d<64, true>(q, k, v, o, lse, s, lay, out_f32, stream)
+                 : launch_d<64, false>(q, k, v, o, lse, s, lay, out_f32,
+                                       stream);
   return hipErrorInvalidValue;
 }
 

@@ -286,10 +286,11 @@ def fa_fwd_paged(q, k_cache, v_cache, page_table, seqlens_k, causal=False,
     max_pages = page_table.shape[1]
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    # (0: the library runs the prefill form, which takes no workspace)
     splits = int(num_splits) or paged_num_splits(B, Hq, Hkv, Nq, d, page_size,
                                                  max_pages)
     if workspace is None:
-        need = splitkv_workspace_bytes(B, Hq, Nq, d, max(splits, 1))
+        need = splitkv_workspace_bytes(B, Hq, Nq, d, splits) if splits else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8,
                                 device=q.device)
     left, right = (int(x) for x in window)
@@ -346,9 +347,10 @@ def fa_fwd_kvlen(q, k, v, seqlens_k, causal=False, scale=None,
                          "tensor [B]")
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     o, lse = _out(q, B, Hq, Nq, d, out_dtype, o, lse)
+    # (0: the library runs the prefill form, which takes no workspace)
     splits = int(num_splits) or default_num_splits(B, Hq, Hkv, Nq, Nk, d)
     if workspace is None:
-        need = splitkv_workspace_bytes(B, Hq, Nq, d, max(splits, 1))
+        need = splitkv_workspace_bytes(B, Hq, Nq, d, splits) if splits else 0
         workspace = torch.empty(max(need, 16), dtype=torch.uint8,
                                 device=q.device)
     left, right = (int(x) for x in window)

@@ -42,12 +42,14 @@
  *     fa_fwd, fa_fwd_noalloc, fa_fwd_window      32, 64, 96, 128, 256
  *     fa_fwd_varlen, fa_fwd_strided,
  *     fa_fwd_block_sparse, fa_fwd_colmask        32, 64, 96, 128
- *     fa_fwd_splitkv, fa_fwd_paged, fa_fwd_kvlen 32, 64, 128, 256
+ *     fa_fwd_paged, fa_fwd_kvlen                 32, 64, 96, 128, 256
+ *     fa_fwd_splitkv                             32, 64, 128, 256
  *     fa_bwd, fa_bwd_window                      64, 128
  *     fa_fwd_fp8                                 128
  *   32 and 96 run in the 64- and 128-column tiles of the prefill kernel
- *   with the columns past d masked; fa_fwd and fa_fwd_window take d = 96
- *   always in the prefill kernel and d = 256 always in the KV-split form.
+ *   with the columns past d masked; fa_fwd, fa_fwd_window, fa_fwd_paged
+ *   and fa_fwd_kvlen take d = 96 only in the prefill kernel and d = 256
+ *   only in the KV-split form.
  * - Every call is asynchronous: it validates its arguments on the host,
  *   enqueues kernels on `stream` and returns.  Results are valid once the
  *   stream has been synchronised; buffers must stay alive until then.
@@ -281,7 +283,8 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
                    int out_dtype, hipStream_t stream);
 
 /*
- * Forward over a paged KV cache (decode and short chunks of queries).
+ * Forward over a paged KV cache (decode, and chunks of queries over a
+ * cache: chunked prefill).
  * "FlashAttention Analysis" (ryotta.opik.net), in its closing section on
  * where the method sits, notes that paged KV caches (PagedAttention, vLLM)
  * run the fused kernels inside; the layout below is that of common serving
@@ -300,16 +303,28 @@ int fa_fwd_strided(const void* q, const void* k, const void* v, void* o,
  * are read on the device; a length is clamped to [0, max_pages_per_seq *
  * page_size] and a page number to [0, num_pages), so bad tables give wrong
  * results but no access outside the caches.  A sequence with no keys gets
- * O = 0 and lse = -inf.  The KV-split form always runs (partial + merge
- * kernels); num_splits = 0 takes fa_paged_num_splits(...), otherwise it
- * must be 1 .. 4096 with no chunk over 62 pages of 32-key blocks
- * (ceil(max_pages_per_seq * page_size / 32 / num_splits) <= 62 *
- * page_size / 32).  `workspace` (16-byte aligned, device) holds at least
- * fa_splitkv_workspace_bytes(B, Hq, Nq, d, splits) bytes.  Errors as for
- * fa_fwd; FA_ERR_INVALID_ARG also for null or misaligned tables, a bad
- * page_size, num_pages or max_pages_per_seq < 1, a bound below -1, a bad
- * split count or a small workspace; FA_ERR_UNSUPPORTED when
- * max_pages_per_seq * page_size exceeds 2^30.
+ * O = 0 and lse = -inf.  Two forms:
+ *   - num_splits = 0 and fa_paged_num_splits(...) = 0: the tiled prefill
+ *     kernel, each 64-key block read from its page.  Chosen when a KV head
+ *     has many query rows (Nq * Hq / Hkv > 64, as fa_fwd decides) or
+ *     d = 96, provided page_size >= 64, max_pages_per_seq <= 8192 and
+ *     d <= 128.  `workspace` is not used (may be NULL).
+ *   - otherwise the KV-split form (partial + merge kernels) with
+ *     fa_paged_num_splits(...) chunks (num_splits = 0) or num_splits
+ *     chunks (1 .. 4096, no chunk over 62 pages of 32-key blocks:
+ *     ceil(max_pages_per_seq * page_size / 32 / num_splits) <= 62 *
+ *     page_size / 32).  `workspace` (16-byte aligned, device) holds at
+ *     least fa_splitkv_workspace_bytes(B, Hq, Nq, d, splits) bytes.
+ * Errors as for fa_fwd; FA_ERR_INVALID_ARG also for null or misaligned
+ * tables, a bad page_size, num_pages or max_pages_per_seq < 1, a bound
+ * below -1, a bad split count or (KV-split form) a small workspace;
+ * FA_ERR_UNSUPPORTED when max_pages_per_seq * page_size exceeds 2^30, or
+ * for d = 96 where the prefill form does not apply (pages of 32 keys, more
+ * than 8192 pages per sequence, num_splits > 0).
+ *
+ * fa_paged_num_splits returns the chunk count of the KV-split form for
+ * num_splits = 0, or 0 when the prefill form runs (and for sizes that no
+ * form takes).  Pure host arithmetic; no HIP call.
  */
 int fa_paged_num_splits(int B, int Hq, int Hkv, int Nq, int d, int page_size,
                         int max_pages_per_seq);
@@ -323,8 +338,9 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
                  size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Variable-length decode over a padded contiguous cache.  Serving engines
- * keep the caches of a batch in one tensor padded to the longest sequence
+ * Variable-length decode (or query chunks) over a padded contiguous cache.
+ * Serving engines keep the caches of a batch in one tensor padded to the
+ * longest sequence
  * ("FlashAttention Analysis", ryotta.opik.net, closing section: the fused
  * kernels run inside paged and cached decoding; as for the paged cache,
  * each sequence attends to its own cache length).
@@ -335,14 +351,20 @@ int fa_fwd_paged(const void* q, const void* k_cache, const void* v_cache,
  * the device); the rows past them are never read.  Its Nq queries attend
  * to them as fa_fwd_window would (causal alignment at its own last key:
  * query i sits at c = i + seqlens_k[b] - Nq; window bounds -1 for none).  A
- * sequence with no keys gets O = 0 and lse = -inf.  The KV-split form runs
- * (partial + merge kernels) with chunks cut from the padded length; chunks
- * past a sequence's length weigh nothing.  num_splits = 0 takes
- * fa_default_num_splits(B, Hq, Hkv, Nq, Nk, d), otherwise 1 .. 4096;
- * `workspace` (16-byte aligned, device) holds at least
- * fa_splitkv_workspace_bytes(B, Hq, Nq, d, splits) bytes.  Errors as for
- * fa_fwd_splitkv; FA_ERR_INVALID_ARG also for a null or misaligned
- * seqlens_k and a bound below -1.
+ * sequence with no keys gets O = 0 and lse = -inf.  Two forms:
+ *   - num_splits = 0 and fa_default_num_splits(B, Hq, Hkv, Nq, Nk, d) = 0
+ *     (many query rows per KV head, or d = 96): the tiled prefill kernel
+ *     with each sequence's key count; `workspace` is not used (may be
+ *     NULL).
+ *   - otherwise the KV-split form (partial + merge kernels) with chunks
+ *     cut from the padded length (chunks past a sequence's length weigh
+ *     nothing): fa_default_num_splits(...) chunks for num_splits = 0,
+ *     else num_splits (1 .. 4096); `workspace` (16-byte aligned, device)
+ *     holds at least fa_splitkv_workspace_bytes(B, Hq, Nq, d, splits)
+ *     bytes.
+ * Errors as for fa_fwd_splitkv; FA_ERR_INVALID_ARG also for a null or
+ * misaligned seqlens_k and a bound below -1; FA_ERR_UNSUPPORTED for d = 96
+ * with num_splits > 0.
  */
 int fa_fwd_kvlen(const void* q, const void* k, const void* v, void* o,
                  float* lse, const int* seqlens_k, int B, int Hq, int Hkv,

@@ -344,7 +344,10 @@ def test_paged_invalid_arguments(lib, kw):
 
 
 def test_paged_unsupported_and_splits(lib):
+    # d = 96 runs only in the prefill form: not with 32-key pages, not with
+    # an explicit split count
     assert _paged(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    assert _paged(lib, d=96, ps=64, Nq=100, S=2) == _lib.FA_ERR_UNSUPPORTED
     assert _paged(lib, ps=1 << 16, mp=1 << 15) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
     # default split count: at least one chunk, none over 62 pages
@@ -352,6 +355,30 @@ def test_paged_unsupported_and_splits(lib):
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 32, 1) == 1
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 64, 48, 10) == 0
     assert lib.fa_paged_num_splits(1, 4, 2, 1, 96, 32, 10) == 0
+
+
+def test_paged_form_choice(lib):
+    """0 = the prefill form: many query rows per KV head (or d = 96) with
+    pages of at least 64 keys and at most 8192 pages per sequence."""
+    assert lib.fa_paged_num_splits(1, 4, 2, 100, 64, 64, 10) == 0
+    assert lib.fa_paged_num_splits(1, 4, 2, 100, 96, 64, 10) == 0
+    assert lib.fa_paged_num_splits(1, 4, 2, 100, 128, 256, 8192) == 0
+    # 32-key pages, too many pages, d = 256: the KV-split form
+    assert lib.fa_paged_num_splits(1, 4, 2, 100, 64, 32, 10) >= 1
+    assert lib.fa_paged_num_splits(1, 4, 2, 100, 64, 64, 8193) >= 1
+    assert lib.fa_paged_num_splits(1, 4, 2, 100, 256, 64, 10) >= 1
+    # few rows per KV head: the KV-split form
+    assert lib.fa_paged_num_splits(1, 4, 2, 32, 64, 64, 10) >= 1
+
+
+def test_paged_prefill_form_passes_validation(lib):
+    """The prefill form takes no workspace; these calls pass every check
+    and reach the device query (FA_ERR_HIP without a GPU)."""
+    assert _fresh(lambda: _paged(lib, Nq=100, ps=64, ws=None, wsb=0)) == \
+        _lib.FA_ERR_HIP
+    assert _fresh(lambda: _paged(lib, Nq=100, ps=64, d=96)) == _lib.FA_ERR_HIP
+    assert _fresh(lambda: _paged(lib, Nq=100, ps=64, d=32, causal=1, wl=50)) \
+        == _lib.FA_ERR_HIP
 
 
 def _kvlen(lib, **kw):
@@ -380,9 +407,20 @@ def test_kvlen_invalid_arguments(lib, kw):
 
 
 def test_kvlen_unsupported(lib):
-    assert _kvlen(lib, d=96) == _lib.FA_ERR_UNSUPPORTED
+    # d = 96 runs only in the prefill form (num_splits = 0)
+    assert _kvlen(lib, d=96, S=2) == _lib.FA_ERR_UNSUPPORTED
     assert _kvlen(lib, Nk=1 << 24, d=128) == _lib.FA_ERR_UNSUPPORTED
     assert lib.fa_last_hip_error() == 0
+
+
+def test_kvlen_prefill_form_passes_validation(lib):
+    """Many query rows per KV head (or d = 96) take the prefill form, with
+    no workspace: the calls reach the device query (FA_ERR_HIP here)."""
+    assert _fresh(lambda: _kvlen(lib, Nq=100, ws=None, wsb=0)) == \
+        _lib.FA_ERR_HIP
+    assert _fresh(lambda: _kvlen(lib, d=96)) == _lib.FA_ERR_HIP
+    # an explicit split count keeps the KV-split form and its workspace
+    assert _kvlen(lib, Nq=100, S=2, ws=None) == _lib.FA_ERR_INVALID_ARG
 
 
 def _colmask(lib, **kw):

@@ -160,15 +160,19 @@ MEASURED_TRAFFIC = {
 
 
 def kernel_source_hash(source):
-    """SHA-256 over a kernel source and the headers every kernel source
-    includes (names, lengths and contents)."""
+    """SHA-256 over a kernel source, the headers every kernel source
+    includes (names, lengths and contents) and the compiler flags the
+    library build gives that source."""
     import hashlib
+    from exact_io_aware_05_amd import build
     h = hashlib.sha256()
     for name in (source, "fa_device.h", "fa_internal.h"):
         path = os.path.join(ROOT, "exact_io_aware_05_amd", "csrc", name)
         with open(path, "rb") as f:
             data = f.read()
         h.update(name.encode() + b"\0" + len(data).to_bytes(8, "little") + data)
+    flags = build.hash_flags(build._flags()) + list(build.EXTRA.get(source, []))
+    h.update("\0".join(flags).encode())
     return h.hexdigest()
 
 

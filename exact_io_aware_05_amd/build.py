@@ -78,9 +78,16 @@ def source_hash() -> str:
         with open(path, "rb") as f:
             data = f.read()
         h.update(len(data).to_bytes(8, "little") + data)
-    flags = _flags() + [f"{k}:{' '.join(v)}" for k, v in sorted(EXTRA.items())]
+    flags = hash_flags(_flags()) + [f"{k}:{' '.join(v)}"
+                                    for k, v in sorted(EXTRA.items())]
     h.update("\0".join(flags).encode())
     return h.hexdigest()
+
+
+def hash_flags(flags):
+    """Compiler flags as they enter a hash: paths inside the repository made
+    relative to its root, so a copy of the tree elsewhere hashes the same."""
+    return [f.replace(ROOT + os.sep, "./") for f in flags]
 
 
 HASH_MARK = b"FA_SOURCE_HASH="

@@ -7,6 +7,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -579,6 +580,25 @@ def test_source_hash_covers_headers_and_flags(monkeypatch, tmp_path):
     assert build.source_hash() == base
     monkeypatch.setattr(build, "EXTRA", {**build.EXTRA, "fa_api.hip": ["-O1"]})
     assert build.source_hash() != base
+
+
+def test_source_hash_does_not_depend_on_the_tree_location(tmp_path):
+    """A copy of the sources at another path (as on a remote host) hashes
+    the same, so a library built here is not taken for stale there."""
+    import shutil
+    from exact_io_aware_05_amd import build
+    root = tmp_path / "elsewhere"
+    shutil.copytree(build.PKG, root / "exact_io_aware_05_amd",
+                    ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    shutil.copytree(build.INCLUDE, root / "include")
+    code = ("import sys; sys.path.insert(0, sys.argv[1]); "
+            "from exact_io_aware_05_amd import build; "
+            "print(build.ROOT); print(build.source_hash())")
+    out = subprocess.run([sys.executable, "-c", code, str(root)],
+                         capture_output=True, text=True, check=True)
+    where, digest = out.stdout.split()
+    assert os.path.realpath(where) == os.path.realpath(root)
+    assert digest == build.source_hash()
 
 
 def test_stale_library_is_refused_without_a_compiler(monkeypatch, tmp_path):

@@ -98,38 +98,42 @@ WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
 FETCH_SCALE = 1048576.0 / 524301.0
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
+    "gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256": {
+        "source": "fa_prefill.hip",
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 70931.1, "write_kib": 66619.8},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "c51b95d35374dd7c4c002ffd79fb3ed6f9ec0f4be612ebe221c74d34b565a8f6",
-        "fetch_kib": 71261.5, "write_kib": 66566.1},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 71176.6, "write_kib": 66560.3},
     "mha_b4_h16_n2048_d64": {
         "source": "fa_prefill.hip",
-        "sha256": "c51b95d35374dd7c4c002ffd79fb3ed6f9ec0f4be612ebe221c74d34b565a8f6",
-        "fetch_kib": 41047.5, "write_kib": 16896.0},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 41044.0, "write_kib": 16896.0},
     "causal_outlier_b2_h16_n4096_d128": {
         "source": "fa_prefill.hip",
-        "sha256": "c51b95d35374dd7c4c002ffd79fb3ed6f9ec0f4be612ebe221c74d34b565a8f6",
-        "fetch_kib": 76713.8, "write_kib": 33432.7},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 76887.0, "write_kib": 33421.9},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
-        "fetch_kib": 514061.6, "write_kib": 266356.0},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 514063.3, "write_kib": 266370.5},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
-        "fetch_kib": 67564.8, "write_kib": 66565.5},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 67543.4, "write_kib": 66560.2},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
-        "fetch_kib": 73478.6, "write_kib": 70657.9},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 72411.1, "write_kib": 68608.8},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "9beba94cd420caf21832825231c34ad5fc2b447c423b76bdd5cd379ed349768c",
-        "fetch_kib": 56167.0, "write_kib": 80295.4},
+        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
+        "fetch_kib": 56161.9, "write_kib": 80124.1},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
-        "sha256": "33d71c45690d58cf5b66d4391cc8ffa33d06f4507deed0898e04e71093e312ae",
-        "fetch_kib": 33947.1, "write_kib": 66561.8},
+        "sha256": "ecb89f434f521516e30ee16ad78c628307bc267c14e18d85f06bd3eb3d4959c8",
+        "fetch_kib": 33948.8, "write_kib": 66561.8},
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",

@@ -121,23 +121,87 @@ bool splitkv_too_large(int B, int Hq, int Hkv, int Nq, int splits) {
   return (long long)B * Hkv * rowtiles * splits > (1LL << 31) - 64;
 }
 
-// The prefill kernel (splits == 0) or the KV-split form with a workspace
-// taken from the stream-ordered pool for this call.
+constexpr int kMaxDevices = 64;
+
+// ---- workspace of the KV-split form inside fa_fwd and fa_fwd_window
+//
+// One buffer per (device, stream), kept for the later calls on that stream:
+// calls on one stream run in stream order, so each may reuse what the one
+// before it used, and a call that needs more frees the old buffer and takes
+// a larger one, both stream-ordered (hipFreeAsync / hipMallocAsync on the
+// stream).  Taking and returning memory on every call cost about 50 us of
+// host time per call on MI355X, more than the kernels of a short windowed
+// decode.  (A stream handle is reused only once the destroyed stream's work
+// has completed, so an entry never outlives the work that used it.)  Under
+// graph capture, and past kMaxCachedStreams entries, a call takes its
+// workspace with hipMallocAsync and returns it with hipFreeAsync, so that a
+// captured graph owns its memory.
+constexpr int kMaxCachedStreams = 32;
+struct StreamWorkspace {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+StreamWorkspace g_ws[kMaxCachedStreams];
+int g_ws_count = 0;
+
+// The KV-split form with its workspace as described above.
+int run_splitkv(const void* q, const void* k, const void* v, void* o,
+                float* lse, const fa::Shape& s, int splits, bool f32,
+                hipStream_t stream) {
+  const size_t bytes =
+      fa::splitkv_workspace_bytes((long long)s.B * s.Hq * s.Nq, s.d, splits);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(stream, &cap);
+  if (e != hipSuccess) return hip_status(e);
+  if (cap == hipStreamCaptureStatusNone) {
+    std::lock_guard<std::mutex> guard(g_ws_mu);
+    int i = 0;
+    while (i < g_ws_count && !(g_ws[i].dev == dev && g_ws[i].stream == stream))
+      ++i;
+    if (i < g_ws_count || g_ws_count < kMaxCachedStreams) {
+      if (i == g_ws_count) g_ws[g_ws_count++] = {dev, stream, nullptr, 0};
+      StreamWorkspace& w = g_ws[i];
+      if (w.bytes < bytes) {
+        if (w.ptr) {
+          e = hipFreeAsync(w.ptr, stream);
+          w.ptr = nullptr;
+          w.bytes = 0;
+          if (e != hipSuccess) return hip_status(e);
+        }
+        e = hipMallocAsync(&w.ptr, bytes, stream);
+        if (e != hipSuccess) {
+          w.ptr = nullptr;
+          return hip_status(e);
+        }
+        w.bytes = bytes;
+      }
+      return hip_status(
+          fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, w.ptr, stream));
+    }
+  }
+  void* ws = nullptr;
+  e = hipMallocAsync(&ws, bytes, stream);
+  if (e != hipSuccess) return hip_status(e);
+  e = fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
+  hipError_t e2 = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(e2);
+}
+
+// The prefill kernel (splits == 0) or the KV-split form.
 int run_forward(const void* q, const void* k, const void* v, void* o,
                 float* lse, const fa::Shape& s, int splits, bool f32,
                 hipStream_t stream) {
   if (splits == 0)
     return hip_status(fa::launch_prefill(q, k, v, o, lse, s,
                                          fa::dense_layout(s), f32, stream));
-  const size_t bytes =
-      fa::splitkv_workspace_bytes((long long)s.B * s.Hq * s.Nq, s.d, splits);
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, stream);
-  if (e != hipSuccess) return hip_status(e);
-  e = fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
-  hipError_t e2 = hipFreeAsync(ws, stream);
-  if (e != hipSuccess) return hip_status(e);
-  return hip_status(e2);
+  return run_splitkv(q, k, v, o, lse, s, splits, f32, stream);
 }
 
 // ---- scratch of the allocation-free entry point (fa_fwd_noalloc)
@@ -153,7 +217,6 @@ int run_forward(const void* q, const void* k, const void* v, void* o,
 constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
-constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 

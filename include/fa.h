@@ -102,10 +102,13 @@ enum { FA_OUT_BF16 = 0, FA_OUT_F32 = 1 };
  * fa_default_num_splits() chunks.  Both forms address one K or V head
  * with 32-bit byte offsets, so Nk * d * 2 must stay below 2^31
  * (FA_ERR_UNSUPPORTED otherwise; Nk < 8388608 at d = 128).  The KV-split
- * form needs a temporary fp32
- * workspace (fa_splitkv_workspace_bytes), which this call takes with
- * hipMallocAsync on `stream` and returns with hipFreeAsync on the same
- * stream.  `stream` may be NULL (the null stream).
+ * form needs an fp32 workspace (fa_splitkv_workspace_bytes).  The library
+ * keeps one per (device, stream) for the later calls on that stream (calls
+ * on one stream run in order), grown with hipFreeAsync / hipMallocAsync on
+ * the stream when a call needs more, and held until the process ends;
+ * under graph capture, or once 32 streams hold one, a call takes its own
+ * with hipMallocAsync and returns it with hipFreeAsync on `stream`.
+ * `stream` may be NULL (the null stream).
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal,

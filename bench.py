@@ -137,29 +137,29 @@ MEASURED_TRAFFIC = {
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
-        "fetch_kib": 1048879.2, "write_kib": 2112.0},
+        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "fetch_kib": 1048840.5, "write_kib": 2112.0},
     "decode_b16_hq32_hkv8_nq1_nk16384_d256": {
         "source": "fa_splitkv.hip",
-        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
-        "fetch_kib": 1050163.8, "write_kib": 6720.2},
+        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "fetch_kib": 1048963.0, "write_kib": 4160.6},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
-        "fetch_kib": 132424.4, "write_kib": 2112.1},
+        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "fetch_kib": 132366.0, "write_kib": 2112.1},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "e322e6a5e5a9a9580e4e60eb15872f9195b38b01dbc8916b06bfa8916f944b4a",
-        "fetch_kib": 1048925.9, "write_kib": 2112.1},
+        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "fetch_kib": 1048863.5, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "e8e76eb17411cfff27993283a50ad0121075c7027f6b089191acfe796ed920d0",
-        "fetch_kib": 576941.8, "write_kib": 100354.8},
+        "sha256": "537026a3e7ff89beebe0b6a3dde2ffe706d378b11343ecef38e8b0224e901f76",
+        "fetch_kib": 405222.7, "write_kib": 100352.0},
     "gqa_prefill_window_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "e8e76eb17411cfff27993283a50ad0121075c7027f6b089191acfe796ed920d0",
-        "fetch_kib": 298552.5, "write_kib": 100352.3},
+        "sha256": "537026a3e7ff89beebe0b6a3dde2ffe706d378b11343ecef38e8b0224e901f76",
+        "fetch_kib": 298726.3, "write_kib": 100352.2},
 }
 
 

@@ -19,8 +19,8 @@
 //   dK^T += Q^T dS.  The two waves of a key group share a SIMD, so one
 //   wave's vector work runs under the other's matrix products.  Tiles of 64
 //   query rows of every query head of the group stream through LDS
-//   (double-buffered), row steps from the last one down and the group's
-//   query heads inside a step.  Scores use v_mfma_f32_32x32x16_bf16 with lane = one
+//   (double-buffered), row steps from the last one down (without a band
+//   the group's query heads inside a step).  Scores use v_mfma_f32_32x32x16_bf16 with lane = one
 //   key and 16 query rows; the query rows are read in an order (bits 2 and
 //   3 of the row index swapped) that makes a lane's score registers 8
 //   consecutive rows, so P and dS serve as B operands as they are, and dO^T
@@ -320,10 +320,16 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
   // modulo the swizzle period for every m), lse2 by wave 0, D by wave 1
   static_assert((2 * Dma::NI) % 8 == 0, "copy split");
   const uint32_t loff = Dma::lane_off(wave);
-  // Row steps run from the last one down, the G query heads of a step
-  // next to each other, so that the workgroups of one KV head (which stop
-  // at different rows under the causal mask) sweep the same Q / dO tiles
-  // at about the same time and share them in L2.
+  // Row steps run from the last one down, so that the workgroups of one KV
+  // head sweep the same Q / dO tiles at about the same time and share them
+  // in L2.  Without a band they all start at the last row and stop at
+  // different rows (causal), so the G query heads of a step come next to
+  // each other and the sweeps stay in step across heads.  With a band each
+  // workgroup's rows are a window that starts 128 rows after the previous
+  // key block's, so the workgroups run staggered by design; there the
+  // heads come one after another, which keeps the rows read at one time to
+  // one head's (heads inside a step multiply them by G and overflow L2).
+  constexpr bool HEADS_INNER = !BAND;
   int pg = 0, pt = t_end - 1;  // query head and row step of the next copy
   auto copy_step = [&](char* dst) {
     const int64_t qh = (int64_t)(b * Hq + hkv * G + pg) * Nq;
@@ -339,9 +345,14 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
     float* st = reinterpret_cast<float*>(dst + 2 * QR * T::ROWP);
     if (wave == 0) Dma::issue_vec(st, lse2 + qh, Nq, r0);
     if (wave == 1) Dma::issue_vec(st + QR, dvec + qh, Nq, r0);
-    if (++pg == G) {
-      pg = 0;
-      --pt;
+    if (HEADS_INNER) {
+      if (++pg == G) {
+        pg = 0;
+        --pt;
+      }
+    } else if (--pt < t_begin) {
+      pt = t_end - 1;
+      ++pg;
     }
   };
   if (n_it > 0) copy_step(smem);
@@ -359,9 +370,13 @@ __global__ __launch_bounds__(NT2, 1) void bwd_dkdv_kernel(
     const float* ls = reinterpret_cast<const float*>(qt + 2 * QR * T::ROWP);
     const float* dd = ls + QR;
     const int q0 = ct_row * QR;
-    if (++ct_g == G) {
-      ct_g = 0;
-      --ct_row;
+    if (HEADS_INNER) {
+      if (++ct_g == G) {
+        ct_g = 0;
+        --ct_row;
+      }
+    } else if (--ct_row < t_begin) {
+      ct_row = t_end - 1;
     }
     if (it + 1 < n_it) copy_step(smem + (1 - PAR) * STAGE);
 

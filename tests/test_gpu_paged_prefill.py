@@ -179,3 +179,25 @@ def test_kvlen_prefill_full_lengths_equal_fa_fwd():
                         out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_paged_small_pages_many_rows_take_the_kvsplit_form():
+    """32-key pages cannot hold the prefill kernel's 64-key blocks, so a
+    chunk of many queries over them runs the KV-split form (many packed row
+    tiles per KV head); the result is the same attention."""
+    B, Hq, Hkv, Nq, d, P, maxp = 2, 8, 2, 300, 128, 32, 24
+    lens = [700, 301]
+    print("paged small pages, many rows", flush=True)
+    ops = _ops()
+    assert ops.paged_num_splits(B, Hq, Hkv, Nq, d, P, maxp) >= 1
+    q, kc, vc, table, sl = _poisoned_paged(B, Hq, Hkv, Nq, d, P, maxp, lens,
+                                           seed=65)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    o, lse = _nan_out(B, Hq, Nq, d, torch.float32)
+    ops.fa_fwd_paged(dev(q), dev(kc), dev(vc), _i32(table), _i32(sl),
+                     causal=True, scale=scale, out_dtype=torch.float32,
+                     o=o, lse=lse)
+    torch.cuda.synchronize()
+    O_ref, L_ref = paged_attention(f64(q), f64(kc), f64(vc), table, sl,
+                                   causal=True, scale=scale)
+    compare(host(o), host(lse), O_ref, L_ref, what="paged 32-key pages")

@@ -442,11 +442,21 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     // multiple of 8 G; the surplus workgroups exit here.
     const int s8 = blockIdx.x >> 3;
     g = s8 % G;
-    const int u = 8 * (s8 / G) + (blockIdx.x & 7);
     const int n_bh = lay.n_seq * Hkv;
-    if (u >= n_bh * n_qblk) return;
-    jq = u / n_bh;
-    bh = u % n_bh;
+    if ((Hkv & 7) == 0) {
+      // KV heads a multiple of 8: XCD x takes the KV heads x, x + 8, ... of
+      // every sequence (the same work on every XCD) and runs them one
+      // (sequence, KV head) after another, Q-block ranks heavy first, so
+      // that its concurrent workgroups share that head's K/V in its L2
+      const int p = s8 / G;
+      jq = p % n_qblk;
+      bh = 8 * (p / n_qblk) + (blockIdx.x & 7);
+    } else {
+      const int u = 8 * (s8 / G) + (blockIdx.x & 7);
+      if (u >= n_bh * n_qblk) return;
+      jq = u / n_bh;
+      bh = u % n_bh;
+    }
   } else if (((n_items / (n_qblk * G)) & 7) == 0) {
     // equal sequences, KV heads a multiple of 8: each XCD (which receives
     // every 8th workgroup in launch order) takes whole KV heads, so a KV

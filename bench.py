@@ -100,36 +100,36 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 70931.1, "write_kib": 66619.8},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 70915.5, "write_kib": 66634.7},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 71176.6, "write_kib": 66560.3},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 71188.5, "write_kib": 66560.3},
     "mha_b4_h16_n2048_d64": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 41044.0, "write_kib": 16896.0},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 41049.5, "write_kib": 16896.0},
     "causal_outlier_b2_h16_n4096_d128": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 76887.0, "write_kib": 33421.9},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 76556.0, "write_kib": 33392.0},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 514063.3, "write_kib": 266370.5},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 249653.8, "write_kib": 266267.0},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 67543.4, "write_kib": 66560.2},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 67576.3, "write_kib": 66561.3},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 72411.1, "write_kib": 68608.8},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 72393.0, "write_kib": 68609.7},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "00751fdbbc6067e8ea5cd6ef42023c5aa8607d78d451d3b83a6277a40130bffd",
-        "fetch_kib": 56161.9, "write_kib": 80124.1},
+        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
+        "fetch_kib": 56174.3, "write_kib": 80141.5},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
         "sha256": "ecb89f434f521516e30ee16ad78c628307bc267c14e18d85f06bd3eb3d4959c8",

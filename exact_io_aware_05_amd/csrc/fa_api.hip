@@ -27,9 +27,10 @@ bool aligned16(const void* p) {
 
 // Head dimensions an entry point takes, as bit sets.  The prefill kernel
 // runs d = 32 and 96 in its 64- and 128-column tiles (the columns past d
-// masked); the KV-split kernel has instances for 32, 64, 128 and 256;
-// fa_fwd and its variants take all five (d = 256 in the KV-split form,
-// d = 96 in the prefill kernel); the backward kernels 64 and 128.
+// masked) and d = 256 in a kernel of its own (dense layouts, optionally
+// with per-sequence key counts); the KV-split kernel has instances for 32,
+// 64, 128 and 256; fa_fwd and its variants take all five (d = 96 only in
+// the prefill form); the backward kernels 64 and 128.
 enum : unsigned { kD32 = 1, kD64 = 2, kD96 = 4, kD128 = 8, kD256 = 16 };
 constexpr unsigned kDimsPrefill = kD32 | kD64 | kD96 | kD128;
 constexpr unsigned kDimsAny = kDimsPrefill | kD256;
@@ -104,13 +105,12 @@ int default_splits(int B, int Hq, int Hkv, int Nq, int Nk) {
   return (int)s;
 }
 
-// The chunk count of fa_fwd's choice for this shape (0: the prefill kernel),
-// by head dimension: d = 96 has only the prefill kernel, d = 256 only the
-// KV-split form (one chunk at least).
+// The chunk count of fa_fwd's choice for this shape (0: the prefill kernel;
+// at d = 256 its own one-wave-per-SIMD kernel); d = 96 has only the prefill
+// kernel.
 int forward_splits(int B, int Hq, int Hkv, int Nq, int Nk, int d) {
   int s = default_splits(B, Hq, Hkv, Nq, Nk);
   if (d == 96) s = 0;
-  if (d == 256 && s == 0) s = 1;
   return s;
 }
 

@@ -95,7 +95,7 @@ struct Layout {
 // V swizzle: 8-byte chunk u of row r is stored at u ^ vswz(r).
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
-  return D == 128 ? 8 * (r & 3) : 8 * ((r >> 1) & 1);
+  return D >= 128 ? 8 * (r & 3) : 8 * ((r >> 1) & 1);
 }
 
 // One 1 KiB HBM -> LDS copy instruction (buffer_load_dwordx4 ... lds):
@@ -143,22 +143,22 @@ __device__ __forceinline__ void barrier() {
 // chunks of columns past d).
 // The copy instructions of one block whose row 0 is at `base`, of which
 // the first `rem` bytes may be read (0: a copy of zeros).
-template <int D>
+template <int D, int NWAVES = NW>
 __device__ __forceinline__ void copy_rows(char* dst, const char* base,
                                           int rem, int wave,
                                           uint32_t lane_off, int step,
                                           int zero_from) {
   using L = Layout<D>;
 #pragma unroll
-  for (int n = 0; n < L::NINS / NW; ++n) {
-    const int i = wave + NW * n;
+  for (int n = 0; n < L::NINS / NWAVES; ++n) {
+    const int i = wave + NWAVES * n;
     const int left = i < zero_from ? rem - step * i : 0;
     dma16(dst + 1024 * i, base + step * i, (uint32_t)(left > 0 ? left : 0),
           lane_off);
   }
 }
 
-template <int D>
+template <int D, int NWAVES = NW>
 __device__ __forceinline__ void copy_block(char* dst, const char* head,
                                            int Nk, int blk, int wave,
                                            uint32_t lane_off, int step,
@@ -170,7 +170,7 @@ __device__ __forceinline__ void copy_block(char* dst, const char* head,
   const int kb = min(max(blk, 0) * BC, Nk);
   const char* base = head + (int64_t)kb * rsb;
   const int rem = (blk >= 0 && kb < Nk) ? (Nk - kb - 1) * rsb + rowb : 0;
-  copy_rows<D>(dst, base, rem, wave, lane_off, step, zero_from);
+  copy_rows<D, NWAVES>(dst, base, rem, wave, lane_off, step, zero_from);
 }
 
 // The same for a block of a paged cache: `roff` is the byte offset of the
@@ -907,6 +907,227 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   }
 }
 
+
+// ---- d = 256: one wave per SIMD
+//
+// At d = 256 a wave's Q^T fragments (64 registers) and O^T accumulators
+// (128) leave no room for two waves per SIMD, so the ping-pong schedule
+// above does not fit.  This kernel runs one wave per SIMD (its 512 VGPRs
+// and AGPRs): a workgroup of 4 waves takes 128 query rows, 32 per wave,
+// with the same products, layouts, lazy reference max and epilogue.  Each
+// wave issues its matrix phase (P_{j-1} V_{j-1}, then S_j) and then the
+// softmax of block j.  The K/V ring has two stages of 64-key blocks (32 KiB
+// each for K and for V, 128 KiB of LDS): group j + 1 (K_{j+1}, V_j) is
+// issued at the top of iteration j into the stages that blocks j - 1 and
+// j - 2 used, which every wave finished reading before the barrier that
+// ended iteration j - 1, and it is waited for at the end of iteration j,
+// so one whole iteration hides its latency.
+constexpr int BR256 = 128;              // query rows per workgroup
+constexpr int NW256 = BR256 / 32;       // 4 waves
+
+template <int MODE, bool OUT_F32>
+__global__ __launch_bounds__(64 * NW256, 1) void prefill256_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, void* __restrict__ o,
+    float* __restrict__ lse, int Hq, int Hkv, int Nq, int Nk_max, float c2,
+    int n_qblk, int n_items, SeqLayout lay, int wl, int wr) {
+  constexpr int D = 256;
+  constexpr bool CAUSAL = MODE == kCausal;
+  constexpr bool BAND = MODE == kBand;
+  using L = Layout<D, 2>;
+  constexpr int NTILE = L::NTILE;
+  constexpr int NSTEP = L::NSTEP;
+  __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+
+  // ---- work item: (b, kv head, Q block, head in group); heavy blocks
+  // first, and the XCD mapping of prefill_kernel
+  const int G = Hq / Hkv;
+  int g, jq, bh;
+  if (((n_items / (n_qblk * G)) & 7) == 0) {
+    const int per = (n_items / (n_qblk * G)) >> 3;
+    const int x = blockIdx.x & 7, sx = blockIdx.x >> 3;
+    g = sx % G;
+    const int t1 = sx / G;
+    bh = x * per + t1 % per;
+    jq = t1 / per;
+  } else {
+    const int item = xcd_contiguous(blockIdx.x, n_items);
+    g = item % G;
+    const int t1 = item / G;
+    jq = t1 % n_qblk;
+    bh = t1 / n_qblk;
+  }
+  const int qblk = MODE != kNone ? (n_qblk - 1 - jq) : jq;
+  const int b = bh / Hkv, hkv = bh % Hkv;
+  const int hq = hkv * G + g;
+  const int q0 = qblk * BR256;
+  if (q0 >= Nq) return;
+  // (a sequence's own key count, clamped into the cache)
+  const int Nk = lay.seqlen_k ? min(max(lay.seqlen_k[b], 0), Nk_max) : Nk_max;
+  const int64_t qbase = b * lay.q_b + hq * lay.q_h;
+  const int64_t obase = b * lay.o_b + hq * lay.o_h;
+  const int64_t lbase = b * lay.l_b + hq * lay.l_h;
+  const int off = Nk - Nq;
+  const int rsb = (int)(2 * lay.k_r);
+  const int rsbv = (int)(2 * lay.v_r);
+  const char* kh = reinterpret_cast<const char*>(k + b * lay.k_b + hkv * lay.k_h);
+  const char* vh = reinterpret_cast<const char*>(v + b * lay.v_b + hkv * lay.v_h);
+
+  int kv_end = Nk;
+  if (CAUSAL) kv_end = min(Nk, q0 + BR256 + off);
+  int j0 = 0;
+  if (BAND) {
+    kv_end = min(Nk, min(q0 + BR256, Nq) + off + wr);
+    j0 = max(0, q0 + off - wl) / BC;
+  }
+  const int nblk = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  const int kv_rows = max(kv_end, 0);
+
+  const int wrow0 = q0 + wave * 32;
+  int w_mask = Nk / BC;
+  if (CAUSAL) w_mask = min(w_mask, max(0, wrow0 + off + 1) / BC);
+  int w_lo = 0;
+  if (BAND) {
+    w_mask = min(w_mask, max(0, wrow0 + off + wr + 1) / BC);
+    w_lo = (max(0, wrow0 + 31 + off - wl) + BC - 1) / BC;
+  }
+
+  // ---- per-lane DMA source offsets (K: chunk i of all 64 rows per
+  // instruction; V: two 512-byte rows per instruction, 16-byte chunks
+  // XOR-swizzled by the tile row; wave w issues instructions w, w + 4, ...,
+  // so bit 1 of the tile rows of its V instructions is bit 0 of w)
+  const uint32_t k_off = (uint32_t)(key_slot(lane) * rsb);
+  uint32_t v_off;
+  {
+    const int row = lane >> 5;                  // row within the KiB
+    const int p = lane & 31;                    // physical 16-byte chunk
+    const int trow = 2 * (wave & 1) + row;      // tile row modulo 4
+    v_off = (uint32_t)(row * rsbv) + ((p ^ (vswz<D>(trow) >> 1)) * 16);
+  }
+  const int v_step = 2 * rsbv;
+
+  const int qrow = wrow0 + col;
+  bf16x8 qf[NSTEP];
+  {
+    const bool ok = qrow < Nq;
+    const uint16_t* qp = q + qbase + (ok ? qrow : 0) * lay.q_r + 8 * h;
+#pragma unroll
+    for (int t = 0; t < NSTEP; ++t)
+      qf[t] = __builtin_bit_cast(bf16x8, ok ? ldg16(qp + 16 * t)
+                                            : u32x4{0u, 0u, 0u, 0u});
+  }
+
+  f32x16 acc[NTILE];
+#pragma unroll
+  for (int i = 0; i < NTILE; ++i) acc[i] = f32x16{};
+  RowState st{-INFINITY, 0.f, 0.f};
+
+  const int k_rd = 1024 * h + 16 * col;
+  const int lg = lane >> 4, lp = lane & 15;
+  int v_rd[NTILE];
+  {
+    const int vrow = 8 * (lg >> 1) + (lp >> 2);
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+      const int u = 8 * tt + 4 * (lg & 1) + (lp & 3);
+      v_rd[tt] = L::VBASE + vrow * L::ROWB + ((u ^ vswz<D>(vrow)) * 8);
+    }
+  }
+  const int lim0 = (CAUSAL ? min(Nk - 1, qrow + off)
+                    : BAND ? min(Nk - 1, qrow + off + wr)
+                           : Nk - 1) - 8 * h;
+  const int lo0 = BAND ? qrow + off - wl - 8 * h : 0;
+
+  f32x16 s0, s1;
+  u32x4 pk[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) pk[i] = u32x4{0u, 0u, 0u, 0u};
+  bool rescale = false;
+  float alpha = 1.f;
+
+  // group g: K_g into K stage g % 2, V_{g-1} into V stage (g + 1) % 2
+  // (V_{j0-1} is a copy of zeros: the all-zero "previous" P multiplies it)
+  auto group = [&](int gi) {
+    copy_block<D, NW256>(smem + (gi & 1) * L::KBYTES, kh, kv_rows, gi, wave,
+                         k_off, 16, rsb, 2 * D);
+    copy_block<D, NW256>(smem + L::VBASE + ((gi + 1) & 1) * L::VBYTES, vh,
+                         kv_rows, gi > j0 ? gi - 1 : -1, wave, v_off, v_step,
+                         rsbv, 2 * D);
+  };
+  group(j0);
+  wait_vmcnt<0>();
+  __syncthreads();
+
+  for (int j = j0; j < nblk; ++j) {
+    group(j + 1);
+    if (rescale) {
+#pragma unroll
+      for (int i = 0; i < NTILE; ++i) acc[i] *= alpha;
+    }
+    {
+      const char* vp[NTILE];
+#pragma unroll
+      for (int tt = 0; tt < NTILE; ++tt)
+        vp[tt] = smem + ((j + 1) & 1) * L::VBYTES + v_rd[tt];
+      const char* kp = smem + (j & 1) * L::KBYTES + k_rd;
+      matrix_phase<D, true, true>(kp, vp, qf, pk, acc, s0, s1);
+    }
+    if (j >= w_mask || (BAND && j < w_lo))
+      rescale = softmax_phase<true, BAND>(s0, s1, lim0 - j * BC,
+                                          lo0 - j * BC, c2, st, alpha, pk);
+    else
+      rescale = softmax_phase<false>(s0, s1, lim0 - j * BC, 0, c2, st, alpha,
+                                     pk);
+    wait_vmcnt<0>();
+    barrier();
+  }
+  if (nblk > j0) {  // P V of the last block
+    if (rescale) {
+#pragma unroll
+      for (int i = 0; i < NTILE; ++i) acc[i] *= alpha;
+    }
+    const char* vp[NTILE];
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt)
+      vp[tt] = smem + ((nblk + 1) & 1) * L::VBYTES + v_rd[tt];
+    matrix_phase<D, true, false>(smem, vp, qf, pk, acc, s0, s1);
+  }
+
+  // ---- epilogue: O = O / lb, lse = (m + log2 l) ln 2
+  const float lt = pair_sum(st.l);
+  const float lbt = pair_sum(st.lb);
+  const float inv = lbt > 0.f ? 1.f / lbt : 0.f;
+  const float lse_v =
+      lt > 0.f ? (st.m + __builtin_amdgcn_logf(lt)) * kLn2 : -INFINITY;
+  if (qrow < Nq) {
+    const int64_t orow = obase + qrow * lay.o_r;
+#pragma unroll
+    for (int tt = 0; tt < NTILE; ++tt) {
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const int c = 32 * tt + 8 * gg + 4 * h;
+        const float x0 = acc[tt][4 * gg + 0] * inv;
+        const float x1 = acc[tt][4 * gg + 1] * inv;
+        const float x2 = acc[tt][4 * gg + 2] * inv;
+        const float x3 = acc[tt][4 * gg + 3] * inv;
+        if (OUT_F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(o) + orow + c) =
+              f32x4{x0, x1, x2, x3};
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(o) + orow + c) =
+              u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      }
+    }
+    if (h == 0) lse[lbase + qrow * lay.l_r] = lse_v;
+  }
+}
+
 template <int D, int MODE, bool OUT_F32, bool SPARSE = false,
           bool COLUMN = false, bool PAGED = false>
 hipError_t launch(const void* q, const void* k, const void* v, void* o,
@@ -934,6 +1155,39 @@ hipError_t launch(const void* q, const void* k, const void* v, void* o,
                      s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr, bm,
                      cm, s.d);
   return hipGetLastError();
+}
+
+template <int MODE, bool OUT_F32>
+hipError_t launch256(const void* q, const void* k, const void* v, void* o,
+                     float* lse, const Shape& s, const SeqLayout& lay, int wl,
+                     int wr, hipStream_t stream) {
+  const int n_qblk = (s.Nq + BR256 - 1) / BR256;
+  const long long n_items = (long long)s.B * s.Hq * n_qblk;
+  const float c2 = fmaxf(s.scale * kLog2e, 1.17549435e-38f);
+  hipLaunchKernelGGL((prefill256_kernel<MODE, OUT_F32>), dim3((unsigned)n_items),
+                     dim3(64 * NW256), 0, stream,
+                     static_cast<const uint16_t*>(q),
+                     static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), o, lse, s.Hq, s.Hkv,
+                     s.Nq, s.Nk, c2, n_qblk, (int)n_items, lay, wl, wr);
+  return hipGetLastError();
+}
+
+// d = 256 (dense layout, optionally per-sequence key counts)
+hipError_t launch_prefill256(const void* q, const void* k, const void* v,
+                             void* o, float* lse, const Shape& s,
+                             const SeqLayout& lay, bool out_f32,
+                             hipStream_t stream) {
+  if (lay.cu_q || lay.page_table) return hipErrorInvalidValue;
+  const MaskBounds m = mask_bounds(s);
+  if (m.kind == 0)
+    return out_f32 ? launch256<kNone, true>(q, k, v, o, lse, s, lay, 0, 0, stream)
+                   : launch256<kNone, false>(q, k, v, o, lse, s, lay, 0, 0, stream);
+  if (m.kind == 1)
+    return out_f32 ? launch256<kCausal, true>(q, k, v, o, lse, s, lay, 0, 0, stream)
+                   : launch256<kCausal, false>(q, k, v, o, lse, s, lay, 0, 0, stream);
+  return out_f32 ? launch256<kBand, true>(q, k, v, o, lse, s, lay, m.wl, m.wr, stream)
+                 : launch256<kBand, false>(q, k, v, o, lse, s, lay, m.wl, m.wr, stream);
 }
 
 template <int D, int MODE, bool PAGED>
@@ -1024,7 +1278,10 @@ hipError_t launch_prefill(const void* q, const void* k, const void* v,
                           const SeqLayout& lay, bool out_f32,
                           hipStream_t stream) {
   // head dimension 96 runs in the 128-column tile and 32 in the 64-column
-  // one, the columns past d masked (Q and K read as zeros, O not stored)
+  // one, the columns past d masked (Q and K read as zeros, O not stored);
+  // 256 in its own kernel
+  if (s.d == 256)
+    return launch_prefill256(q, k, v, o, lse, s, lay, out_f32, stream);
   const bool paged = lay.page_table != nullptr;
   if (s.d == 128 || s.d == 96)
     return paged ? launch_d<128, true>(q, k, v, o, lse, s, lay, out_f32, stream)

@@ -47,8 +47,9 @@
  *     fa_bwd, fa_bwd_window                      64, 128
  *     fa_fwd_fp8                                 128
  *   32 and 96 run in the 64- and 128-column tiles of the prefill kernel
- *   with the columns past d masked; fa_fwd, fa_fwd_window, fa_fwd_paged
- *   and fa_fwd_kvlen take d = 96 only in the prefill kernel and d = 256
+ *   with the columns past d masked, 256 in a prefill kernel of its own (one
+ *   wave per SIMD); fa_fwd, fa_fwd_window, fa_fwd_paged and fa_fwd_kvlen
+ *   take d = 96 only in the prefill form, and fa_fwd_paged takes d = 256
  *   only in the KV-split form.
  * - Every call is asynchronous: it validates its arguments on the host,
  *   enqueues kernels on `stream` and returns.  Results are valid once the

@@ -113,13 +113,14 @@ def test_fwd_head_dims_pass_validation(lib, d):
 
 
 def test_fwd_form_by_head_dim(lib):
-    """fa_fwd's form: d = 96 always runs the prefill kernel (0 chunks),
-    d = 256 always the KV-split form (at least one chunk)."""
+    """fa_fwd's form: d = 96 always runs the prefill kernel (0 chunks); d =
+    256 takes the prefill form (its own kernel) for many query rows per KV
+    head and the KV-split form for few, like d = 64 and 128."""
     assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 128) == 0
     assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 128) > 1
     assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 96) == 0
     assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 96) == 0
-    assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 256) == 1
+    assert lib.fa_default_num_splits(1, 32, 8, 8192, 8192, 256) == 0
     assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 256) > 1
     assert lib.fa_default_num_splits(1, 32, 8, 1, 8192, 100) == 0
 

@@ -2,7 +2,8 @@
 
 32 and 96 run in the prefill kernel's 64- and 128-column tiles with the
 columns past d masked (Q and K read as zeros, O not stored); 256 runs in
-the KV-split form at every size.  Small and ragged shapes element by
+its own one-wave-per-SIMD prefill kernel when a KV head has many query rows
+and in the KV-split form otherwise.  Small and ragged shapes element by
 element (both output types, the bf16 one the round-to-nearest-even of the
 fp32 one), a GQA prefill of a few thousand rows on every row, outputs
 pre-filled with NaN, and strided rows whose padding past d must stay
@@ -62,6 +63,47 @@ def test_fa_fwd_head_dims_match_oracle(shape, d):
     O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=causal,
                                        scale=scale)
     compare(host(o32), host(l32), O_ref, L_ref, what=f"d{d} {shape}")
+
+
+# B, Hq, Hkv, N, causal, window: the d = 256 prefill kernel on several
+# 128-row query blocks with ragged tails, every row
+D256_PREFILL = [
+    (1, 8, 4, 2048, True, None),
+    (2, 4, 2, 1000, False, None),
+    (1, 8, 8, 1500, True, (300, -1)),
+    (1, 4, 1, 777, False, (100, 50)),
+]
+
+
+@pytest.mark.parametrize("case", D256_PREFILL,
+                         ids=lambda c: "x".join(map(str, c[:5])) + f"-w{c[5]}")
+def test_d256_prefill_kernel_every_row(case):
+    B, Hq, Hkv, N, causal, window = case
+    print(f"d256 prefill {case}", flush=True)
+    ops = _ops()
+    assert ops.default_num_splits(B, Hq, Hkv, N, N, 256) == 0
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, 256, seed=93)
+    Q, K, V = dev(q), dev(k), dev(v)
+    scale = _scale(256)
+    outs = []
+    for dt in (torch.float32, torch.bfloat16):
+        o = torch.full((B, Hq, N, 256), float("nan"), dtype=dt, device="cuda")
+        lse = torch.full((B, Hq, N), float("nan"), device="cuda")
+        if window is None:
+            ops.fa_fwd(Q, K, V, causal=causal, scale=scale, out_dtype=dt,
+                       o=o, lse=lse)
+        else:
+            ops.fa_fwd_window(Q, K, V, window, causal=causal, scale=scale,
+                              out_dtype=dt, o=o, lse=lse)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    (o32, l32), (o16, l16) = outs
+    assert torch.equal(o32.to(torch.bfloat16), o16), "bf16 O != RNE(fp32 O)"
+    assert torch.equal(l32, l16)
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=causal,
+                                       scale=scale, window=window)
+    eo, el = compare(host(o32), host(l32), O_ref, L_ref, what=f"d256 {case}")
+    print(f"  max |dO| {eo:.2e}  max |dlse| {el:.2e}", flush=True)
 
 
 @pytest.mark.parametrize("causal", [False, True])

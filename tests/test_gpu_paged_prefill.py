@@ -135,6 +135,7 @@ KVLEN_CASES = [
     (2, 4, 4, 300, 640, 64, [640, 257], False, (-1, -1)),
     (2, 8, 2, 400, 512, 96, [512, 300], True, (-1, -1)),
     (2, 8, 8, 260, 700, 32, [700, 65], False, (128, 64)),
+    (2, 8, 4, 300, 700, 256, [700, 333], True, (-1, -1)),
 ]
 
 

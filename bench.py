@@ -33,7 +33,9 @@ with E4M3 inputs and reports TFLOP/s against the FP8 matrix-core peak.
 prefill with a seeded block mask (a quarter of the 128 x 64 blocks plus the
 diagonal), priced at the visible pairs of the kept blocks.
 ``--workload decode_d256`` runs the decode with head dimension 256 over
-16384 keys (the same K/V bytes as the decode workload).
+16384 keys (the same K/V bytes as the decode workload), and
+``--workload gqa_prefill_d256`` the GQA prefill with head dimension 256 over
+16 query heads and 8 KV heads (the same FLOPs).
 ``--workload gqa_prefill_docmask`` runs ``fa_fwd_colmask`` on the GQA
 prefill's shape with the 8192 tokens split into causal documents of seeded
 lengths in [300, 2500] (a column-interval mask), priced at the exact visible
@@ -78,11 +80,16 @@ WORKLOADS = {"gqa_prefill": 3, "decode": 4, "mha_d64": 1, "causal_outlier": 2,
              "gqa_prefill_window_bwd": 3, "decode_paged": None,
              "gqa_prefill_fp8": None, "gqa_prefill_sparse": None,
              "gqa_prefill_docmask": None, "decode_d256": 4,
-             "gqa_prefill_paged": None}
+             "gqa_prefill_paged": None, "gqa_prefill_d256": 3}
 # workloads that change one configuration's shape: head dimension 256 on
 # the decode (half the keys, so the same K/V bytes)
 VARIANTS = {"decode_d256": dict(name="decode_b16_hq32_hkv8_nq1_nk16384_d256",
-                                Nk=16384, d=256, scale=0.0625)}
+                                Nk=16384, d=256, scale=0.0625),
+            # head dimension 256 on the GQA prefill: the same total head
+            # width (16 query heads over 8 KV heads), the same FLOPs
+            "gqa_prefill_d256": dict(
+                name="gqa_prefill_b1_hq16_hkv8_n8192_d256_causal", Hq=16,
+                Hkv=8, d=256, scale=0.0625)}
 # sliding-window workloads: (left, right) bounds, run through fa_fwd_window
 # (and fa_bwd_window)
 WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
@@ -98,38 +105,42 @@ WINDOWS = {"gqa_prefill_window": (4096, -1), "decode_window": (4096, -1),
 FETCH_SCALE = 1048576.0 / 524301.0
 WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
+    "gqa_prefill_b1_hq16_hkv8_n8192_d256_causal": {
+        "source": "fa_prefill.hip",
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 113890.7, "write_kib": 66058.5},
     "gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 70915.5, "write_kib": 66634.7},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 70924.1, "write_kib": 66636.1},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 71188.5, "write_kib": 66560.3},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 71189.6, "write_kib": 66560.8},
     "mha_b4_h16_n2048_d64": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 41049.5, "write_kib": 16896.0},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 41044.5, "write_kib": 16896.0},
     "causal_outlier_b2_h16_n4096_d128": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 76556.0, "write_kib": 33392.0},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 76707.6, "write_kib": 33408.3},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 249653.8, "write_kib": 266267.0},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 249693.0, "write_kib": 266266.8},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 67576.3, "write_kib": 66561.3},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 67581.2, "write_kib": 66561.2},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 72393.0, "write_kib": 68609.7},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 72438.4, "write_kib": 68608.6},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "6b6d7726aa764c2e485a86af50f77bfa474212e60ac9e637498cb7d9fa361546",
-        "fetch_kib": 56174.3, "write_kib": 80141.5},
+        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
+        "fetch_kib": 56159.9, "write_kib": 80144.8},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
         "sha256": "ecb89f434f521516e30ee16ad78c628307bc267c14e18d85f06bd3eb3d4959c8",

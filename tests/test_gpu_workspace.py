@@ -52,3 +52,33 @@ def test_fa_fwd_workspace_per_stream():
             o, lse = outs[si][i]
             assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), \
                 (shp, si)
+
+
+def test_fa_fwd_kvsplit_under_graph_capture():
+    """Under stream capture the KV-split form takes its workspace with
+    hipMallocAsync / hipFreeAsync on the stream (memory the graph owns), not
+    the per-stream buffer.  Replays, with eager calls of another size on the
+    same stream between them, match the eager result bit for bit."""
+    ops = _ops()
+    B, Hq, Hkv, Nq, Nk, d = 2, 8, 2, 1, 4096, 128
+    q, k, v = (dev(x) for x in make_qkv(B, Hq, Hkv, Nq, Nk, d, seed=97))
+    q2, k2, v2 = (dev(x) for x in make_qkv(1, 16, 4, 1, 9000, 128, seed=98))
+    o_ref, l_ref = ops.fa_fwd(q, k, v, out_dtype=torch.float32)
+    o = torch.empty_like(o_ref)
+    lse = torch.empty_like(l_ref)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ops.fa_fwd(q, k, v, out_dtype=torch.float32, o=o, lse=lse)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref) and torch.equal(lse, l_ref), rep
+        with torch.cuda.stream(s):
+            ops.fa_fwd(q2, k2, v2, out_dtype=torch.float32)
+        torch.cuda.synchronize()

@@ -680,7 +680,7 @@ int fa_fwd_colmask(const void* q, const void* k, const void* v, void* o,
   if (!col_bounds || (reinterpret_cast<uintptr_t>(col_bounds) & 7u))
     return FA_ERR_INVALID_ARG;
   const int nkb = (Nk + fa::kPrefillKeys - 1) / fa::kPrefillKeys;
-  if (nkb > fa::kSparseMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
+  if (nkb > fa::kColMaxKeyBlocks) return FA_ERR_UNSUPPORTED;
   if ((long long)Nk * d * 2 > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;
   const long long qblk = ((long long)Nq + fa::kPrefillRows - 1) / fa::kPrefillRows;
   if ((long long)B * Hq * qblk > (1LL << 31) - 1) return FA_ERR_UNSUPPORTED;

@@ -140,7 +140,10 @@ struct BlockMask {
 // seen by the query rows bounds[2 (b mb + j)] .. bounds[2 (b mb + j) + 1]
 // - 1 (int32 pairs, shared by the sequence's heads), on top of the causal
 // flag.  The workgroup lists the key blocks that any of its rows may see
-// (at most kSparseMaxKeyBlocks) in the same LDS list as a block mask.
+// (at most kColMaxKeyBlocks) in an LDS list like a block mask's; the LDS
+// that the list gives up holds a ring of each listed block's bounds and
+// per-wave visibility masks.
+constexpr int kColMaxKeyBlocks = 6655;
 struct ColMask {
   const int* bounds;
   long long mb;  // pairs between sequences

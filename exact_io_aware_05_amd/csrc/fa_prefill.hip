@@ -130,6 +130,19 @@ __device__ __forceinline__ void barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// This lane's index, computed where it is used: the compiler can neither
+// hoist nor merge it, so a loop does not keep it (or values derived from
+// it) in a register across its busiest part, where a kept value would be
+// spilled.
+__device__ __forceinline__ int lane_now() {
+  int l;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 %0, -1, %0"
+      : "=v"(l));
+  return l;
+}
+
 // Starts the HBM -> LDS copy of block `blk` (64 rows) of one K or V head
 // (`head`: its row 0; rows `rsb` bytes apart) into the LDS buffer at `dst`,
 // shared by the NW waves: wave w issues 1 KiB buffer_load ... lds
@@ -292,26 +305,47 @@ __device__ __forceinline__ void matrix_phase(const char* kp,
 // The rounded weights feed P V and their own row sum lb, so O = acc / lb
 // is an exact convex combination of V rows up to fp32 summation; the fp32
 // sum l of the unrounded weights gives lse.
-// With COL, a column-interval mask as well: bit i of `cbits` hides this
-// lane's key of score register i (i < 16: s0, else s1 register i - 16).
+// With COL, a column-interval mask as well: `cm` (LDS) holds one word per
+// key of the block from this lane's first key on (key 8h of the block),
+// whose bit `crow` (this lane's row within its wave) says whether the row
+// may see the key.
 template <bool MASK, bool LOWER = false, bool COL = false>
 __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
                                               const f32x16& s1, int lim,
                                               int lo, float c2, RowState& st,
                                               float& alpha, u32x4* pk,
-                                              uint32_t cbits = 0) {
+                                              const uint32_t* cm = nullptr,
+                                              int crow = 0) {
   // The mask never overwrites the score registers (that would make the
   // masked and unmasked variants rejoin with copies): hidden keys are left
   // out of the max and get weight 0 after the exponential.
   auto hidden = [&](int key) {
     return MASK && (key > lim || (LOWER && key < lo));
   };
-  auto hide0 = [&](int r) {
-    return hidden(16 * (r >> 3) + (r & 7)) | (COL && ((cbits >> r) & 1u));
+  auto hide0 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7)); };
+  auto hide1 = [&](int r) { return hidden(16 * (r >> 3) + (r & 7) + 32); };
+  // column mask words of the keys of score registers r of s0 (keys 0..7
+  // and 16..23 from cm) and of s1 (32 further on), and the lane's bit of
+  // one of them as 0 or all ones
+  uint32_t cw0[16], cw1[16];
+  if (COL) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int kq = 16 * (q >> 1) + 4 * (q & 1);
+      const u32x4 a = *reinterpret_cast<const u32x4*>(cm + kq);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(cm + 32 + kq);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        cw0[4 * q + e] = a[e];
+        cw1[4 * q + e] = b[e];
+      }
+    }
+  }
+  auto vis = [&](uint32_t w) {
+    return (uint32_t)__builtin_amdgcn_sbfe((int)w, (unsigned)crow, 1u);
   };
-  auto hide1 = [&](int r) {
-    return hidden(16 * (r >> 3) + (r & 7) + 32) |
-           (COL && ((cbits >> (16 + r)) & 1u));
+  auto keep = [&](float e, uint32_t w) {
+    return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, e) & vis(w));
   };
   // weights p = 2^(s c2 - msub) (0 for hidden keys), rounded to bf16 once
   // into pk; partial sums of the fp32 and of the rounded weights
@@ -331,6 +365,12 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
       if (hide0(r + 1)) e1 = 0.f;
       if (hide1(r)) e2 = 0.f;
       if (hide1(r + 1)) e3 = 0.f;
+      if (COL) {
+        e0 = keep(e0, cw0[r]);
+        e1 = keep(e1, cw0[r + 1]);
+        e2 = keep(e2, cw1[r]);
+        e3 = keep(e3, cw1[r + 1]);
+      }
       rs[0] += e0;
       rs[1] += e1;
       rs[2] += e2;
@@ -368,9 +408,12 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
   // rescaled, and the weights are recomputed.
   float mq[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-  for (int r = 0; r < 16; ++r)
-    mq[r & 3] = fmaxf(fmaxf(mq[r & 3], hide0(r) ? -INFINITY : s0[r]),
-                      hide1(r) ? -INFINITY : s1[r]);
+  for (int r = 0; r < 16; ++r) {
+    const bool h0 = hide0(r) || (COL && vis(cw0[r]) == 0u);
+    const bool h1 = hide1(r) || (COL && vis(cw1[r]) == 0u);
+    mq[r & 3] = fmaxf(fmaxf(mq[r & 3], h0 ? -INFINITY : s0[r]),
+                      h1 ? -INFINITY : s1[r]);
+  }
   float mx = fmaxf(fmaxf(mq[0], mq[1]), fmaxf(mq[2], mq[3]));
   mx = pair_max(mx) * c2;
   const float m_new = fmaxf(st.m, mx);
@@ -416,9 +459,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // 0..23 the block, bit 24 / 25 set when the rows of group A / B use it),
   // then their count
   // paged cache: the page numbers of the pages this workgroup reads
-  __shared__ int blist[LISTED  ? kSparseMaxKeyBlocks + 1
+  // column mask: the same list (bits 0..15 the block, bit 16 + w set when
+  // wave w must test its rows key by key, bit 24 + w when some row of wave
+  // w may see some key), a ring stage per K stage holding the listed
+  // block's 64 bound pairs, and one visibility word per key and wave
+  constexpr int LMAX = COLUMN ? kColMaxKeyBlocks : kSparseMaxKeyBlocks;
+  __shared__ int blist[LISTED  ? LMAX + 1
                        : PAGED ? kPagedPrefillMaxPages
                                : 1];
+  __shared__ __attribute__((aligned(16))) int cbnd[COLUMN ? NSTG * 2 * BC : 1];
+  __shared__ __attribute__((aligned(16))) uint32_t cmk[COLUMN ? NW * BC : 1];
   constexpr int NTILE = L::NTILE;
   constexpr int NSTEP = L::NSTEP;
   __shared__ __attribute__((aligned(1024))) char smem[L::TOTAL];
@@ -561,17 +611,17 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
         if (ua || ub) blist[pos] = i | (ua ? 1 << 24 : 0) | (ub ? 1 << 25 : 0);
         cnt += (int)__builtin_popcountll(bal);
       }
-      if (lane == 0) blist[kSparseMaxKeyBlocks] = cnt;
+      if (lane == 0) blist[LMAX] = cnt;
     }
     __syncthreads();
-    n_act = __builtin_amdgcn_readfirstlane(blist[kSparseMaxKeyBlocks]);
+    n_act = __builtin_amdgcn_readfirstlane(blist[LMAX]);
   }
   // ---- column mask: every wave classifies the key blocks wave, wave + NW,
   // ... below nblk (lane = key of the block) into blist[block]: bits 0..15
-  // the block, bit 16 + w set when some key of the block is hidden from
-  // some row of wave w (that wave then tests every key), bits 24 / 25 when
-  // some row of half A / B may see some key.  Wave 0 then drops the blocks
-  // neither half sees, in place and in order.
+  // the block, bit 16 + w set when the interval of some key hides it from
+  // some row of wave w that would otherwise see it (that wave then tests
+  // every key), bit 24 + w when some row of wave w may see some key.  Wave
+  // 0 then drops the blocks no wave sees, in place and in order.
   if (COLUMN) {
     const int* cb = cmask.bounds + 2 * ((int64_t)b * cmask.mb);
     constexpr int UNR = 4;
@@ -601,19 +651,20 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
         uint32_t bits = 0;
 #pragma unroll
         for (int w = 0; w < NW; ++w) {
-          const int r0 = q0 + 32 * w, r1 = min(r0 + 32, Nq);
+          const int w0 = q0 + 32 * w, r1 = min(w0 + 32, Nq);
+          // the rows of wave w whose view of the key the interval decides:
+          // all of them, or under the causal mask those from the first row
+          // that sees the key (the causal limit hides it from the others)
+          const int r0 = CAUSAL ? max(w0, key - off) : w0;
           const bool all_vis =
               r0 >= r1 || !valid || (blo[u] <= r0 && bhi[u] >= r1);
           if (__builtin_amdgcn_ballot_w64(all_vis) != ~0ull)
             bits |= 1u << (16 + w);
+          // some row of the wave may see the key
+          if (__builtin_amdgcn_ballot_w64(valid &&
+                                          max(vlo, w0) < min(vhi, r1)) != 0)
+            bits |= 1u << (24 + w);
         }
-        const int ha1 = min(q0 + BR / 2, Nq), hb1 = min(q0 + BR, Nq);
-        if (__builtin_amdgcn_ballot_w64(valid && vlo < ha1 && vhi > q0 &&
-                                        vlo < vhi) != 0)
-          bits |= 1u << 24;
-        if (__builtin_amdgcn_ballot_w64(valid && vlo < hb1 &&
-                                        vhi > q0 + BR / 2 && vlo < vhi) != 0)
-          bits |= 1u << 25;
         if (lane == 0) blist[kb] = kb | (int)bits;
       }
     }
@@ -623,7 +674,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       for (int base = 0; base < nblk; base += 64) {
         const int i = base + lane;
         const int e = i < nblk ? blist[i] : 0;
-        const bool kept = ((e >> 24) & 3) != 0;
+        const bool kept = ((e >> 24) & 0xFF) != 0;
         const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
         const int pos =
             cnt + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
@@ -632,10 +683,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
         if (kept) blist[pos] = e;
         cnt += (int)__builtin_popcountll(bal);
       }
-      if (lane == 0) blist[kSparseMaxKeyBlocks] = cnt;
+      if (lane == 0) blist[LMAX] = cnt;
     }
     __syncthreads();
-    n_act = __builtin_amdgcn_readfirstlane(blist[kSparseMaxKeyBlocks]);
+    n_act = __builtin_amdgcn_readfirstlane(blist[LMAX]);
   }
   // key block at ring position p: p itself, or the p-th listed block (past
   // the list: a block past Nk, whose copies are zeros)
@@ -755,7 +806,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // for those of iteration j - (NS - 3); the first reader of K_{j+NS-1} /
   // V_{j+NS-2}, group A's matrix phase of iteration j + NS - 1, comes after
   // both waits and a barrier.
-  constexpr int OPS = 2 * (L::NINS / NW);  // copy instructions per wave
+  // copy instructions per wave and block (column mask: one more, for the
+  // block's bounds)
+  constexpr int OPS = 2 * (L::NINS / NW) + (COLUMN ? 1 : 0);
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
   // (V_{j0-1}, before the first block, is a copy of zeros: block j0's
   // matrix phase multiplies it by the all-zero "previous" P, and 0 *
@@ -784,6 +837,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
           rsbv, 2 * dq);
       prev_ro = ro;
     } else {
+      if constexpr (COLUMN) {
+        // bounds of the keys of the block at position g into stage g % NS:
+        // wave w copies keys 8w .. 8w + 7 (64 bytes, four lanes); keys past
+        // Nk read as zeros (an empty interval)
+        const int kk = min(blk_at(g) * BC + 8 * wave, Nk);
+        const char* src = reinterpret_cast<const char*>(
+            cmask.bounds + 2 * ((int64_t)b * cmask.mb + kk));
+        const int ln = lane_now();
+        if (ln < 4)
+          dma16(reinterpret_cast<char*>(cbnd) + (g % L::NS) * 8 * BC +
+                    64 * wave,
+                src, (uint32_t)min(Nk - kk, 8) * 8u, 16 * ln);
+      }
       copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, blk_at(g),
                     wave, k_off, 16, rsb, 2 * dq, dq / 8);
       copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
@@ -821,41 +887,32 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     if (LISTED) {
       const int e = __builtin_amdgcn_readfirstlane(blist[j]);
       jb = e & BLKBITS;
-      keep = (e >> (group_a ? 24 : 25)) & 1;
-      if (COLUMN) colm = keep && ((e >> (16 + wave)) & 1);
-    }
-    // the row bounds of the block's keys, one per lane, loaded before the
-    // matrix phase (keys past Nk are hidden by the limit anyway)
-    int clo = 0, chi = 0;
-    if (COLUMN && colm) {
-      const int key = jb * BC + lane;
-      if (key < Nk) {
-        const int2 x = *reinterpret_cast<const int2*>(
-            cmask.bounds + 2 * ((int64_t)b * cmask.mb + key));
-        clo = x.x;
-        chi = x.y;
+      keep = (e >> (group_a ? 24 : 25)) & 1;  // block mask: per half
+      if (COLUMN) {
+        keep = (e >> (24 + wave)) & 1;
+        colm = keep && ((e >> (16 + wave)) & 1);
       }
     }
     mphase(j, std::true_type{}, keep_prev, keep);
     barrier();
     copies(j);
     if (LISTED && !keep)
-      rescale = false;  // nothing of this block enters this half's rows
+      rescale = false;  // nothing of this block enters this wave's rows
     else if (COLUMN && colm) {
-      // this lane's 32 keys against its row: key 16 (i / 8 % 2) + i % 8
-      // + 8 h (+ 32 for i >= 16) of the block, its bounds fetched from the
-      // lane that loaded them
-      uint32_t cbits = 0;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const int r = i & 15;
-        const int key = 16 * (r >> 3) + (r & 7) + 8 * h + 32 * (i >> 4);
-        const int klo = __builtin_amdgcn_ds_bpermute(4 * key, clo);
-        const int khi = __builtin_amdgcn_ds_bpermute(4 * key, chi);
-        cbits |= (uint32_t)((qrow < klo) | (qrow >= khi)) << i;
-      }
+      // each key's visibility to the 32 rows of this wave as a bit mask
+      // (lane = key of the block), from its interval clamped to the rows
+      const int ln = lane_now();
+      const int2 x = *reinterpret_cast<const int2*>(
+          cbnd + (j % L::NS) * 2 * BC + 2 * ln);
+      const int ra = min(max(x.x, wrow0), wrow0 + 32) - wrow0;
+      const int rb = min(max(x.y, wrow0), wrow0 + 32) - wrow0;
+      const uint32_t m = rb <= ra        ? 0u
+                         : rb - ra >= 32 ? ~0u
+                                         : ((1u << (rb - ra)) - 1u) << ra;
+      cmk[wave * BC + ln] = m;
       rescale = softmax_phase<true, false, true>(s0, s1, lim0 - jb * BC, 0,
-                                                 c2, st, alpha, pk, cbits);
+                                                 c2, st, alpha, pk,
+                                                 cmk + wave * BC + 8 * h, col);
     }
     else if (jb >= w_mask || (BAND && jb < w_lo))
       rescale = softmax_phase<true, BAND>(s0, s1, lim0 - jb * BC,

@@ -258,7 +258,7 @@ int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
  * of its rows.  Bounds are read on the device and used as given (rows
  * outside [0, Nq) simply match no row).  Errors as for fa_fwd;
  * FA_ERR_INVALID_ARG also for a null or not 8-byte aligned col_bounds;
- * FA_ERR_UNSUPPORTED when Nk exceeds 8191 blocks of 64 keys.
+ * FA_ERR_UNSUPPORTED when Nk exceeds 6655 blocks of 64 keys (425,920 keys).
  */
 int fa_fwd_colmask(const void* q, const void* k, const void* v, void* o,
                    float* lse, const int* col_bounds, int B, int Hq, int Hkv,

@@ -451,6 +451,9 @@ def test_colmask_unsupported(lib):
     assert _colmask(lib, d=256) == _lib.FA_ERR_UNSUPPORTED
     assert _fresh(lambda: _colmask(lib, d=96)) == _lib.FA_ERR_HIP
     assert _colmask(lib, Nk=64 * 8192) == _lib.FA_ERR_UNSUPPORTED
+    assert _colmask(lib, Nk=64 * 6655 + 1) == _lib.FA_ERR_UNSUPPORTED
+    # the largest key count passes validation (no device here)
+    assert _fresh(lambda: _colmask(lib, Nk=64 * 6655)) == _lib.FA_ERR_HIP
     assert lib.fa_last_hip_error() == 0
 
 

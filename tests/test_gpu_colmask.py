@@ -1,8 +1,9 @@
 """Forward with a column-interval mask (fa_fwd_colmask) against the float64
 oracle: document masks (causal and bidirectional inside documents), a
-prefix-LM mask, random intervals (some empty), Nq != Nk and ragged sizes,
-GQA, d = 64 and 128; sampled rows of a long packed-document sequence; and,
-with every key visible to every row, bit-for-bit agreement with fa_fwd."""
+prefix-LM mask, random intervals (some empty), bounds outside [0, Nq) and
+reversed intervals, Nq != Nk and ragged sizes, GQA, d = 32 to 128, a zero
+scale; sampled rows of a long packed-document sequence; and, with every key
+visible to every row, bit-for-bit agreement with fa_fwd."""
 import numpy as np
 import pytest
 
@@ -32,6 +33,10 @@ def _bounds(kind, B, Nq, Nk, seed):
                                               causal_docs=False))
         elif kind == "prefix":
             out.append(prefix_lm_column_bounds(Nk, 100 + 37 * b))
+        elif kind == "wild":
+            # bounds outside [0, Nq) and reversed (empty) intervals
+            rng = np.random.default_rng(seed + b)
+            out.append(rng.integers(-300, Nq + 300, size=(Nk, 2)))
         else:
             out.append(random_column_bounds(Nq, Nk, seed=seed + b))
     return np.ascontiguousarray(np.stack(out), dtype=np.int32)
@@ -47,6 +52,9 @@ CASES = [
     (1, 4, 2, 257, 257, 128, True, "docs_bidir"),
     (1, 4, 2, 600, 600, 96, True, "docs_causal"),
     (1, 4, 4, 500, 777, 32, False, "random"),
+    (1, 4, 2, 300, 900, 128, True, "random"),
+    (1, 4, 2, 513, 513, 64, True, "wild"),
+    (1, 4, 2, 700, 700, 128, False, "wild"),
 ]
 
 
@@ -108,3 +116,18 @@ def test_all_visible_matches_fa_fwd(causal):
     o2, l2 = ops.fa_fwd(dev(q), dev(k), dev(v), causal=causal, scale=scale)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_colmask_zero_scale():
+    """Scale 0: every visible key has the same weight, so each row is the
+    mean of the V rows it sees (hidden keys must still get weight 0)."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 900, 128
+    q, k, v = make_qkv(B, Hq, Hkv, N, N, d, seed=67)
+    cb = _bounds("docs_causal", B, N, N, seed=68)
+    o, lse = _ops().fa_fwd_colmask(dev(q), dev(k), dev(v),
+                                   torch.from_numpy(cb).cuda(), causal=True,
+                                   scale=0.0, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=True,
+                                       scale=0.0, col_bounds=cb)
+    compare(host(o), host(lse), O_ref, L_ref, what="colmask scale 0")

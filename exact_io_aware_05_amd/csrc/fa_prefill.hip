@@ -688,13 +688,15 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     __syncthreads();
     n_act = __builtin_amdgcn_readfirstlane(blist[LMAX]);
   }
-  // key block at ring position p: p itself, or the p-th listed block (past
-  // the list: a block past Nk, whose copies are zeros)
-  auto blk_at = [&](int p) {
-    if (!LISTED) return p;
-    return p < n_act ? __builtin_amdgcn_readfirstlane(blist[p] & BLKBITS)
-                     : nblk + 1;
+  // list entry of ring position p (past the list: block nblk + 1, past
+  // Nk, whose copies are zeros, and no keep bits).  The entries of the
+  // positions whose copies are in flight stay in scalar registers, ent[i]
+  // for position j + i at the start of iteration j, so that each iteration
+  // reads one entry from LDS.
+  auto entry = [&](int p) {
+    return p < n_act ? __builtin_amdgcn_readfirstlane(blist[p]) : nblk + 1;
   };
+  int ent[LISTED ? L::NS - 1 : 1];
 
   // this wave's rows: blocks from w_mask on may hide keys from one of them
   // (past the causal limit of its first row, or past Nk)
@@ -825,7 +827,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     return (((int64_t)pg << lay.page_shift) |
             (kb & ((1 << lay.page_shift) - 1))) * rsb;
   };
-  auto group = [&](int g) {
+  // group g: K of key block kblk, V of key block vblk (the block of
+  // position g - 1; negative: a copy of zeros)
+  auto group = [&](int g, int kblk, int vblk) {
     if constexpr (PAGED) {
       const int64_t ro = page_off(g);
       copy_block_paged<D>(smem + (g % L::NS) * L::KBYTES, kh, ro,
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
         // bounds of the keys of the block at position g into stage g % NS:
         // wave w copies keys 8w .. 8w + 7 (64 bytes, four lanes); keys past
         // Nk read as zeros (an empty interval)
-        const int kk = min(blk_at(g) * BC + 8 * wave, Nk);
+        const int kk = min(kblk * BC + 8 * wave, Nk);
         const char* src = reinterpret_cast<const char*>(
             cmask.bounds + 2 * ((int64_t)b * cmask.mb + kk));
         const int ln = lane_now();
@@ -850,18 +854,37 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
                     64 * wave,
                 src, (uint32_t)min(Nk - kk, 8) * 8u, 16 * ln);
       }
-      copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, blk_at(g),
+      copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, kblk,
                     wave, k_off, 16, rsb, 2 * dq, dq / 8);
       copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
-                    vh, kv_rows, g > j0 ? blk_at(g - 1) : -1, wave, v_off,
-                    v_step, rsbv, 2 * dq);
+                    vh, kv_rows, vblk, wave, v_off, v_step, rsbv, 2 * dq);
     }
   };
-  auto copies = [&](int j) { group(j + L::NS - 1); };
+  auto copies = [&](int j) {
+    const int g = j + L::NS - 1;
+    if constexpr (LISTED) {
+      const int en = entry(g);
+      group(g, en & BLKBITS, ent[L::NS - 2] & BLKBITS);
+#pragma unroll
+      for (int i = 0; i + 1 < L::NS - 1; ++i) ent[i] = ent[i + 1];
+      ent[L::NS - 2] = en;
+    } else {
+      group(g, g, g - 1);
+    }
+  };
   // prologue: groups j0 .. j0 + NS - 2.  The first two must have landed for
   // every wave before the loop: group B's first wait in the loop comes one
   // barrier too late for group j0 + 1.
-  for (int g = j0; g < j0 + L::NS - 1; ++g) group(g);
+#pragma unroll
+  for (int i = 0; i < L::NS - 1; ++i) {
+    const int g = j0 + i;
+    if constexpr (LISTED) {
+      ent[i] = entry(g);
+      group(g, ent[i] & BLKBITS, i > 0 ? ent[i - 1] & BLKBITS : -1);
+    } else {
+      group(g, g, i > 0 ? g - 1 : -1);
+    }
+  }
   wait_vmcnt<(L::NS - 3) * OPS>();
   __syncthreads();
 
@@ -884,8 +907,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     int jb = j;
     bool keep = true;
     bool colm = false;  // column mask: this wave tests every key
-    if (LISTED) {
-      const int e = __builtin_amdgcn_readfirstlane(blist[j]);
+    if constexpr (LISTED) {
+      const int e = ent[0];
       jb = e & BLKBITS;
       keep = (e >> (group_a ? 24 : 25)) & 1;  // block mask: per half
       if (COLUMN) {

@@ -923,19 +923,37 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       rescale = false;  // nothing of this block enters this wave's rows
     else if (COLUMN && colm) {
       // each key's visibility to the 32 rows of this wave as a bit mask
-      // (lane = key of the block), from its interval clamped to the rows
+      // (lane = key of the block), from its interval clamped to the rows;
+      // rows from which the limit hides the key anyway (causal, or a key
+      // past Nk) count as seeing it
       const int ln = lane_now();
       const int2 x = *reinterpret_cast<const int2*>(
           cbnd + (j % L::NS) * 2 * BC + 2 * ln);
       const int ra = min(max(x.x, wrow0), wrow0 + 32) - wrow0;
       const int rb = min(max(x.y, wrow0), wrow0 + 32) - wrow0;
-      const uint32_t m = rb <= ra        ? 0u
-                         : rb - ra >= 32 ? ~0u
-                                         : ((1u << (rb - ra)) - 1u) << ra;
-      cmk[wave * BC + ln] = m;
-      rescale = softmax_phase<true, false, true>(s0, s1, lim0 - jb * BC, 0,
-                                                 c2, st, alpha, pk,
-                                                 cmk + wave * BC + 8 * h, col);
+      uint32_t m = rb <= ra        ? 0u
+                   : rb - ra >= 32 ? ~0u
+                                   : ((1u << (rb - ra)) - 1u) << ra;
+      const int key = jb * BC + ln;
+      if (CAUSAL) {
+        const int cd = min(max(key - off - wrow0, 0), 32);
+        m |= cd >= 32 ? ~0u : (1u << cd) - 1u;
+      }
+      if (key >= Nk) m = ~0u;
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(m);
+      if (__builtin_amdgcn_ballot_w64(m != m0) == 0) {
+        // every key of the block has the same rows: a row either sees all
+        // of them the limit lets through or none
+        rescale = softmax_phase<true>(s0, s1,
+                                      ((m0 >> col) & 1u) ? lim0 - jb * BC
+                                                         : -1,
+                                      0, c2, st, alpha, pk);
+      } else {
+        cmk[wave * BC + ln] = m;
+        rescale = softmax_phase<true, false, true>(
+            s0, s1, lim0 - jb * BC, 0, c2, st, alpha, pk,
+            cmk + wave * BC + 8 * h, col);
+      }
     }
     else if (jb >= w_mask || (BAND && jb < w_lo))
       rescale = softmax_phase<true, BAND>(s0, s1, lim0 - jb * BC,

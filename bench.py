@@ -107,70 +107,70 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq16_hkv8_n8192_d256_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 113890.7, "write_kib": 66058.5},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 113955.8, "write_kib": 66071.2},
     "gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 70924.1, "write_kib": 66636.1},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 70928.8, "write_kib": 66634.2},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 71189.6, "write_kib": 66560.8},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 71192.9, "write_kib": 66560.6},
     "mha_b4_h16_n2048_d64": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 41044.5, "write_kib": 16896.0},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 41050.0, "write_kib": 16896.0},
     "causal_outlier_b2_h16_n4096_d128": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 76707.6, "write_kib": 33408.3},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 76567.1, "write_kib": 33436.8},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 249693.0, "write_kib": 266266.8},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 249729.0, "write_kib": 266267.0},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 67581.2, "write_kib": 66561.2},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 67551.1, "write_kib": 66560.3},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 72438.4, "write_kib": 68608.6},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 72351.6, "write_kib": 68608.0},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "136bb8b9650dda8354b4357425a7d179190d6b6ea4db6f1f281bbf2e495bd49a",
-        "fetch_kib": 56159.9, "write_kib": 80144.8},
+        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
+        "fetch_kib": 54824.7, "write_kib": 74509.8},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
-        "sha256": "ecb89f434f521516e30ee16ad78c628307bc267c14e18d85f06bd3eb3d4959c8",
-        "fetch_kib": 33948.8, "write_kib": 66561.8},
+        "sha256": "b4950e249992e75d05564cc958d85c334fe4ede09310d5168a3b374e9439bd70",
+        "fetch_kib": 33979.4, "write_kib": 66560.0},
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
         "fetch_kib": 1048840.5, "write_kib": 2112.0},
     "decode_b16_hq32_hkv8_nq1_nk16384_d256": {
         "source": "fa_splitkv.hip",
-        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
         "fetch_kib": 1048963.0, "write_kib": 4160.6},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
         "fetch_kib": 132366.0, "write_kib": 2112.1},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "8f98429769507a3cbd41bbe553f6d0a161c1ff9af1151644f30d3921bc98e2f3",
+        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
         "fetch_kib": 1048863.5, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "537026a3e7ff89beebe0b6a3dde2ffe706d378b11343ecef38e8b0224e901f76",
-        "fetch_kib": 405222.7, "write_kib": 100352.0},
+        "sha256": "cdc5f107c28d6cf2bd30fa288b46cdad134a89264d965dc715b7fd9f9d04c630",
+        "fetch_kib": 405216.9, "write_kib": 100352.0},
     "gqa_prefill_window_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "537026a3e7ff89beebe0b6a3dde2ffe706d378b11343ecef38e8b0224e901f76",
-        "fetch_kib": 298726.3, "write_kib": 100352.2},
+        "sha256": "cdc5f107c28d6cf2bd30fa288b46cdad134a89264d965dc715b7fd9f9d04c630",
+        "fetch_kib": 298712.3, "write_kib": 100352.2},
 }
 
 

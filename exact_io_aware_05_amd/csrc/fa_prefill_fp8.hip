@@ -67,6 +67,13 @@ __device__ __forceinline__ void mfma8(i32x8 a, i32x8 b, f32x16& c) {
                                                       0);
 }
 
+// Workgroup barrier that neither waits for the copies in flight nor lets
+// the compiler move memory accesses across it (the loop's explicit vmcnt
+// waits order the ring; __syncthreads would wait for every copy).
+__device__ __forceinline__ void barrier() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // s_waitcnt with vmcnt = N (expcnt, lgkmcnt left free); gfx9 encoding.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -298,8 +305,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_fp8_kernel(
                         32 * h;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const u32x4 a = ok ? ldg16(qp + 64 * t) : u32x4{0u, 0u, 0u, 0u};
-      const u32x4 c = ok ? ldg16(qp + 64 * t + 16) : u32x4{0u, 0u, 0u, 0u};
+      // every lane loads (its address is kept inside the tensor), then
+      // zeros: a load under a branch leaves the compiler unsure at the main
+      // loop whether it has landed, and it then waits for every copy in
+      // flight in every iteration
+      u32x4 a = ldg16(qp + 64 * t), c = ldg16(qp + 64 * t + 16);
+      if (!ok) a = c = u32x4{0u, 0u, 0u, 0u};
       i32x8 v;
       v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
       v[4] = c[0]; v[5] = c[1]; v[6] = c[2]; v[7] = c[3];
@@ -375,7 +386,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_fp8_kernel(
   if (!group_a) __syncthreads();
   for (int j = 0; j < nblk; ++j) {
     mphase(j, std::true_type{});
-    __syncthreads();
+    barrier();
     copies(j);
     if (j >= w_mask)
       rescale = softmax_phase<true>(s0, s1, lim0 - j * BC, c2, st, alpha, pk);
@@ -385,9 +396,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_fp8_kernel(
       wait_vmcnt<2 * OPS>();
     else
       wait_vmcnt<OPS>();
-    __syncthreads();
+    barrier();
   }
   if (nblk > 0) mphase(nblk, std::false_type{});
+  wait_vmcnt<0>();  // no copy may be in flight when the wave ends
   __syncthreads();
   if (group_a) __syncthreads();
 

@@ -107,40 +107,40 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq16_hkv8_n8192_d256_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 113955.8, "write_kib": 66071.2},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 113917.2, "write_kib": 66077.6},
     "gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 70928.8, "write_kib": 66634.2},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 70932.1, "write_kib": 66635.0},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 71192.9, "write_kib": 66560.6},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 71181.8, "write_kib": 66560.4},
     "mha_b4_h16_n2048_d64": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 41050.0, "write_kib": 16896.0},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 41048.5, "write_kib": 16896.0},
     "causal_outlier_b2_h16_n4096_d128": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 76567.1, "write_kib": 33436.8},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 76707.3, "write_kib": 33387.8},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 249729.0, "write_kib": 266267.0},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 249612.9, "write_kib": 266266.7},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 67551.1, "write_kib": 66560.3},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 67545.5, "write_kib": 66560.1},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 72351.6, "write_kib": 68608.0},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 73946.0, "write_kib": 70656.0},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "d8fea3f598288819103976267e933373d8823782d8e0e9431d185d994288d212",
-        "fetch_kib": 54824.7, "write_kib": 74509.8},
+        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
+        "fetch_kib": 54825.6, "write_kib": 74520.3},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
         "sha256": "b4950e249992e75d05564cc958d85c334fe4ede09310d5168a3b374e9439bd70",

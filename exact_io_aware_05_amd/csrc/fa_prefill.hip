@@ -455,6 +455,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // of the listed variants; a fifth stage at d = 128 measured slower)
   constexpr int NSTG = D == 64 ? 8 : 4;
   using L = Layout<D, NSTG>;
+  // block-sparse: each half has a ring of its own, half of the stages (its
+  // waves copy and read only its blocks); NSR stages per ring, ring base
+  // stage gofs, CW waves share a ring's copies
+  constexpr int NSR = SPARSE ? NSTG / 2 : NSTG;
+  constexpr int CW = SPARSE ? NW / 2 : NW;
   // block-sparse: the key blocks this workgroup computes, in order (bits
   // 0..23 the block, bit 24 / 25 set when the rows of group A / B use it),
   // then their count
@@ -478,6 +483,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool group_a = wave < NW / 2;
   const int h = lane >> 5, col = lane & 31;
+  const int gofs = SPARSE && !group_a ? NSR : 0;
+  const int cwave = SPARSE ? (wave & (CW - 1)) : wave;
 
   // ---- work item: (b, kv head, Q block, head in group); heavy blocks first
   const int G = Hq / Hkv;
@@ -592,29 +599,38 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     __syncthreads();
   }
 
-  // ---- block-sparse: wave 0 lists the key blocks below nblk that either
-  // 128-row half of this workgroup keeps (mask rows 2 qblk and 2 qblk + 1)
+  // ---- block-sparse: each 128-row half lists the key blocks below nblk
+  // that its own mask row keeps (wave 0: row 2 qblk, for rows q0 ..; wave
+  // NW/2: row 2 qblk + 1), entry p of half X in 16-bit slot 2p + X, its
+  // count in slot 2 LMAX + X.  The halves then walk their lists side by
+  // side, each with its own copy ring, so that both have a block to work on
+  // in every iteration until the shorter list ends.
   int n_act = nblk;
+  int n_mine = 0;  // block-sparse: entries of this wave's half
   if (SPARSE) {
-    if (wave == 0) {
+    uint16_t* bl16 = reinterpret_cast<uint16_t*>(blist);
+    if (wave == 0 || wave == NW / 2) {
+      const int X = wave == 0 ? 0 : 1;
+      const bool has = q0 + X * (BR / 2) < Nq;
       const uint8_t* ma = bmask.mask + b * bmask.mb + hq * bmask.mh +
-                          (int64_t)(2 * qblk) * bmask.nkb;
-      const bool has_b = q0 + BR / 2 < Nq;
+                          (int64_t)(2 * qblk + X) * bmask.nkb;
       int cnt = 0;
       for (int base = 0; base < nblk; base += 64) {
         const int i = base + lane;
-        const bool ua = i < nblk && ma[i] != 0;
-        const bool ub = i < nblk && has_b && ma[bmask.nkb + i] != 0;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(ua || ub);
+        const bool u = has && i < nblk && ma[i] != 0;
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(u);
         const int pos =
             cnt + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        if (ua || ub) blist[pos] = i | (ua ? 1 << 24 : 0) | (ub ? 1 << 25 : 0);
+        if (u) bl16[2 * pos + X] = (uint16_t)i;
         cnt += (int)__builtin_popcountll(bal);
       }
-      if (lane == 0) blist[LMAX] = cnt;
+      if (lane == 0) bl16[2 * LMAX + X] = (uint16_t)cnt;
     }
     __syncthreads();
-    n_act = __builtin_amdgcn_readfirstlane(blist[LMAX]);
+    const int cnts = __builtin_amdgcn_readfirstlane(blist[LMAX]);
+    const int na = cnts & 0xFFFF, nb = (cnts >> 16) & 0xFFFF;
+    n_act = max(na, nb);
+    n_mine = group_a ? na : nb;
   }
   // ---- column mask: every wave classifies the key blocks wave, wave + NW,
   // ... below nblk (lane = key of the block) into blist[block]: bits 0..15
@@ -693,10 +709,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // positions whose copies are in flight stay in scalar registers, ent[i]
   // for position j + i at the start of iteration j, so that each iteration
   // reads one entry from LDS.
+  // block-sparse: a half's own entries, bit 24 set (its rows keep the
+  // block)
   auto entry = [&](int p) {
+    if constexpr (SPARSE) {
+      const uint16_t* bl16 = reinterpret_cast<const uint16_t*>(blist);
+      return p < n_mine ? __builtin_amdgcn_readfirstlane(
+                              bl16[2 * p + (group_a ? 0 : 1)]) |
+                              (1 << 24)
+                        : nblk + 1;
+    }
     return p < n_act ? __builtin_amdgcn_readfirstlane(blist[p]) : nblk + 1;
   };
-  int ent[LISTED ? L::NS - 1 : 1];
+  int ent[LISTED ? NSR - 1 : 1];
 
   // this wave's rows: blocks from w_mask on may hide keys from one of them
   // (past the causal limit of its first row, or past Nk)
@@ -783,8 +808,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     const char* vp[NTILE];
 #pragma unroll
     for (int tt = 0; tt < NTILE; ++tt)
-      vp[tt] = smem + ((j + L::NS - 1) % L::NS) * L::VBYTES + v_rd[tt];
-    const char* kp = smem + (j % L::NS) * L::KBYTES + k_rd;
+      vp[tt] = smem + (gofs + (j + NSR - 1) % NSR) * L::VBYTES + v_rd[tt];
+    const char* kp = smem + (gofs + j % NSR) * L::KBYTES + k_rd;
     constexpr bool QK = decltype(qk_tag)::value;
     __builtin_amdgcn_s_setprio(1);
     if (!LISTED || (pv && qk)) {
@@ -810,7 +835,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // both waits and a barrier.
   // copy instructions per wave and block (column mask: one more, for the
   // block's bounds)
-  constexpr int OPS = 2 * (L::NINS / NW) + (COLUMN ? 1 : 0);
+  constexpr int OPS = 2 * (L::NINS / CW) + (COLUMN ? 1 : 0);
   const int kv_rows = max(kv_end, 0);      // rows past this are not needed
   // (V_{j0-1}, before the first block, is a copy of zeros: block j0's
   // matrix phase multiplies it by the all-zero "previous" P, and 0 *
@@ -850,24 +875,25 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
             cmask.bounds + 2 * ((int64_t)b * cmask.mb + kk));
         const int ln = lane_now();
         if (ln < 4)
-          dma16(reinterpret_cast<char*>(cbnd) + (g % L::NS) * 8 * BC +
+          dma16(reinterpret_cast<char*>(cbnd) + (g % NSR) * 8 * BC +
                     64 * wave,
                 src, (uint32_t)min(Nk - kk, 8) * 8u, 16 * ln);
       }
-      copy_block<D>(smem + (g % L::NS) * L::KBYTES, kh, kv_rows, kblk,
-                    wave, k_off, 16, rsb, 2 * dq, dq / 8);
-      copy_block<D>(smem + L::VBASE + ((g + L::NS - 1) % L::NS) * L::VBYTES,
-                    vh, kv_rows, vblk, wave, v_off, v_step, rsbv, 2 * dq);
+      copy_block<D, CW>(smem + (gofs + g % NSR) * L::KBYTES, kh, kv_rows,
+                        kblk, cwave, k_off, 16, rsb, 2 * dq, dq / 8);
+      copy_block<D, CW>(
+          smem + L::VBASE + (gofs + (g + NSR - 1) % NSR) * L::VBYTES, vh,
+          kv_rows, vblk, cwave, v_off, v_step, rsbv, 2 * dq);
     }
   };
   auto copies = [&](int j) {
-    const int g = j + L::NS - 1;
+    const int g = j + NSR - 1;
     if constexpr (LISTED) {
       const int en = entry(g);
-      group(g, en & BLKBITS, ent[L::NS - 2] & BLKBITS);
+      group(g, en & BLKBITS, ent[NSR - 2] & BLKBITS);
 #pragma unroll
-      for (int i = 0; i + 1 < L::NS - 1; ++i) ent[i] = ent[i + 1];
-      ent[L::NS - 2] = en;
+      for (int i = 0; i + 1 < NSR - 1; ++i) ent[i] = ent[i + 1];
+      ent[NSR - 2] = en;
     } else {
       group(g, g, g - 1);
     }
@@ -876,7 +902,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
   // every wave before the loop: group B's first wait in the loop comes one
   // barrier too late for group j0 + 1.
 #pragma unroll
-  for (int i = 0; i < L::NS - 1; ++i) {
+  for (int i = 0; i < NSR - 1; ++i) {
     const int g = j0 + i;
     if constexpr (LISTED) {
       ent[i] = entry(g);
@@ -885,7 +911,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       group(g, g, i > 0 ? g - 1 : -1);
     }
   }
-  wait_vmcnt<(L::NS - 3) * OPS>();
+  // (block-sparse: each half reads only its own ring, so its first block
+  // is all it needs)
+  if constexpr (SPARSE)
+    wait_vmcnt<(NSR - 2) * OPS>();
+  else
+    wait_vmcnt<(L::NS - 3) * OPS>();
   __syncthreads();
 
   // ---- main loop.  Every wave runs the same code, one barrier after each
@@ -910,7 +941,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     if constexpr (LISTED) {
       const int e = ent[0];
       jb = e & BLKBITS;
-      keep = (e >> (group_a ? 24 : 25)) & 1;  // block mask: per half
+      keep = (e >> 24) & 1;  // block mask: this half has a block here
       if (COLUMN) {
         keep = (e >> (24 + wave)) & 1;
         colm = keep && ((e >> (16 + wave)) & 1);
@@ -928,7 +959,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       // past Nk) count as seeing it
       const int ln = lane_now();
       const int2 x = *reinterpret_cast<const int2*>(
-          cbnd + (j % L::NS) * 2 * BC + 2 * ln);
+          cbnd + (j % NSR) * 2 * BC + 2 * ln);
       const int ra = min(max(x.x, wrow0), wrow0 + 32) - wrow0;
       const int rb = min(max(x.y, wrow0), wrow0 + 32) - wrow0;
       uint32_t m = rb <= ra        ? 0u
@@ -962,7 +993,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
       rescale = softmax_phase<false>(s0, s1, lim0 - jb * BC, 0, c2, st,
                                      alpha, pk);
     keep_prev = keep;
-    if (group_a)
+    if constexpr (SPARSE)
+      wait_vmcnt<(NSR - 2) * OPS>();  // own ring: the next block, landed
+    else if (group_a)
       wait_vmcnt<(L::NS - 2) * OPS>();
     else
       wait_vmcnt<(L::NS - 3) * OPS>();

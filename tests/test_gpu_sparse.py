@@ -1,8 +1,9 @@
 """Block-sparse forward (fa_fwd_block_sparse, blocks of 128 query rows x 64
 keys) against the float64 oracle with the same block mask: random masks
-per head and shared ones, empty mask rows, causal; the all-ones mask
-against fa_fwd bit for bit; and the GQA prefill at full size with a
-quarter of the blocks kept, on sampled rows."""
+per head and shared ones, empty mask rows, causal; the two halves of a
+query block with very different block lists; the all-ones mask against
+fa_fwd bit for bit; and the GQA prefill at full size with a quarter of the
+blocks kept, on sampled rows."""
 import numpy as np
 import pytest
 
@@ -103,3 +104,31 @@ def test_gqa_prefill_quarter_blocks_sampled_rows():
                                        scale=float(np.float32(w.scale)),
                                        rows=rows, block_mask=bm, block_size=BS)
     compare(O[:, :, rows], L[:, :, rows], O_ref, L_ref, what="gqa sparse")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_halves_with_unequal_lists(causal):
+    """The two 128-row halves of a 256-row query block walk their own block
+    lists side by side: one half keeps every key block and the other none,
+    or one keeps a single block, or they keep disjoint sets; the half that
+    runs out of blocks first still meets every barrier."""
+    B, Hq, Hkv, Nq, Nk, d = 1, 4, 2, 1000, 1200, 128
+    q, k, v = make_qkv(B, Hq, Hkv, Nq, Nk, d, seed=85)
+    nqb, nkb = _nb(Nq, 128), _nb(Nk, 64)
+    bm = np.zeros((B, Hq, nqb, nkb), dtype=np.uint8)
+    bm[0, 0, 0::2, :] = 1          # head 0: even halves all, odd halves none
+    bm[0, 1, 0::2, 3] = 1          # head 1: even halves one block ...
+    bm[0, 1, 1::2, :] = 1          # ... odd halves all
+    bm[0, 2, :, 0::2] = 1          # head 2: disjoint sets per half
+    bm[0, 2, 1::2, :] ^= 1
+    bm[0, 3] = _mask((nqb, nkb), 0.1, seed=86)[...]
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    o, lse = _ops().fa_fwd_block_sparse(dev(q), dev(k), dev(v),
+                                        torch.from_numpy(bm).cuda(),
+                                        causal=causal, scale=scale,
+                                        out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    O_ref, L_ref = reference_attention(f64(q), f64(k), f64(v), causal=causal,
+                                       scale=scale, block_mask=bm,
+                                       block_size=BS)
+    compare(host(o), host(lse), O_ref, L_ref, what="unequal halves")

@@ -123,7 +123,8 @@ bool splitkv_too_large(int B, int Hq, int Hkv, int Nq, int splits) {
 
 constexpr int kMaxDevices = 64;
 
-// ---- workspace of the KV-split form inside fa_fwd and fa_fwd_window
+// ---- workspace of the KV-split form inside fa_fwd and fa_fwd_window, and
+// of the column-mask classification inside fa_fwd_colmask
 //
 // One buffer per (device, stream), kept for the later calls on that stream:
 // calls on one stream run in stream order, so each may reuse what the one
@@ -147,12 +148,10 @@ std::mutex g_ws_mu;
 StreamWorkspace g_ws[kMaxCachedStreams];
 int g_ws_count = 0;
 
-// The KV-split form with its workspace as described above.
-int run_splitkv(const void* q, const void* k, const void* v, void* o,
-                float* lse, const fa::Shape& s, int splits, bool f32,
-                hipStream_t stream) {
-  const size_t bytes =
-      fa::splitkv_workspace_bytes((long long)s.B * s.Hq * s.Nq, s.d, splits);
+// Runs launch(ws) with a workspace of at least `bytes` bytes, taken as
+// described above.
+template <class F>
+int with_workspace(hipStream_t stream, size_t bytes, F&& launch) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_status(e);
@@ -181,17 +180,27 @@ int run_splitkv(const void* q, const void* k, const void* v, void* o,
         }
         w.bytes = bytes;
       }
-      return hip_status(
-          fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, w.ptr, stream));
+      return hip_status(launch(w.ptr));
     }
   }
   void* ws = nullptr;
   e = hipMallocAsync(&ws, bytes, stream);
   if (e != hipSuccess) return hip_status(e);
-  e = fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
+  e = launch(ws);
   hipError_t e2 = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(e2);
+}
+
+// The KV-split form with its workspace as described above.
+int run_splitkv(const void* q, const void* k, const void* v, void* o,
+                float* lse, const fa::Shape& s, int splits, bool f32,
+                hipStream_t stream) {
+  const size_t bytes =
+      fa::splitkv_workspace_bytes((long long)s.B * s.Hq * s.Nq, s.d, splits);
+  return with_workspace(stream, bytes, [&](void* ws) {
+    return fa::launch_splitkv(q, k, v, o, lse, s, f32, splits, ws, stream);
+  });
 }
 
 // The prefill kernel (splits == 0) or the KV-split form.
@@ -687,10 +696,13 @@ int fa_fwd_colmask(const void* q, const void* k, const void* v, void* o,
   st = check_device();
   if (st != FA_OK) return st;
   const fa::Shape s{B, Hq, Hkv, Nq, Nk, d, causal, scale};
-  const fa::ColMask cm{col_bounds, (long long)Nk};
-  return hip_status(fa::launch_prefill_column(q, k, v, o, lse, s, cm,
-                                              out_dtype == FA_OUT_F32,
-                                              stream));
+  return with_workspace(
+      stream, fa::column_list_bytes(B, Nq, Nk), [&](void* ws) {
+        const fa::ColMask cm{col_bounds, (long long)Nk,
+                             static_cast<int*>(ws), (long long)nkb};
+        return fa::launch_prefill_column(q, k, v, o, lse, s, cm,
+                                         out_dtype == FA_OUT_F32, stream);
+      });
 }
 
 int fa_fwd_varlen(const void* q, const void* k, const void* v, void* o,

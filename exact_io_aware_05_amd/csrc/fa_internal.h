@@ -139,15 +139,21 @@ struct BlockMask {
 // Column-interval mask of the prefill kernel: key j of sequence b may be
 // seen by the query rows bounds[2 (b mb + j)] .. bounds[2 (b mb + j) + 1]
 // - 1 (int32 pairs, shared by the sequence's heads), on top of the causal
-// flag.  The workgroup lists the key blocks that any of its rows may see
-// (at most kColMaxKeyBlocks) in an LDS list like a block mask's; the LDS
-// that the list gives up holds a ring of each listed block's bounds and
-// per-wave visibility masks.
+// flag.  A first kernel classifies each (sequence, 256-row query block, key
+// block) once for all heads into `lists` (one int per key block, rows of
+// lstride); each prefill workgroup then keeps the key blocks that any of
+// its rows may see (at most kColMaxKeyBlocks) in an LDS list like a block
+// mask's.  The LDS that the list gives up holds a ring of each listed
+// block's bounds and per-wave visibility masks.
 constexpr int kColMaxKeyBlocks = 6655;
 struct ColMask {
   const int* bounds;
-  long long mb;  // pairs between sequences
+  long long mb;       // pairs between sequences
+  int* lists;         // B * ceil(Nq / 256) rows of lstride ints (workspace)
+  long long lstride;  // key blocks of 64 keys: ceil(Nk / 64)
 };
+// bytes of the classification rows of a column-mask call
+size_t column_list_bytes(int B, int Nq, int Nk);
 
 hipError_t launch_prefill_column(const void* q, const void* k, const void* v,
                                  void* o, float* lse, const Shape& s,

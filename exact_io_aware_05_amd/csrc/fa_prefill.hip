@@ -433,6 +433,57 @@ __device__ __forceinline__ bool softmax_phase(const f32x16& s0,
 // kBand (iff i + Nk - Nq - wl <= j <= i + Nk - Nq + wr, wl and wr >= 0).
 constexpr int kNone = 0, kCausal = 1, kBand = 2;
 
+// Column mask, once per call for all heads: one wave per (sequence, query
+// block of BR rows, key block of BC keys below the block's causal limit),
+// lane = key, writes the block's entry for the prefill kernel's list: bits
+// 0..15 the block, bit 16 + w set when the interval of some key hides it
+// from some row of wave w (rows BR-block + 32 w ..) that would otherwise see
+// it (that wave then tests every key), bit 24 + w when some row of wave w
+// may see some key.  Entries past a query block's causal limit are not
+// written (the prefill kernel reads only those below it).
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void column_list_kernel(
+    ColMask cm, int Nq, int Nk, int n_qblk, long long n_waves) {
+  const int lane = threadIdx.x & 63;
+  const long long wv =
+      (long long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wv >= n_waves) return;
+  const int kb = (int)(wv % cm.lstride);
+  const long long t = wv / cm.lstride;
+  const int qblk = (int)(t % n_qblk);
+  const int b = (int)(t / n_qblk);
+  const int q0 = qblk * BR;
+  const int off = Nk - Nq;
+  const int kv_end = CAUSAL ? min(Nk, q0 + BR + off) : Nk;
+  if (kb * BC >= kv_end) return;  // whole wave: past the block's keys
+  const int key = kb * BC + lane;
+  const bool valid = key < kv_end;
+  int lo = 0, hi = 0;
+  if (valid) {
+    const int2 x = *reinterpret_cast<const int2*>(
+        cm.bounds + 2 * ((int64_t)b * cm.mb + key));
+    lo = x.x;
+    hi = x.y;
+  }
+  // rows that may see this key: its interval, and (causal) from its place on
+  const int vlo = CAUSAL ? max(lo, key - off) : lo;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int w0 = q0 + 32 * w, r1 = min(w0 + 32, Nq);
+    // the rows of wave w whose view of the key the interval decides: all of
+    // them, or under the causal mask those from the first row that sees the
+    // key (the causal limit hides it from the others)
+    const int r0 = CAUSAL ? max(w0, key - off) : w0;
+    const bool all_vis = r0 >= r1 || !valid || (lo <= r0 && hi >= r1);
+    if (__builtin_amdgcn_ballot_w64(all_vis) != ~0ull) bits |= 1u << (16 + w);
+    // some row of the wave may see the key
+    if (__builtin_amdgcn_ballot_w64(valid && max(vlo, w0) < min(hi, r1)) != 0)
+      bits |= 1u << (24 + w);
+  }
+  if (lane == 0) cm.lists[t * cm.lstride + kb] = kb | (int)bits;
+}
+
 template <int D, int MODE, bool OUT_F32, bool SPARSE = false,
           bool COLUMN = false, bool PAGED = false>
 __global__ __launch_bounds__(NT, 1) void prefill_kernel(
@@ -632,77 +683,39 @@ __global__ __launch_bounds__(NT, 1) void prefill_kernel(
     n_act = max(na, nb);
     n_mine = group_a ? na : nb;
   }
-  // ---- column mask: every wave classifies the key blocks wave, wave + NW,
-  // ... below nblk (lane = key of the block) into blist[block]: bits 0..15
-  // the block, bit 16 + w set when the interval of some key hides it from
-  // some row of wave w that would otherwise see it (that wave then tests
-  // every key), bit 24 + w when some row of wave w may see some key.  Wave
-  // 0 then drops the blocks no wave sees, in place and in order.
+  // ---- column mask: the classification of this query block's key blocks
+  // below nblk (one int each: bits 0..15 the block, bit 16 + w when wave w
+  // must test its rows key by key, bit 24 + w when some row of wave w may
+  // see some key), made once for all heads by column_list_kernel; the
+  // waves keep the blocks some wave sees, in order, wave w compacting the
+  // entries w * 64 .. w * 64 + 63 of each round of NW * 64 (the per-wave
+  // counts of a round in the first NW words of the mask area, unused
+  // before the main loop)
   if (COLUMN) {
-    const int* cb = cmask.bounds + 2 * ((int64_t)b * cmask.mb);
-    constexpr int UNR = 4;
-    for (int kb0 = wave; kb0 < nblk; kb0 += UNR * NW) {
-      int blo[UNR], bhi[UNR];
+    const int* ge = cmask.lists + (int64_t)(b * n_qblk + qblk) * cmask.lstride;
+    uint32_t* ccnt = cmk;
+    int total = 0;
+    for (int base = 0; base < nblk; base += 64 * NW) {
+      const int i = base + 64 * wave + lane;
+      const int e = i < nblk ? ge[i] : 0;
+      const bool kept = ((e >> 24) & 0xFF) != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
+      if (lane == 0) ccnt[wave] = (uint32_t)__builtin_popcountll(bal);
+      __syncthreads();
+      int pre = total, all = total;
 #pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int key = (kb0 + NW * u) * BC + lane;
-        blo[u] = 0;
-        bhi[u] = 0;
-        if (kb0 + NW * u < nblk && key < kv_end) {
-          const int2 x = *reinterpret_cast<const int2*>(cb + 2 * key);
-          blo[u] = x.x;
-          bhi[u] = x.y;
-        }
+      for (int w = 0; w < NW; ++w) {
+        const int c = (int)ccnt[w];
+        pre += w < wave ? c : 0;
+        all += c;
       }
-#pragma unroll
-      for (int u = 0; u < UNR; ++u) {
-        const int kb = kb0 + NW * u;
-        if (kb >= nblk) break;
-        const int key = kb * BC + lane;
-        const bool valid = key < kv_end;
-        // rows that may see this key: its interval, and (causal) from its
-        // place on
-        const int vlo = CAUSAL ? max(blo[u], key - off) : blo[u];
-        const int vhi = bhi[u];
-        uint32_t bits = 0;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const int w0 = q0 + 32 * w, r1 = min(w0 + 32, Nq);
-          // the rows of wave w whose view of the key the interval decides:
-          // all of them, or under the causal mask those from the first row
-          // that sees the key (the causal limit hides it from the others)
-          const int r0 = CAUSAL ? max(w0, key - off) : w0;
-          const bool all_vis =
-              r0 >= r1 || !valid || (blo[u] <= r0 && bhi[u] >= r1);
-          if (__builtin_amdgcn_ballot_w64(all_vis) != ~0ull)
-            bits |= 1u << (16 + w);
-          // some row of the wave may see the key
-          if (__builtin_amdgcn_ballot_w64(valid &&
-                                          max(vlo, w0) < min(vhi, r1)) != 0)
-            bits |= 1u << (24 + w);
-        }
-        if (lane == 0) blist[kb] = kb | (int)bits;
-      }
+      if (kept)
+        blist[pre + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull))] =
+            e;
+      total = all;
+      __syncthreads();  // (ccnt is reused by the next round)
     }
-    __syncthreads();
-    if (wave == 0) {
-      int cnt = 0;
-      for (int base = 0; base < nblk; base += 64) {
-        const int i = base + lane;
-        const int e = i < nblk ? blist[i] : 0;
-        const bool kept = ((e >> 24) & 0xFF) != 0;
-        const uint64_t bal = __builtin_amdgcn_ballot_w64(kept);
-        const int pos =
-            cnt + (int)__builtin_popcountll(bal & ((1ull << lane) - 1ull));
-        // (every lane has read its entry before any lane writes, and an
-        // entry moves only down, never past an unread one)
-        if (kept) blist[pos] = e;
-        cnt += (int)__builtin_popcountll(bal);
-      }
-      if (lane == 0) blist[LMAX] = cnt;
-    }
-    __syncthreads();
-    n_act = __builtin_amdgcn_readfirstlane(blist[LMAX]);
+    n_act = __builtin_amdgcn_readfirstlane(total);
   }
   // list entry of ring position p (past the list: block nblk + 1, past
   // Nk, whose copies are zeros, and no keep bits).  The entries of the
@@ -1371,6 +1384,20 @@ hipError_t launch_column_d(const void* q, const void* k, const void* v,
                            const ColMask& cm, bool out_f32,
                            hipStream_t stream) {
   const SeqLayout lay = dense_layout(s);
+  {
+    const int n_qblk = (s.Nq + BR - 1) / BR;
+    const long long n_waves = (long long)s.B * n_qblk * cm.lstride;
+    if (s.causal)
+      hipLaunchKernelGGL(column_list_kernel<true>,
+                         dim3((unsigned)((n_waves + 3) / 4)), dim3(256), 0,
+                         stream, cm, s.Nq, s.Nk, n_qblk, n_waves);
+    else
+      hipLaunchKernelGGL(column_list_kernel<false>,
+                         dim3((unsigned)((n_waves + 3) / 4)), dim3(256), 0,
+                         stream, cm, s.Nq, s.Nk, n_qblk, n_waves);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   if (s.causal)
     return out_f32 ? launch<D, kCausal, true, false, true>(
                          q, k, v, o, lse, s, lay, 0, 0, stream, {}, cm)
@@ -1380,6 +1407,12 @@ hipError_t launch_column_d(const void* q, const void* k, const void* v,
                                                        0, 0, stream, {}, cm)
                  : launch<D, kNone, false, false, true>(
                        q, k, v, o, lse, s, lay, 0, 0, stream, {}, cm);
+}
+
+size_t column_list_bytes(int B, int Nq, int Nk) {
+  const long long n_qblk = ((long long)Nq + BR - 1) / BR;
+  const long long nkb = ((long long)Nk + BC - 1) / BC;
+  return (size_t)(B * n_qblk * nkb) * sizeof(int);
 }
 
 hipError_t launch_prefill_column(const void* q, const void* k, const void* v,

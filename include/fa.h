@@ -252,11 +252,15 @@ int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o,
  *                 hi - 1 = [b][j][1] - 1 (an empty range hides the key),
  * shared by the sequence's heads and applied on top of the causal flag
  * (bottom-right alignment).  Document masks, prefix-LM masks and windows
- * are such intervals.  q, k, v, o, lse as for fa_fwd.  The workgroup lists
- * the 64-key blocks that any of its rows may see and skips the rest; a
- * wave tests every key only where some key of a block is hidden from some
- * of its rows.  Bounds are read on the device and used as given (rows
- * outside [0, Nq) simply match no row).  Errors as for fa_fwd;
+ * are such intervals.  q, k, v, o, lse as for fa_fwd.  A first kernel
+ * classifies every (256-row query block, 64-key block) once for all heads;
+ * each workgroup then computes only the key blocks that some of its rows
+ * may see, and a wave tests every key only where some key of a block is
+ * hidden from some of its rows.  The classification (B * ceil(Nq / 256) *
+ * ceil(Nk / 64) ints) lives in the same per-stream library workspace as
+ * fa_fwd's KV-split partials, taken and grown the same way.  Bounds are
+ * read on the device and used as given (rows outside [0, Nq) simply match
+ * no row).  Errors as for fa_fwd;
  * FA_ERR_INVALID_ARG also for a null or not 8-byte aligned col_bounds;
  * FA_ERR_UNSUPPORTED when Nk exceeds 6655 blocks of 64 keys (425,920 keys).
  */

@@ -107,70 +107,70 @@ WRITE_SCALE = 1048576.0 / 1048576.0
 MEASURED_TRAFFIC = {
     "gqa_prefill_b1_hq16_hkv8_n8192_d256_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 113917.2, "write_kib": 66077.6},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 113879.5, "write_kib": 66076.8},
     "gqa_prefill_paged_b1_hq32_hkv8_n8192_d128_causal_p256": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 70932.1, "write_kib": 66635.0},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 71241.3, "write_kib": 66616.3},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 71181.8, "write_kib": 66560.4},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 71198.9, "write_kib": 66560.5},
     "mha_b4_h16_n2048_d64": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 41048.5, "write_kib": 16896.0},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 41049.5, "write_kib": 16896.0},
     "causal_outlier_b2_h16_n4096_d128": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 76707.3, "write_kib": 33387.8},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 76681.5, "write_kib": 33418.3},
     "varlen_prefill_t32768_hq32_hkv8_d128_causal": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 249612.9, "write_kib": 266266.7},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 250547.0, "write_kib": 266269.5},
     "gqa_prefill_window": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 67545.5, "write_kib": 66560.1},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 67555.6, "write_kib": 66560.4},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_sparse25": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 73946.0, "write_kib": 70656.0},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 74004.6, "write_kib": 70656.1},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_docmask": {
         "source": "fa_prefill.hip",
-        "sha256": "52dd8f0ac2f4cf1eacfcb718469b44e3c7abfcce64c4f0afcc1b2bd044e78b6c",
-        "fetch_kib": 54825.6, "write_kib": 74520.3},
+        "sha256": "9b9b9698dd11d0c43cf794d84c00fd747c7571b8763e1a12d6ef6bd0fe536f5c",
+        "fetch_kib": 54351.9, "write_kib": 74180.9},
     "gqa_prefill_b1_hq32_hkv8_n8192_d128_causal_fp8": {
         "source": "fa_prefill_fp8.hip",
-        "sha256": "b4950e249992e75d05564cc958d85c334fe4ede09310d5168a3b374e9439bd70",
-        "fetch_kib": 33979.4, "write_kib": 66560.0},
+        "sha256": "dab1cbc0965c5dcf285d570693bab4a13bd9ac0427ae06ed6a211b042298aa0c",
+        "fetch_kib": 33978.0, "write_kib": 66560.6},
     # the partial kernel (the merge kernel reads the 2 MB of partials)
     "decode_b16_hq32_hkv8_nq1_nk32768_d128": {
         "source": "fa_splitkv.hip",
-        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
+        "sha256": "cbae59c9b79c3f43b4c024ebe9392a2b2bad2f84acbb2fc164c2e4da4d61511c",
         "fetch_kib": 1048840.5, "write_kib": 2112.0},
     "decode_b16_hq32_hkv8_nq1_nk16384_d256": {
         "source": "fa_splitkv.hip",
-        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
-        "fetch_kib": 1048963.0, "write_kib": 4160.6},
+        "sha256": "cbae59c9b79c3f43b4c024ebe9392a2b2bad2f84acbb2fc164c2e4da4d61511c",
+        "fetch_kib": 1048963.0, "write_kib": 4160.3},
     "decode_window": {
         "source": "fa_splitkv.hip",
-        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
-        "fetch_kib": 132366.0, "write_kib": 2112.1},
+        "sha256": "cbae59c9b79c3f43b4c024ebe9392a2b2bad2f84acbb2fc164c2e4da4d61511c",
+        "fetch_kib": 132366.0, "write_kib": 2112.0},
     "decode_paged_b16_hq32_hkv8_nq1_nk32768_d128_p256": {
         "source": "fa_splitkv.hip",
-        "sha256": "ce7d415bd98d3dbdad7ac873039ec23e2f7f37b1de7f68dcd3d440c14318c3b9",
+        "sha256": "cbae59c9b79c3f43b4c024ebe9392a2b2bad2f84acbb2fc164c2e4da4d61511c",
         "fetch_kib": 1048863.5, "write_kib": 2112.0},
     # the whole fa_bwd call: row preprocessing + dK/dV + dQ kernels
     "gqa_prefill_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "cdc5f107c28d6cf2bd30fa288b46cdad134a89264d965dc715b7fd9f9d04c630",
-        "fetch_kib": 405216.9, "write_kib": 100352.0},
+        "sha256": "ea262dd0d9899bfa6c10edee3451a0dcd920fd2beaa6170ef3d0561d1a661e4d",
+        "fetch_kib": 406973.1, "write_kib": 100352.0},
     "gqa_prefill_window_bwd": {
         "source": "fa_backward.hip",
-        "sha256": "cdc5f107c28d6cf2bd30fa288b46cdad134a89264d965dc715b7fd9f9d04c630",
-        "fetch_kib": 298712.3, "write_kib": 100352.2},
+        "sha256": "ea262dd0d9899bfa6c10edee3451a0dcd920fd2beaa6170ef3d0561d1a661e4d",
+        "fetch_kib": 298627.6, "write_kib": 100352.5},
 }
 
 

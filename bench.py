@@ -1,11 +1,12 @@
 """Throughput of the fused attention forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--settle S]
 
 A step is one ``fa_fwd`` call over the whole workload with inputs resident
-in HBM.  W untimed steps, then exactly K timed steps bracketed by device
-synchronisation; a pair of HIP events on the stream the kernels run on
+in HBM.  Untimed steps for ``--settle`` seconds (0.25 by default: the GPU
+clock of a fresh process settles after about 80 ms of load) and W untimed
+steps, then exactly K timed steps bracketed by device synchronisation; a pair of HIP events on the stream the kernels run on
 brackets the K steps too, which gives the average device time of a step
 used for the roofline.  Prints ONE JSON line.
 
@@ -296,10 +297,39 @@ def calibrate_copy(mib, steps, warmup):
     return 0
 
 
+# Untimed load before the warm-up steps, in seconds of wall time.  On a
+# fresh process the GPU's clock is not settled: the causal GQA prefill takes
+# 544-573 us for its first calls, 596-669 us for calls 4-20 while the power
+# manager pulls the clock down, and settles at 503-508 us after about 80 ms
+# of load (per-call HIP event times, MI355X).  A few warm-up steps alone would
+# time that transient instead of the sustained rate.
+SETTLE_S = 0.25
+_settle = {"s": SETTLE_S, "steps": 0}
+
+
+def _emit(out):
+    """Print one bench line, with the untimed settle load beside W."""
+    line = {}
+    for key, val in out.items():
+        line[key] = val
+        if key == "warmup":
+            line["settle"] = {"seconds": _settle["s"], "steps": _settle["steps"]}
+    print(json.dumps(line), flush=True)
+
+
 def _time_steps(step, steps, warmup, stream):
-    """W untimed steps, then K steps between device synchronisations with
-    one HIP event pair on the launch stream: (wall ms, device ms) per step."""
+    """Untimed steps for SETTLE_S seconds, W untimed steps, then K steps
+    between device synchronisations with one HIP event pair on the launch
+    stream: (wall ms, device ms) per step."""
     import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < _settle["s"]:
+        for _ in range(8):
+            step()
+        n += 8
+        torch.cuda.synchronize()
+    _settle["steps"] = n
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -394,7 +424,7 @@ def bench_varlen(args):
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_varlen(spec, lens, q, k, v, cu_q)
-    print(json.dumps(out), flush=True)
+    _emit(out)
     return 0
 
 
@@ -471,7 +501,7 @@ def bench_paged(args, sp):
                 "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                 "data": data, "config": config, "roofline": roof,
                 "cpu_baseline": None})
-    print(json.dumps(out), flush=True)
+    _emit(out)
     return 0
 
 
@@ -545,7 +575,7 @@ def bench_fp8(args):
             "cpu": _cpu_model(),
             "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
                       f"float64 numpy on the decoded inputs; {t_total:.1f} s"}
-    print(json.dumps(out), flush=True)
+    _emit(out)
     return 0
 
 
@@ -620,7 +650,7 @@ def bench_sparse(args):
             "cpu": _cpu_model(),
             "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
                       f"float64 numpy; {t_total:.1f} s"}
-    print(json.dumps(out), flush=True)
+    _emit(out)
     return 0
 
 
@@ -695,7 +725,7 @@ def bench_docmask(args):
             "cpu": _cpu_model(),
             "sample": f"{done} of {w.Hq} heads, all {w.Nq} query rows each, "
                       f"float64 numpy; {t_total:.1f} s"}
-    print(json.dumps(out), flush=True)
+    _emit(out)
     return 0
 
 
@@ -706,6 +736,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="gqa_prefill", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=float, default=SETTLE_S, metavar="S",
+                    help="seconds of untimed steps before the warm-up steps "
+                         "(the GPU clock settles after about 80 ms of load)")
     ap.add_argument("--splits", type=int, default=0,
                     help="decode: KV splits (0: the library's default)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -713,6 +746,7 @@ def main(argv=None):
                          "instead (the reference kernel for scaling HBM "
                          "byte counters)")
     args = ap.parse_args(argv)
+    _settle["s"] = max(0.0, args.settle)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the attention forward runs on "
@@ -874,7 +908,7 @@ def main(argv=None):
         if w.Nq == 1:
             cb = out["cpu_baseline"]
             cb["note"] = "oracle TFLOP/s (decode bytes are not a CPU metric)"
-    print(json.dumps(out), flush=True)
+    _emit(out)
     return 0
 
 
